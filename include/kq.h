@@ -1,0 +1,140 @@
+/*
+ * kq.h -- C ABI of libkq, the k-quant matmul for AMD Instinct MI355X (gfx950).
+ *
+ * The library multiplies llama.cpp-style k-quant weights (Q4_K, and Q6_K for
+ * the output head) by activations quantised to q8_1:
+ *
+ *   - kq_quantize_q8_1: activations f32 -> q8_1 blocks, once per matmul input
+ *     (leone-cuda "CUDA kernel design": a separate kernel quantises the
+ *     activation vector to q8_1 once per GEMV input; minfer "The CUDA
+ *     backend" 2.3: activations quantised once per matmul call by a small
+ *     prepass before the GEMM).
+ *   - kq_gemv_q4k / kq_gemv_q6k: the decode matrix-vector product at batch
+ *     1..4, weight-streaming bound (minfer "The CUDA backend" 2.2 and 2.3,
+ *     MMVQ; leone-cuda "CUDA kernel design": Q4_K and Q6_K GEMV, residual
+ *     epilogue; cajeta "One model, start to last token" 4.1 and 4.2).
+ *   - kq_mmq_q4k: the prefill matrix-matrix product over many tokens on the
+ *     int8 matrix cores (minfer "The CUDA backend" 2.3, MMQ, and 3.2.6).
+ *
+ * Formats (little-endian; the pages give the sizes and field lists, the bit
+ * positions are the public GGUF k-quant layout):
+ *
+ *   Q4_K superblock, 256 values, 144 bytes:
+ *     [0,2) f16 d   [2,4) f16 dmin   [4,16) 8 six-bit scales + 8 six-bit mins
+ *     [16,144) 128 bytes of 4-bit codes.
+ *     w = (d*sc_j)*q - (dmin*m_j) for the value's 32-value sub-block j.
+ *   Q6_K superblock, 256 values, 210 bytes:
+ *     [0,128) ql low 4 bits   [128,192) qh high 2 bits   [192,208) 16 int8
+ *     scales (one per 16 values)   [208,210) f16 d.   w = (d*sc)*(q - 32).
+ *   q8_1 block, 32 values, 36 bytes:
+ *     [0,2) f16 d8   [2,4) f16 s (sum of the 32 source values)
+ *     [4,36) 32 int8 codes.  xh = d8 * code.
+ *
+ * Matrices are row-major: weight row r is k/256 consecutive superblocks;
+ * activations, residuals and outputs are token-major ([token][...]).
+ *
+ * Common contract of every call:
+ *   - all data pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps a pointer after the call returns;
+ *   - the work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *     the null stream); no call synchronises;
+ *   - argument errors return KQ_ERR_ARG before anything is launched, and
+ *     kq_last_error() names the call and the offending values;
+ *   - KQ_ERR_UNSUPPORTED: the current HIP device is not a gfx950 GPU;
+ *   - KQ_ERR_HIP: the launch failed; kq_last_error() holds the HIP error;
+ *   - there is no fallback path: a call either launches the gfx950 kernel or
+ *     returns an error;
+ *   - results are deterministic: the same inputs give the same output bits
+ *     on every run (no atomics, fixed reduction order);
+ *   - sizes of zero rows / tokens (m == 0, n == 0, rows == 0, batch rows of an
+ *     empty matrix) are valid and launch nothing;
+ *   - calls are thread-safe; the error text is per host thread.
+ */
+#ifndef KQ_H_
+#define KQ_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KQ_OK = 0,
+    KQ_ERR_ARG = -1,
+    KQ_ERR_UNSUPPORTED = -2,
+    KQ_ERR_HIP = -3
+} kq_status;
+
+/* Largest k accepted by the matmul and quantise calls. */
+#define KQ_MAX_K 65536
+/* Largest m / n / rows accepted (outputs are indexed with 32-bit rows). */
+#define KQ_MAX_ROWS 0x7fffffff
+
+/*
+ * Quantise f32 activations to q8_1.
+ *   x     f32 [rows][k], row-major, 16-byte aligned.
+ *   xq    out: [rows][k/32] q8_1 blocks of 36 bytes, 4-byte aligned.
+ *   rows  >= 0;  k > 0, k % 32 == 0, k <= KQ_MAX_K.
+ * Per 32-value block: amax = max|x|; d = amax/127 (f32, IEEE division);
+ * id = 1/d (0 if d == 0); code = roundf(x*id) (half away from zero);
+ * s = f32 pairwise-tree sum of the 32 source values (a[i] += a[i+h] for
+ * h = 16, 8, 4, 2, 1); d and s stored as f16 rounded to nearest-even.
+ * The result is bit-exact.  NaN/Inf inputs and blocks whose 1/d overflows
+ * (amax < 127*2^-128) are outside the contract.
+ * xq must not overlap x.
+ */
+int kq_quantize_q8_1(const float* x, void* xq, int64_t rows, int64_t k, void* stream);
+
+/*
+ * Q4_K x q8_1 matrix-vector product for 1..4 activation vectors, with an
+ * optional residual added when each output is written.
+ *   w         [m][k/256] Q4_K superblocks (144 bytes), 16-byte aligned.
+ *   xq        [batch][k/32] q8_1 blocks (from kq_quantize_q8_1), 4-byte aligned.
+ *   y         out: f32 [batch][m], 4-byte aligned.
+ *   residual  NULL, or f32 [batch][m], 4-byte aligned; y == residual is
+ *             allowed (in place); any other overlap is an error.
+ *   m >= 0;  k > 0, k % 256 == 0, k <= KQ_MAX_K;  1 <= batch <= 4.
+ * y[t][r] = residual[t][r] + sum over the k/32 blocks j of
+ *           d8[t][j] * (d*sc_j * A - dmin*m_j * Bq), with A the integer dot of
+ * the block's 4-bit codes with the q8 codes and Bq the sum of the q8 codes
+ * (the minimum term is formed from the codes, not from the stored sum s).
+ * y must not overlap w or xq.
+ */
+int kq_gemv_q4k(const void* w, const void* xq, float* y, const float* residual,
+                int64_t m, int64_t k, int32_t batch, void* stream);
+
+/*
+ * Q6_K x q8_1 matrix-vector product for 1..4 activation vectors, with an
+ * optional residual.  Same arguments and rules as kq_gemv_q4k except:
+ *   w   [m][k/256] Q6_K superblocks (210 bytes), 16-byte aligned; the row
+ *       stride 210*k/256 need not be a multiple of 16.
+ * y[t][r] = residual[t][r] + sum over blocks j of
+ *           d8[t][j] * sum over the block's two 16-value groups g of
+ *           d*sc_g * (sum of (q-32)*code over the group).
+ */
+int kq_gemv_q6k(const void* w, const void* xq, float* y, const float* residual,
+                int64_t m, int64_t k, int32_t batch, void* stream);
+
+/*
+ * Q4_K x q8_1 matrix-matrix product for n tokens on the int8 matrix cores.
+ *   w    [m][k/256] Q4_K superblocks, 16-byte aligned.
+ *   xq   [n][k/32] q8_1 blocks, 4-byte aligned.
+ *   y    out: f32 [n][m], 4-byte aligned; must not overlap w or xq.
+ *   m >= 0, n >= 0, k > 0, k % 256 == 0, k <= KQ_MAX_K.
+ * Same value per output as kq_gemv_q4k without a residual.
+ */
+int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
+               void* stream);
+
+/* Text of the last error on this host thread ("" if none). */
+const char* kq_last_error(void);
+
+/* Version of this ABI (incremented on any incompatible change). */
+int kq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQ_H_ */

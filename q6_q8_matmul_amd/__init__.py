@@ -1,0 +1,160 @@
+"""Python binding of libkq, the k-quant matmul for AMD MI355X (gfx950).
+
+Thin ``ctypes`` marshalling over the C ABI declared in ``include/kq.h``:
+every function below has the name of a C entry point, turns tensors into
+device pointers and the current torch stream into a ``hipStream_t``, calls
+the library and raises :class:`KQError` on a non-zero status.  All
+arithmetic runs in the library's gfx950 kernels; there is no other path.
+
+PyTorch (ROCm build) supplies device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkq.so")
+
+KQ_OK = 0
+KQ_ERR_ARG = -1
+KQ_ERR_UNSUPPORTED = -2
+KQ_ERR_HIP = -3
+
+Q4K_BYTES = 144
+Q6K_BYTES = 210
+Q81_BYTES = 36
+
+
+class KQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m q6_q8_matmul_amd.build` "
+                "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.kq_quantize_q8_1.argtypes = [p, p, i64, i64, p]
+        L.kq_gemv_q4k.argtypes = [p, p, p, p, i64, i64, i32, p]
+        L.kq_gemv_q6k.argtypes = [p, p, p, p, i64, i64, i32, p]
+        L.kq_mmq_q4k.argtypes = [p, p, p, i64, i64, i64, p]
+        for fn in (L.kq_quantize_q8_1, L.kq_gemv_q4k, L.kq_gemv_q6k, L.kq_mmq_q4k):
+            fn.restype = ctypes.c_int
+        L.kq_last_error.argtypes = []
+        L.kq_last_error.restype = ctypes.c_char_p
+        L.kq_abi_version.argtypes = []
+        L.kq_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    """Device address of a tensor (or pass an int/None through)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int) -> None:
+    if rc != KQ_OK:
+        raise KQError(rc, kq_last_error())
+
+
+# ------------------------------------------------------------- the C ABI ----
+
+def kq_last_error() -> str:
+    return lib().kq_last_error().decode()
+
+
+def kq_abi_version() -> int:
+    return int(lib().kq_abi_version())
+
+
+def kq_quantize_q8_1(x, xq, rows: int, k: int, stream=None) -> None:
+    _check(lib().kq_quantize_q8_1(_ptr(x), _ptr(xq), rows, k, _stream(stream)))
+
+
+def kq_gemv_q4k(w, xq, y, residual, m: int, k: int, batch: int, stream=None) -> None:
+    _check(lib().kq_gemv_q4k(_ptr(w), _ptr(xq), _ptr(y), _ptr(residual), m, k, batch,
+                             _stream(stream)))
+
+
+def kq_gemv_q6k(w, xq, y, residual, m: int, k: int, batch: int, stream=None) -> None:
+    _check(lib().kq_gemv_q6k(_ptr(w), _ptr(xq), _ptr(y), _ptr(residual), m, k, batch,
+                             _stream(stream)))
+
+
+def kq_mmq_q4k(w, xq, y, m: int, n: int, k: int, stream=None) -> None:
+    _check(lib().kq_mmq_q4k(_ptr(w), _ptr(xq), _ptr(y), m, n, k, _stream(stream)))
+
+
+# ------------------------------------------- allocating conveniences -------
+# These allocate the output with torch and call the entry point above.
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def quantize_q8_1(x, stream=None):
+    """f32 ``[rows, k]`` -> uint8 ``[rows, k/32*36]`` q8_1 tensor."""
+    import torch
+
+    _require_cuda(x)
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 tensor")
+    rows, k = x.shape
+    xq = torch.empty((rows, (k // 32) * Q81_BYTES), dtype=torch.uint8, device=x.device)
+    kq_quantize_q8_1(x, xq, rows, k, stream)
+    return xq
+
+
+def gemv_q4k(w, xq, m: int, k: int, batch: int, residual=None, out=None, stream=None):
+    import torch
+
+    _require_cuda(w, xq, residual)
+    y = out if out is not None else torch.empty((batch, m), dtype=torch.float32, device=w.device)
+    kq_gemv_q4k(w, xq, y, residual, m, k, batch, stream)
+    return y
+
+
+def gemv_q6k(w, xq, m: int, k: int, batch: int, residual=None, out=None, stream=None):
+    import torch
+
+    _require_cuda(w, xq, residual)
+    y = out if out is not None else torch.empty((batch, m), dtype=torch.float32, device=w.device)
+    kq_gemv_q6k(w, xq, y, residual, m, k, batch, stream)
+    return y
+
+
+def mmq_q4k(w, xq, m: int, n: int, k: int, out=None, stream=None):
+    import torch
+
+    _require_cuda(w, xq)
+    y = out if out is not None else torch.empty((n, m), dtype=torch.float32, device=w.device)
+    kq_mmq_q4k(w, xq, y, m, n, k, stream)
+    return y

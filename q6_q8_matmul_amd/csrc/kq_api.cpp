@@ -1,0 +1,175 @@
+// kq_api.cpp -- the C ABI of libkq (declared in include/kq.h).
+//
+// Every entry point validates its arguments before touching the HIP runtime,
+// checks that the current device is a gfx950 GPU, launches exactly one kernel
+// on the caller's stream and reports the launch status.  Invariant
+// violations return an error that names the offending values; nothing falls
+// back to another path (minfer "The CUDA backend" 3.4: a violated invariant
+// is an error with the values, never a silent detour).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/kq.h"
+#include "kq_device.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return KQ_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// [a, a+na) and [b, b+nb) intersect
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return na > 0 && nb > 0 && x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+// Per device: 0 unknown, 1 gfx950, -1 other.  Also the LDS limit per block.
+std::atomic<int> g_arch[64];
+std::atomic<int> g_lds[64];
+
+int check_device(const char* fn, int* lds_limit) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0)
+        return fail(KQ_ERR_UNSUPPORTED, "%s: no HIP device (%s)", fn, hipGetErrorString(e));
+    if (dev >= 64) return fail(KQ_ERR_UNSUPPORTED, "%s: device index %d out of range", fn, dev);
+    int state = g_arch[dev].load(std::memory_order_acquire);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(KQ_ERR_UNSUPPORTED, "%s: hipGetDeviceProperties(%d) failed: %s", fn, dev,
+                        hipGetErrorString(e));
+        state = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        g_lds[dev].store((int)prop.sharedMemPerBlock, std::memory_order_relaxed);
+        g_arch[dev].store(state, std::memory_order_release);
+        if (state < 0)
+            return fail(KQ_ERR_UNSUPPORTED, "%s: device %d is %s, not gfx950", fn, dev,
+                        prop.gcnArchName);
+    }
+    if (state < 0) return fail(KQ_ERR_UNSUPPORTED, "%s: device %d is not gfx950", fn, dev);
+    if (lds_limit) *lds_limit = g_lds[dev].load(std::memory_order_relaxed);
+    return KQ_OK;
+}
+
+int launched(const char* fn, hipError_t e) {
+    if (e != hipSuccess) return fail(KQ_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+int check_k(const char* fn, int64_t k, int64_t mult) {
+    if (k <= 0 || k % mult != 0 || k > KQ_MAX_K)
+        return fail(KQ_ERR_ARG, "%s: k=%lld must be a positive multiple of %lld and <= %d", fn,
+                    (long long)k, (long long)mult, KQ_MAX_K);
+    return KQ_OK;
+}
+
+int gemv_common(const char* fn, int wbytes, const void* w, const void* xq, float* y,
+                const float* residual, int64_t m, int64_t k, int32_t batch) {
+    if (!w || !xq || !y)
+        return fail(KQ_ERR_ARG, "%s: null pointer (w=%p xq=%p y=%p)", fn, w, xq, (void*)y);
+    if (int rc = check_k(fn, k, 256)) return rc;
+    if (m < 0 || m > KQ_MAX_ROWS)
+        return fail(KQ_ERR_ARG, "%s: m=%lld out of range [0, %d]", fn, (long long)m, KQ_MAX_ROWS);
+    if (batch < 1 || batch > 4)
+        return fail(KQ_ERR_ARG, "%s: batch=%d must be in [1, 4]", fn, (int)batch);
+    if (!aligned(w, 16) || !aligned(xq, 4) || !aligned(y, 4) || (residual && !aligned(residual, 4)))
+        return fail(KQ_ERR_ARG, "%s: misaligned pointer (w=%p needs 16, xq=%p y=%p residual=%p need 4)",
+                    fn, w, xq, (void*)y, (const void*)residual);
+    const int64_t wn = m * (k / 256) * wbytes;
+    const int64_t xn = (int64_t)batch * (k / 32) * 36;
+    const int64_t yn = (int64_t)batch * m * 4;
+    if (overlap(y, yn, w, wn) || overlap(y, yn, xq, xn))
+        return fail(KQ_ERR_ARG, "%s: output y=%p overlaps an input (w=%p, xq=%p)", fn, (void*)y, w, xq);
+    if (residual && residual != y && overlap(y, yn, residual, yn))
+        return fail(KQ_ERR_ARG, "%s: y=%p partially overlaps residual=%p", fn, (void*)y,
+                    (const void*)residual);
+    return KQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kq_quantize_q8_1(const float* x, void* xq, int64_t rows, int64_t k, void* stream) {
+    const char* fn = "kq_quantize_q8_1";
+    if (!x || !xq) return fail(KQ_ERR_ARG, "%s: null pointer (x=%p xq=%p)", fn, (const void*)x, xq);
+    if (int rc = check_k(fn, k, 32)) return rc;
+    if (rows < 0 || rows > KQ_MAX_ROWS)
+        return fail(KQ_ERR_ARG, "%s: rows=%lld out of range [0, %d]", fn, (long long)rows, KQ_MAX_ROWS);
+    if (rows * k / 1024 >= 0x7fffffffLL)
+        return fail(KQ_ERR_ARG, "%s: rows*k=%lld too large for one launch", fn, (long long)(rows * k));
+    if (!aligned(x, 16) || !aligned(xq, 4))
+        return fail(KQ_ERR_ARG, "%s: misaligned pointer (x=%p needs 16, xq=%p needs 4)", fn,
+                    (const void*)x, xq);
+    if (overlap(x, rows * k * 4, xq, rows * (k / 32) * 36))
+        return fail(KQ_ERR_ARG, "%s: xq=%p overlaps x=%p", fn, xq, (const void*)x);
+    if (rows == 0) return ok();
+    if (int rc = check_device(fn, nullptr)) return rc;
+    return launched(fn, kq::launch_quantize_q8_1(x, xq, rows, k, (hipStream_t)stream));
+}
+
+int kq_gemv_q4k(const void* w, const void* xq, float* y, const float* residual, int64_t m,
+                int64_t k, int32_t batch, void* stream) {
+    const char* fn = "kq_gemv_q4k";
+    if (int rc = gemv_common(fn, 144, w, xq, y, residual, m, k, batch)) return rc;
+    if (m == 0) return ok();
+    int lds = 0;
+    if (int rc = check_device(fn, &lds)) return rc;
+    return launched(fn, kq::launch_gemv_q4k(w, xq, y, residual, m, k, batch, lds, (hipStream_t)stream));
+}
+
+int kq_gemv_q6k(const void* w, const void* xq, float* y, const float* residual, int64_t m,
+                int64_t k, int32_t batch, void* stream) {
+    const char* fn = "kq_gemv_q6k";
+    if (int rc = gemv_common(fn, 210, w, xq, y, residual, m, k, batch)) return rc;
+    if (m == 0) return ok();
+    int lds = 0;
+    if (int rc = check_device(fn, &lds)) return rc;
+    return launched(fn, kq::launch_gemv_q6k(w, xq, y, residual, m, k, batch, lds, (hipStream_t)stream));
+}
+
+int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
+               void* stream) {
+    const char* fn = "kq_mmq_q4k";
+    if (!w || !xq || !y)
+        return fail(KQ_ERR_ARG, "%s: null pointer (w=%p xq=%p y=%p)", fn, w, xq, (void*)y);
+    if (int rc = check_k(fn, k, 256)) return rc;
+    if (m < 0 || m > KQ_MAX_ROWS || n < 0 || n > 65535LL * 128)
+        return fail(KQ_ERR_ARG, "%s: m=%lld or n=%lld out of range (m <= %d, n <= %lld)", fn,
+                    (long long)m, (long long)n, KQ_MAX_ROWS, 65535LL * 128);
+    if (!aligned(w, 16) || !aligned(xq, 4) || !aligned(y, 4))
+        return fail(KQ_ERR_ARG, "%s: misaligned pointer (w=%p needs 16, xq=%p y=%p need 4)", fn, w,
+                    xq, (void*)y);
+    const int64_t yn = n * m * 4;
+    if (overlap(y, yn, w, m * (k / 256) * 144) || overlap(y, yn, xq, n * (k / 32) * 36))
+        return fail(KQ_ERR_ARG, "%s: output y=%p overlaps an input (w=%p, xq=%p)", fn, (void*)y, w, xq);
+    if (m == 0 || n == 0) return ok();
+    if (int rc = check_device(fn, nullptr)) return rc;
+    return launched(fn, kq::launch_mmq_q4k(w, xq, y, m, n, k, (hipStream_t)stream));
+}
+
+const char* kq_last_error(void) { return g_err; }
+
+int kq_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+// mmq_q4k.hip -- Q4_K x q8_1 matrix-matrix product on the int8 matrix cores.
+//
+// minfer "The CUDA backend" 2.3 describes the method: the weights are never
+// dequantised -- their raw block bytes are staged in on-chip memory and
+// decoded in registers where the integer matrix instruction needs them; the
+// activations are quantised once per call by a prepass; the integer tile
+// product accumulates exactly in int32; the float scales are applied after
+// the integer loop.  On gfx950 one v_mfma_i32_32x32x32_i8 covers K = 32, i.e.
+// exactly one q8_1 block, so every MFMA result is the integer dot A of one
+// (weight row, token, 32-block) and receives its own scale:
+//     T = d8 * (D * A - Mn * Bq),  D = d*sc, Mn = dmin*m, Bq = sum of q8 codes.
+//
+// Tiling: a workgroup (4 wavefronts, 2 x 2) computes 128 weight rows x 128
+// tokens; each wavefront a 64 x 64 block of four 32 x 32 MFMA tiles.  The K
+// loop walks one superblock (256 values, 8 q8_1 blocks) at a time:
+//   * raw Q4_K superblocks of the 128 rows -> LDS (16-byte loads);
+//     per row and sub-block the f32 pair (D, Mn) -> LDS;
+//   * q8_1 blocks of the 128 tokens -> LDS as int8 codes (rows padded to
+//     272 bytes against bank conflicts) plus per (token, block) d8 and
+//     d8*Bq;
+//   * per block: nibbles -> int8 operand in registers, 4 MFMAs, scale
+//     epilogue into a per-superblock f32 partial; the partials are added to
+//     the output accumulator once per superblock, so each output sees about
+//     8 + k/256 f32 additions in sequence.
+// Outputs beyond m or n are computed from clamped (valid) rows/tokens and not
+// stored.  No atomics; results are bitwise reproducible.
+#include "kq_device.h"
+
+namespace kq {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 128;            // weight rows per workgroup
+constexpr int BN = 128;            // tokens per workgroup
+constexpr int kCodeStride = 272;   // LDS bytes per token row of codes (256 + 16 pad)
+
+struct Smem {
+    uint8_t wraw[BM * kQ4KBytes];        // raw superblocks, 144 bytes per row
+    float dsc[8][BM];                    // D = d*sc   per (block, row)
+    float msc[8][BM];                    // Mn = dmin*m per (block, row)
+    int8_t codes[BN * kCodeStride];      // q8 codes per token
+    float d8[BN][8];                     // per (token, block)
+    float z[BN][8];                      // d8 * Bq
+};
+
+__global__ __launch_bounds__(256) void mmq_q4k_kernel(const uint8_t* __restrict__ w,
+                                                      const uint8_t* __restrict__ xq,
+                                                      float* __restrict__ y, int M, int N,
+                                                      int S) {
+    __shared__ __align__(16) Smem sm;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;  // wave position in the 2 x 2 grid
+    const int l32 = lane & 31, h2 = lane >> 5;
+    const int m0 = blockIdx.x * BM;
+    const int n0 = blockIdx.y * BN;
+    const int64_t row_bytes = (int64_t)S * kQ4KBytes;
+    const int nb_row = S * 8;
+
+    float acc[2][2][16];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+    for (int sb = 0; sb < S; ++sb) {
+        // ---- stage raw weights: 128 rows x 9 chunks of 16 bytes
+        for (int idx = tid; idx < BM * 9; idx += 256) {
+            const int r = idx / 9, ch = idx - r * 9;
+            const int gr = min(m0 + r, M - 1);
+            const uint4 v = *(const uint4*)(w + (int64_t)gr * row_bytes + (int64_t)sb * kQ4KBytes + 16 * ch);
+            *(uint4*)(sm.wraw + r * kQ4KBytes + 16 * ch) = v;
+        }
+        // ---- (D, Mn) per row and sub-block, from the header
+        if (tid < BM) {
+            const int gr = min(m0 + tid, M - 1);
+            const uint4 hd = *(const uint4*)(w + (int64_t)gr * row_bytes + (int64_t)sb * kQ4KBytes);
+            const float d = half_bits_to_float(hd.x), dmin = half_bits_to_float(hd.x >> 16);
+            const uint32_t lowS = hd.y & 0x3f3f3f3fu, lowM = hd.z & 0x3f3f3f3fu;
+            const uint32_t hiS = (hd.w & 0x0f0f0f0fu) | ((hd.y >> 2) & 0x30303030u);
+            const uint32_t hiM = ((hd.w >> 4) & 0x0f0f0f0fu) | ((hd.z >> 2) & 0x30303030u);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t s4 = j < 4 ? lowS : hiS, m4 = j < 4 ? lowM : hiM;
+                const int sh = 8 * (j & 3);
+                sm.dsc[j][tid] = d * (float)((s4 >> sh) & 0xff);
+                sm.msc[j][tid] = dmin * (float)((m4 >> sh) & 0xff);
+            }
+        }
+        // ---- activations: 128 tokens x 8 q8_1 blocks
+        for (int idx = tid; idx < BN * 8; idx += 256) {
+            const int t = idx >> 3, j = idx & 7;
+            const int gt = min(n0 + t, N - 1);
+            const uint32_t* blk = (const uint32_t*)(xq + ((int64_t)gt * nb_row + sb * 8 + j) * kQ81Bytes);
+            uint32_t c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = blk[1 + i];
+            int s = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s = dot4(c[i], 0x01010101u, s);
+            const float d8 = half_bits_to_float(blk[0]);
+            uint4* dst = (uint4*)(sm.codes + t * kCodeStride + 32 * j);
+            dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
+            dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
+            sm.d8[t][j] = d8;
+            sm.z[t][j] = d8 * (float)s;
+        }
+        __syncthreads();
+
+        float part[2][2][16];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) part[a][b][i] = 0.0f;
+
+#pragma unroll 2
+        for (int j = 0; j < 8; ++j) {
+            const int c = j >> 1, hi = j & 1;
+            // A operands: weight rows (l32) of the wave's two 32-row tiles
+            v4i A[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const int r = wm * 64 + mt * 32 + l32;
+                const uint4 q = *(const uint4*)(sm.wraw + r * kQ4KBytes + 16 + 32 * c + 16 * h2);
+                const uint32_t sft = hi ? 4u : 0u;
+                A[mt] = v4i{(int)((q.x >> sft) & 0x0f0f0f0fu), (int)((q.y >> sft) & 0x0f0f0f0fu),
+                            (int)((q.z >> sft) & 0x0f0f0f0fu), (int)((q.w >> sft) & 0x0f0f0f0fu)};
+            }
+            // B operands: tokens (l32) of the wave's two 32-token tiles
+            v4i B[2];
+            float d8n[2], zn[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int t = wn * 64 + nt * 32 + l32;
+                const uint4 a = *(const uint4*)(sm.codes + t * kCodeStride + 32 * j + 16 * h2);
+                B[nt] = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+                d8n[nt] = sm.d8[t][j];
+                zn[nt] = sm.z[t][j];
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                // rows of this lane's 16 outputs: 8*(i/4) + 4*h2 + (i%4)
+                float Dm[16], Mm[16];
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int rb = wm * 64 + mt * 32 + 8 * a4 + 4 * h2;
+                    const float4 dv = *(const float4*)&sm.dsc[j][rb];
+                    const float4 mv = *(const float4*)&sm.msc[j][rb];
+                    Dm[4 * a4 + 0] = dv.x; Dm[4 * a4 + 1] = dv.y; Dm[4 * a4 + 2] = dv.z; Dm[4 * a4 + 3] = dv.w;
+                    Mm[4 * a4 + 0] = mv.x; Mm[4 * a4 + 1] = mv.y; Mm[4 * a4 + 2] = mv.z; Mm[4 * a4 + 3] = mv.w;
+                }
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+                    const v16i r = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mt], B[nt], zero, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float s = Dm[i] * d8n[nt];
+                        part[mt][nt][i] += (float)r[i] * s - Mm[i] * zn[nt];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[a][b][i] += part[a][b][i];
+        __syncthreads();
+    }
+
+    // ---- store: lane holds token (l32) and 16 rows of each tile
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int n = n0 + wn * 64 + nt * 32 + l32;
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = m0 + wm * 64 + mt * 32 + 8 * (i >> 2) + 4 * h2 + (i & 3);
+                if (m < M) y[(int64_t)n * M + m] = acc[mt][nt][i];
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
+                          int64_t k, hipStream_t stream) {
+    const int S = (int)(k / kQK);
+    dim3 grid((unsigned)((m + BM - 1) / BM), (unsigned)((n + BN - 1) / BN));
+    hipLaunchKernelGGL(mmq_q4k_kernel, grid, dim3(256), 0, stream, (const uint8_t*)w,
+                       (const uint8_t*)xq, y, (int)m, (int)n, S);
+    return hipGetLastError();
+}
+
+}  // namespace kq

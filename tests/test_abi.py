@@ -1,0 +1,140 @@
+"""The C ABI library loads, exports what include/kq.h declares, and rejects
+bad arguments before touching the GPU.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "kq.h")
+
+
+@pytest.fixture(scope="module")
+def kq():
+    import q6_q8_matmul_amd as kq
+    from q6_q8_matmul_amd import build
+
+    if not os.path.exists(kq.LIB_PATH):
+        build.build()
+    kq.lib()
+    return kq
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kq_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "kq_quantize_q8_1", "kq_gemv_q4k", "kq_gemv_q6k", "kq_mmq_q4k",
+        "kq_last_error", "kq_abi_version"])
+
+
+def test_library_exports_every_declared_symbol(kq):
+    lib = ctypes.CDLL(kq.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_abi_version(kq):
+    assert kq.kq_abi_version() == 1
+
+
+# Fake, aligned, never-dereferenced addresses: every call below fails argument
+# validation, which runs before any HIP call.
+W = 0x10000
+X = 0x20000
+Y = 0x40000
+R = 0x80000
+
+
+def _rc(fn, *args):
+    return fn(*args)
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((None, X, 1, 256, None), "null pointer"),
+    ((W, None, 1, 256, None), "null pointer"),
+    ((W, X, 1, 0, None), "k=0"),
+    ((W, X, 1, 48, None), "k=48"),
+    ((W, X, 1, 65536 + 32, None), "k=65568"),
+    ((W, X, -1, 256, None), "rows=-1"),
+    ((W + 4, X, 1, 256, None), "misaligned"),
+    ((W, X + 2, 1, 256, None), "misaligned"),
+    ((W, W + 64, 1, 256, None), "overlaps"),
+])
+def test_quantize_rejects(kq, args, needle):
+    rc = kq.lib().kq_quantize_q8_1(*args)
+    assert rc == kq.KQ_ERR_ARG
+    assert needle in kq.kq_last_error()
+    assert "kq_quantize_q8_1" in kq.kq_last_error()
+
+
+@pytest.mark.parametrize("fn", ["kq_gemv_q4k", "kq_gemv_q6k"])
+@pytest.mark.parametrize("args,needle", [
+    ((None, X, Y, None, 8, 256, 1, None), "null pointer"),
+    ((W, X, None, None, 8, 256, 1, None), "null pointer"),
+    ((W, X, Y, None, 8, 128, 1, None), "k=128"),
+    ((W, X, Y, None, 8, 256 * 257, 1, None), "k="),
+    ((W, X, Y, None, -3, 256, 1, None), "m=-3"),
+    ((W, X, Y, None, 8, 256, 0, None), "batch=0"),
+    ((W, X, Y, None, 8, 256, 5, None), "batch=5"),
+    ((W + 8, X, Y, None, 8, 256, 1, None), "misaligned"),
+    ((W, X + 1, Y, None, 8, 256, 1, None), "misaligned"),
+    ((W, X, Y + 2, None, 8, 256, 1, None), "misaligned"),
+    ((W, X, Y, R + 2, 8, 256, 1, None), "misaligned"),
+    ((W, X, W + 16, None, 8, 256, 1, None), "overlaps"),
+    ((W, X, X, None, 8, 256, 1, None), "overlaps"),
+    ((W, X, Y, Y + 4, 8, 256, 1, None), "partially overlaps"),
+])
+def test_gemv_rejects(kq, fn, args, needle):
+    rc = getattr(kq.lib(), fn)(*args)
+    assert rc == kq.KQ_ERR_ARG, kq.kq_last_error()
+    assert needle in kq.kq_last_error()
+    assert fn in kq.kq_last_error()
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((None, X, Y, 8, 8, 256, None), "null pointer"),
+    ((W, X, Y, 8, 8, 100, None), "k=100"),
+    ((W, X, Y, -1, 8, 256, None), "m=-1"),
+    ((W, X, Y, 8, -1, 256, None), "n=-1"),
+    ((W, X, Y, 8, 65535 * 128 + 1, 256, None), "out of range"),
+    ((W + 4, X, Y, 8, 8, 256, None), "misaligned"),
+    ((W, X, W, 8, 8, 256, None), "overlaps"),
+])
+def test_mmq_rejects(kq, args, needle):
+    rc = kq.lib().kq_mmq_q4k(*args)
+    assert rc == kq.KQ_ERR_ARG, kq.kq_last_error()
+    assert needle in kq.kq_last_error()
+
+
+def test_empty_inputs_launch_nothing(kq):
+    # zero rows / tokens are valid and return before any device access
+    L = kq.lib()
+    assert L.kq_quantize_q8_1(W, X, 0, 256, None) == kq.KQ_OK
+    assert L.kq_gemv_q4k(W, X, Y, None, 0, 256, 1, None) == kq.KQ_OK
+    assert L.kq_gemv_q6k(W, X, Y, None, 0, 256, 4, None) == kq.KQ_OK
+    assert L.kq_mmq_q4k(W, X, Y, 0, 16, 256, None) == kq.KQ_OK
+    assert L.kq_mmq_q4k(W, X, Y, 16, 0, 256, None) == kq.KQ_OK
+
+
+def test_binding_raises_with_message(kq):
+    with pytest.raises(kq.KQError, match="batch=7"):
+        kq.kq_gemv_q4k(W, X, Y, None, 8, 256, 7, stream=0)
+
+
+def test_no_gpu_means_unsupported(kq):
+    """Valid arguments on a host without a gfx950 device: KQ_ERR_UNSUPPORTED,
+    nothing launched.  Only meaningful where no GPU is visible."""
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible")
+    rc = kq.lib().kq_gemv_q4k(W, X, Y, None, 8, 256, 1, None)
+    assert rc == kq.KQ_ERR_UNSUPPORTED
+    assert "kq_gemv_q4k" in kq.kq_last_error()

@@ -1,0 +1,275 @@
+"""Parity of the gfx950 kernels with the CPU oracle, through the C ABI.
+
+* q8_1 quantisation: bit-exact (codes, f16 scale, f16 source sum).
+* matmuls: |y_gpu - y_oracle| <= 1e-5 * (sum_j |T_j| + |residual|) for every
+  output checked, T_j being the oracle's per-32-block term (f64).
+GEMVs are checked on every output at the workloads' full sizes; the prefill
+MMQ is checked on every output at sizes spanning several tiles with ragged
+edges, and on sampled outputs (tile corners plus random picks) at the
+prefill workload's full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kq_inputs import WORKLOADS, random_case, tensor
+from oracle_pins import _adversarial_blocks, _distinguishing_blocks
+
+pytestmark = pytest.mark.gpu
+RTOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def kq():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    import q6_q8_matmul_amd as kq
+
+    kq.lib()
+    oracle.build(force=False)
+    return kq
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def check_close(y_gpu, y_ref, den, label):
+    ok, ratio = oracle.tolerance_ok(y_gpu, y_ref, den, RTOL)
+    say(f"{label}: max |gpu-oracle|/den = {ratio:.3e}")
+    assert ok, f"{label}: tolerance exceeded, max ratio {ratio:.3e} > {RTOL}"
+
+
+# ------------------------------------------------------------ quantiser ----
+
+ACTS = [(c, name) for c, wl in WORKLOADS.items() for (name, kind, *_r) in wl["tensors"]
+        if kind == "act"]
+
+
+@pytest.mark.parametrize("cfg,name", ACTS, ids=[f"cfg{c}-{n}" for c, n in ACTS])
+def test_quantize_bitexact_workloads(kq, cfg, name):
+    x = tensor(cfg, name)
+    say(f"quantize cfg{cfg} {name} {x.shape}")
+    ref = oracle.quantize_q8_1(x)
+    got = host(kq.quantize_q8_1(dev(x)))
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} bytes differ"
+
+
+def test_quantize_bitexact_adversarial(kq):
+    blocks = np.concatenate([_adversarial_blocks(), _distinguishing_blocks()]).astype(np.float32)
+    rng = np.random.default_rng(3)
+    extra = [
+        (rng.standard_normal((64, 32)) * 2.0 ** -20).astype(np.float32),  # f16-subnormal d
+        (rng.standard_normal((64, 32)) * 6e4).astype(np.float32),         # large values
+        np.full((2, 32), -0.0, dtype=np.float32),
+    ]
+    x = np.concatenate([blocks] + extra)
+    n = (x.shape[0] // 8) * 8
+    x = x[:n].reshape(-1, 256)
+    say(f"quantize adversarial {x.shape}")
+    ref = oracle.quantize_q8_1(x)
+    got = host(kq.quantize_q8_1(dev(x)))
+    bad = np.nonzero((got != ref).any(axis=1))[0]
+    assert bad.size == 0, f"rows {bad[:5]} differ"
+
+
+@pytest.mark.parametrize("rows,k", [(1, 32), (3, 96), (5, 256), (7, 4128), (1000, 64)])
+def test_quantize_ragged(kq, rows, k):
+    x = np.random.default_rng(rows * 7 + k).standard_normal((rows, k)).astype(np.float32)
+    say(f"quantize ragged rows={rows} k={k}")
+    assert np.array_equal(host(kq.quantize_q8_1(dev(x))), oracle.quantize_q8_1(x))
+
+
+# --------------------------------------------------------------- GEMVs -----
+
+def run_gemv(kq, kind, w, xq, m, k, batch, res=None, inplace=False):
+    wd, xd = dev(w), dev(xq)
+    rd = dev(res) if res is not None else None
+    fn = kq.gemv_q4k if kind == "q4k" else kq.gemv_q6k
+    if inplace:
+        y = fn(wd, xd, m, k, batch, residual=rd, out=rd)
+    else:
+        y = fn(wd, xd, m, k, batch, residual=rd)
+    return host(y)
+
+
+GEMV_OPS = [(c, i) for c in (0, 1, 2, 3) for i in range(len(WORKLOADS[c]["ops"]))]
+
+
+@pytest.mark.parametrize("cfg,i", GEMV_OPS,
+                         ids=[f"cfg{c}-{WORKLOADS[c]['ops'][i]['label']}" for c, i in GEMV_OPS])
+def test_gemv_workloads_full(kq, cfg, i):
+    op = WORKLOADS[cfg]["ops"][i]
+    kind = "q4k" if op["op"] == "gemv_q4k" else "q6k"
+    m, k, b = op["m"], op["k"], op["batch"]
+    say(f"gemv {kind} cfg{cfg} {op['label']} m={m} k={k} batch={b}")
+    w = tensor(cfg, op["w"])
+    x = tensor(cfg, op["x"])
+    res = tensor(cfg, op["residual"]) if "residual" in op else None
+    xq = oracle.quantize_q8_1(x)
+    y_ref, den = oracle.matmul(kind, w, xq, m, b, k, residual=res)
+    y = run_gemv(kq, kind, w, xq, m, k, b, res)
+    check_close(y, y_ref, den, f"cfg{cfg} {op['label']}")
+
+
+SHAPES = [
+    # kind, m, k, batch, residual -- ragged rows, one superblock, odd superblock
+    # counts (Q6_K superblocks at 2 mod 4), several LDS chunks (k*batch large)
+    ("q4k", 1, 256, 1, False), ("q4k", 7, 768, 3, True), ("q4k", 13, 2304, 2, False),
+    ("q4k", 1000, 1024, 4, True), ("q4k", 37, 14336, 4, True), ("q4k", 9, 32768, 4, False),
+    ("q4k", 300, 4352, 1, False),
+    ("q6k", 1, 256, 1, False), ("q6k", 7, 768, 3, True), ("q6k", 13, 2304, 2, False),
+    ("q6k", 1001, 1280, 4, True), ("q6k", 37, 14336, 4, True), ("q6k", 9, 32768, 4, False),
+    ("q6k", 300, 4352, 1, False),
+]
+
+
+@pytest.mark.parametrize("kind,m,k,batch,with_res", SHAPES,
+                         ids=[f"{s[0]}-m{s[1]}-k{s[2]}-b{s[3]}{'-res' if s[4] else ''}" for s in SHAPES])
+def test_gemv_shapes(kq, kind, m, k, batch, with_res):
+    say(f"gemv {kind} m={m} k={k} batch={batch} residual={with_res}")
+    w, x, res = random_case(m * 131 + k + batch, kind, m, k, batch, with_residual=with_res)
+    xq = oracle.quantize_q8_1(x)
+    y_ref, den = oracle.matmul(kind, w, xq, m, batch, k, residual=res)
+    check_close(run_gemv(kq, kind, w, xq, m, k, batch, res), y_ref, den, f"{kind} m{m} k{k} b{batch}")
+
+
+@pytest.mark.parametrize("kind", ["q4k", "q6k"])
+def test_gemv_in_place_residual(kq, kind):
+    m, k, b = 333, 4096, 4
+    say(f"gemv {kind} in place m={m} k={k} batch={b}")
+    w, x, res = random_case(77, kind, m, k, b, with_residual=True)
+    xq = oracle.quantize_q8_1(x)
+    y_ref, den = oracle.matmul(kind, w, xq, m, b, k, residual=res)
+    check_close(run_gemv(kq, kind, w, xq, m, k, b, res, inplace=True), y_ref, den, "in place")
+
+
+@pytest.mark.parametrize("kind", ["q4k", "q6k"])
+@pytest.mark.parametrize("k", [4096, 14336])
+def test_gemv_batch_columns(kq, kind, k):
+    """Column b of a batch-4 call against the batch-1 call on x_b: bitwise
+    where both stage the activation in one piece, else within tolerance."""
+    m = 515
+    say(f"gemv {kind} batch columns m={m} k={k}")
+    w, x, _ = random_case(88 + k, kind, m, k, 4)
+    xq = oracle.quantize_q8_1(x)
+    y4 = run_gemv(kq, kind, w, xq, m, k, 4)
+    y_ref, den = oracle.matmul(kind, w, xq, m, 4, k)
+    for b in range(4):
+        y1 = run_gemv(kq, kind, w, xq[b:b + 1], m, k, 1)[0]
+        if k == 4096:
+            assert np.array_equal(y1, y4[b]), f"column {b} differs bitwise"
+        check_close(y1, y_ref[b], den[b], f"column {b} batch-1")
+
+
+@pytest.mark.parametrize("kind", ["q4k", "q6k"])
+def test_gemv_deterministic(kq, kind):
+    m, k, b = 4096, 4096, 4
+    say(f"gemv {kind} determinism m={m} k={k} batch={b}")
+    w, x, _ = random_case(5, kind, m, k, b)
+    xq = oracle.quantize_q8_1(x)
+    wd, xd = dev(w), dev(xq)
+    fn = kq.gemv_q4k if kind == "q4k" else kq.gemv_q6k
+    a = host(fn(wd, xd, m, k, b))
+    for _ in range(3):
+        assert np.array_equal(a, host(fn(wd, xd, m, k, b)))
+
+
+# ----------------------------------------------------------------- MMQ -----
+
+MMQ_SHAPES = [(1, 1, 256), (5, 3, 512), (128, 128, 256), (200, 150, 1024), (129, 257, 768),
+              (300, 64, 3584), (64, 300, 2048)]
+
+
+@pytest.mark.parametrize("m,n,k", MMQ_SHAPES, ids=[f"m{m}-n{n}-k{k}" for m, n, k in MMQ_SHAPES])
+def test_mmq_full(kq, m, n, k):
+    say(f"mmq m={m} n={n} k={k}")
+    w, x, _ = random_case(m + 3 * n + k, "q4k", m, k, n)
+    xq = oracle.quantize_q8_1(x)
+    y_ref, den = oracle.matmul("q4k", w, xq, m, n, k)
+    y = host(kq.mmq_q4k(dev(w), dev(xq), m, n, k))
+    check_close(y, y_ref, den, f"mmq m{m} n{n} k{k}")
+
+
+def _sample_pairs(m, n, rng, nrand=1500):
+    edge_r = sorted({0, 1, 31, 32, 63, 64, 127, 128, 129, m // 2, m - 129, m - 128, m - 2, m - 1})
+    edge_t = sorted({0, 1, 31, 32, 64, 127, 128, n // 2, n - 129, n - 1})
+    edge_r = [r for r in edge_r if 0 <= r < m]
+    edge_t = [t for t in edge_t if 0 <= t < n]
+    tok = [t for t in edge_t for _ in edge_r] + list(rng.integers(0, n, nrand))
+    row = [r for _ in edge_t for r in edge_r] + list(rng.integers(0, m, nrand))
+    return np.array(tok, dtype=np.int64), np.array(row, dtype=np.int64)
+
+
+MMQ_OPS = list(range(len(WORKLOADS[4]["ops"])))
+
+
+@pytest.mark.parametrize("i", MMQ_OPS, ids=[WORKLOADS[4]["ops"][i]["label"] for i in MMQ_OPS])
+def test_mmq_prefill_sampled(kq, i):
+    op = WORKLOADS[4]["ops"][i]
+    m, n, k = op["m"], op["n"], op["k"]
+    say(f"mmq cfg4 {op['label']} m={m} n={n} k={k} (sampled)")
+    w = tensor(4, op["w"])
+    x = tensor(4, op["x"])
+    xq_ref = oracle.quantize_q8_1(x)
+    xd = dev(x)
+    xq = kq.quantize_q8_1(xd)              # the path as the bench runs it
+    assert np.array_equal(host(xq), xq_ref)
+    y = host(kq.mmq_q4k(dev(w), xq, m, n, k))
+    tok, row = _sample_pairs(m, n, np.random.default_rng(i))
+    y_ref, den = oracle.matmul_pairs("q4k", w, xq_ref, m, n, k, tok, row)
+    check_close(y[tok, row], y_ref, den, f"cfg4 {op['label']} ({tok.size} outputs)")
+    assert np.all(np.isfinite(y))
+
+
+def test_mmq_matches_gemv_columns(kq):
+    m, n, k = 777, 5, 4096
+    say(f"mmq vs gemv m={m} n={n} k={k}")
+    w, x, _ = random_case(99, "q4k", m, k, n)
+    xq = oracle.quantize_q8_1(x)
+    wd, xd = dev(w), dev(xq)
+    y = host(kq.mmq_q4k(wd, xd, m, n, k))
+    y_ref, den = oracle.matmul("q4k", w, xq, m, n, k)
+    for t in range(n):
+        g = host(kq.gemv_q4k(wd, xd[t:t + 1], m, k, 1))[0]
+        check_close(g, y_ref[t], den[t], f"gemv token {t}")
+        check_close(y[t], y_ref[t], den[t], f"mmq token {t}")
+
+
+def test_mmq_deterministic(kq):
+    m, n, k = 512, 256, 3584
+    say(f"mmq determinism m={m} n={n} k={k}")
+    w, x, _ = random_case(6, "q4k", m, k, n)
+    xq = oracle.quantize_q8_1(x)
+    wd, xd = dev(w), dev(xq)
+    a = host(kq.mmq_q4k(wd, xd, m, n, k))
+    for _ in range(3):
+        assert np.array_equal(a, host(kq.mmq_q4k(wd, xd, m, n, k)))
+
+
+# ------------------------------------------------------ error handling ------
+
+def test_bad_arguments_launch_nothing(kq):
+    say("argument errors on real buffers")
+    w, x, _ = random_case(1, "q4k", 64, 512, 2)
+    xq = dev(oracle.quantize_q8_1(x))
+    wd = dev(w)
+    y = torch.full((2, 64), 7.0, device="cuda")
+    for call in (
+        lambda: kq.kq_gemv_q4k(wd, xq, y, None, 64, 500, 2),
+        lambda: kq.kq_gemv_q4k(wd, xq, y, None, 64, 512, 5),
+        lambda: kq.kq_gemv_q6k(wd, xq, y, y[:, 1:], 64, 512, 2),
+        lambda: kq.kq_mmq_q4k(wd, xq, wd, 64, 2, 512),
+    ):
+        with pytest.raises(kq.KQError):
+            call()
+    assert torch.all(y == 7.0).item()
