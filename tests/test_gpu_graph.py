@@ -1,0 +1,53 @@
+"""HIP-graph capture of a decode step (what bench.py replays): every replay,
+interleaved with eager work and synchronisations, must reproduce the eager
+outputs bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replay_matches_eager():
+    import q6_q8_matmul_amd as kq
+    from kq_inputs import random_case
+
+    print("\n[case] graph replay: quantize + gemv_q4k + gemv_q6k(residual) + mmq_q4k", flush=True)
+    w4, x4, _ = random_case(1, "q4k", 1000, 4096, 4)
+    w6, _, res = random_case(2, "q6k", 700, 4096, 4, with_residual=True)
+    wm, xm, _ = random_case(3, "q4k", 300, 1024, 200)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    w4d, x4d, w6d, resd, wmd, xmd = d(w4), d(x4), d(w6), d(res), d(wm), d(xm)
+    xq = torch.empty((4, 4096 // 32 * 36), dtype=torch.uint8, device="cuda")
+    xqm = torch.empty((200, 1024 // 32 * 36), dtype=torch.uint8, device="cuda")
+    y4 = torch.empty((4, 1000), device="cuda")
+    y6 = torch.empty((4, 700), device="cuda")
+    ym = torch.empty((200, 300), device="cuda")
+
+    def step():
+        kq.kq_quantize_q8_1(x4d, xq, 4, 4096)
+        kq.kq_gemv_q4k(w4d, xq, y4, None, 1000, 4096, 4)
+        kq.kq_gemv_q6k(w6d, xq, y6, resd, 700, 4096, 4)
+        kq.kq_quantize_q8_1(xmd, xqm, 200, 1024)
+        kq.kq_mmq_q4k(wmd, xqm, ym, 300, 200, 1024)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (xq, y4, y6, ym)]
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        step()
+    for rep in range(4):
+        for t in (xq, y4, y6, ym):
+            t.zero_()                       # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (xq, y4, y6, ym)):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
+        step()                              # eager again, still identical
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (xq, y4, y6, ym)):
+            assert torch.equal(a, b)
