@@ -6,9 +6,9 @@ TOPS (fraction of int8 MFMA peak).
 
 A step is one Llama-3-8B-shaped decode pass at batch 1 (workload
 "llama3_8b_decode_gemv_q4k_b1"): quantise the attention-output input and run
-attn-out 4096x4096; quantise the FFN input and run gate and up 14336x4096
-(one shared q8_1 activation); quantise the down input and run down
-4096x14336.  ``value`` is the weight bytes of that pass (108,527,616) per
+attn-out 4096x4096; quantise the FFN input and run gate and up 14336x4096 as
+one launch over their contiguous 28672 rows (one shared q8_1 activation);
+quantise the down input and run down 4096x14336.  ``value`` is the weight bytes of that pass (108,527,616) per
 second of step time.  The weights rotate over enough device copies that the
 footprint exceeds twice the 256 MB Infinity Cache, so every step streams its
 weights from HBM.  Inputs are resident in HBM before the timed region.
@@ -21,8 +21,10 @@ QKV 4608x3584).
 
 ``roofline`` describes the dominant kernel of the step, kq_gemv_q4k: its
 algorithmic bytes per launch (weights + q8_1 activation + f32 output) over
-its average launch duration, measured with HIP events recorded on the launch
-stream around every GEMV launch of an instrumented copy of the timed steps.
+its average launch duration.  Each launch of the step is timed on its own
+right after the timed steps: a HIP graph runs it back to back once per weight
+copy, and HIP events recorded on that stream around repeated replays give the
+average duration per launch.
 
 ``cpu_baseline`` times the CPU oracle on the host cores on the same step and
 also reports how far the GPU step outputs are from it.
@@ -68,10 +70,15 @@ class Workload:
         self.kq = kq
         self.cfg = cfg
         self.wl = WORKLOADS[cfg]
-        self.ops = self.wl["ops"]
+        self.ops = [dict(op) for op in self.wl.get("bench_ops", self.wl["ops"])]
         host = {}
         for name, kind, a, b in self.wl["tensors"]:
             host[name] = tensor(cfg, name)
+        for op in self.ops:              # row-concatenated weights share one launch
+            if isinstance(op["w"], list):
+                key = "|".join(op["w"])
+                host[key] = np.concatenate([host[n] for n in op["w"]], axis=0)
+                op["w"] = key
         self.host = host
         wnames = sorted({op["w"] for op in self.ops})
         self.weight_bytes_step = sum(host[op["w"]].nbytes for op in self.ops)
@@ -178,32 +185,39 @@ def timed_steps(wl: Workload, steps: int, warmup: int, graphs=None):
     return start.elapsed_time(end) / steps
 
 
-def kernel_durations(wl: Workload, steps: int):
-    """Average duration (ms) of every launch of the step, from HIP events
-    recorded on the launch stream around each launch; eager launches."""
+def kernel_durations(wl: Workload, target_ms: float = 20.0):
+    """Average duration (ms) of every launch of the step.  For each launch a
+    HIP graph holds it once per weight copy, back to back on one stream; the
+    graph is replayed between two HIP events recorded on the stream the
+    kernels run on, and the elapsed time is divided by the launch count."""
     import torch
 
-    stream = torch.cuda.current_stream()
-    labels = None
-    rec = []
-    for i in range(steps):
-        row = []
-        for label, kind, fn in wl.launches(i % wl.ncopies):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            row.append((label, kind, a, b))
-        rec.append(row)
-    torch.cuda.synchronize()
-    labels = [(l, k) for l, k, _, _ in rec[0]]
-    avg = []
-    for j, (label, kind) in enumerate(labels):
-        d = [r[j][2].elapsed_time(r[j][3]) for r in rec]
-        d.sort()
-        avg.append((label, kind, sum(d) / len(d), d[len(d) // 2]))
-    return avg
+    side = torch.cuda.Stream()
+    out = []
+    launches = wl.launches(0)
+    for j, (label, kind, _) in enumerate(launches):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for c in range(wl.ncopies):
+                wl.launches(c)[j][2]()
+        stream = torch.cuda.current_stream()
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        reps = max(3, min(200, int(target_ms / max(a.elapsed_time(b), 1e-3))))
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        out.append((label, kind, a.elapsed_time(b) / (reps * wl.ncopies)))
+        del g
+    return out
 
 
 def measure(cfg: int, steps: int, warmup: int, use_graph: bool):
@@ -214,7 +228,7 @@ def measure(cfg: int, steps: int, warmup: int, use_graph: bool):
     torch.cuda.synchronize()
     graphs = build_graphs(wl) if use_graph else None
     ms = timed_steps(wl, steps, warmup, graphs)
-    durs = kernel_durations(wl, max(5, min(steps, 50)))
+    durs = kernel_durations(wl)
     del graphs
     return wl, ms, durs
 
@@ -265,6 +279,166 @@ def cpu_baseline(wl: Workload, seconds: float):
     }, {"q8_1_bitexact": bool(q_ok), "max_err_over_den": worst, "tolerance": 1e-5}
 
 
+# --------------------------------------------------------------------------
+# Summaries of rocprofv3 output (kernel traces and counter collections) for
+# the launches of one step, and the HBM traffic they record.
+# --------------------------------------------------------------------------
+
+KERNEL_SOURCES = {
+    "gemv_q4k": "q6_q8_matmul_amd/csrc/gemv_q4k.hip",
+    "gemv_q6k": "q6_q8_matmul_amd/csrc/gemv_q6k.hip",
+    "mmq_q4k": "q6_q8_matmul_amd/csrc/mmq_q4k.hip",
+    "quantize": "q6_q8_matmul_amd/csrc/quantize_q8_1.hip",
+}
+FETCH_SCALE_NOTE = ("FETCH_SIZE and WRITE_SIZE are scaled by bytes / counter reading of the "
+                    "plain copy kernels (__amd_rocclr_copyBuffer, the weight copies of known size) "
+                    "in the same run")
+
+
+def source_hash(kernel: str) -> str:
+    import hashlib
+
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _step_labels(cfg: int):
+    from kq_inputs import WORKLOADS
+
+    wl = WORKLOADS[cfg]
+    ops = wl.get("bench_ops", wl["ops"])
+    labels, kinds, seen = [], [], set()
+    for op in ops:
+        if op["x"] not in seen:
+            labels.append(f"quantize {op['x']}")
+            kinds.append("quantize")
+            seen.add(op["x"])
+        labels.append(op["label"])
+        kinds.append(op["op"])
+    return labels, kinds
+
+
+KERNEL_NAMES = {"quantize": "quantize_q8_1_kernel", "gemv_q4k": "gemv_q4k_kernel",
+                "gemv_q6k": "gemv_q6k_kernel", "mmq_q4k": "mmq_q4k_kernel"}
+
+
+def _steps_in(rows, cfg):
+    """Per step, the dispatches of its launches in order (matched by kernel name)."""
+    labels, kinds = _step_labels(cfg)
+    by_disp = {}
+    for r in rows:
+        if "kq::" in r["Kernel_Name"]:
+            by_disp.setdefault(r.get("Dispatch_Id") or r.get("Correlation_Id"), []).append(r)
+    disp = sorted(by_disp.values(), key=lambda v: int(v[0]["Start_Timestamp"]))
+    steps, j, n = [], 0, len(kinds)
+    while j + n <= len(disp):
+        if all(KERNEL_NAMES[kinds[t]] in disp[j + t][0]["Kernel_Name"] for t in range(n)):
+            steps.append(disp[j:j + n])
+            j += n
+        else:
+            j += 1
+    return labels, kinds, steps
+
+
+def _op_bytes(cfg: int):
+    """Algorithmic bytes per launch label: weights + q8_1 input + f32 output
+    (+ f32 residual), and the weight sizes the run copies."""
+    from kq_inputs import WORKLOADS
+
+    wl = WORKLOADS[cfg]
+    ops = wl.get("bench_ops", wl["ops"])
+    shapes = {name: (kind, a, b) for name, kind, a, b in wl["tensors"]}
+    out, weights = {}, set()
+    for op in ops:
+        names = op["w"] if isinstance(op["w"], list) else [op["w"]]
+        wb = sum(shapes[nm][1] * shapes[nm][2] // 256 * (144 if shapes[nm][0] == "q4k" else 210)
+                 for nm in names)
+        weights.add(wb)
+        rows = op.get("batch", op.get("n"))
+        b = wb + rows * (op["k"] // 32) * 36 + rows * op["m"] * 4
+        if "residual" in op:
+            b += rows * op["m"] * 4
+        out[op["label"]] = b
+    return out, sorted(weights)
+
+
+def summarize(cfg: int, trace_csv=None, fetch_csv=None, write_csv=None):
+    """Text summary of rocprofv3 CSV output of this script for workload cfg.
+    Counter readings are scaled by (bytes / reading) of the plain copy
+    kernels in the same run -- the weight copies, whose sizes are known."""
+    import csv
+
+    out = []
+    labels, kinds = _step_labels(cfg)
+    if trace_csv:
+        rows = list(csv.DictReader(open(trace_csv)))
+        _, _, steps = _steps_in(rows, cfg)
+        out.append(f"kernel trace: {len(steps)} steps matched in {trace_csv}")
+        out.append(f"{'launch':22s} {'kernel':16s} {'median_us':>10s} {'min_us':>8s}")
+        for t, lab in enumerate(labels):
+            d = sorted(int(s[t][0]["End_Timestamp"]) - int(s[t][0]["Start_Timestamp"]) for s in steps)
+            if d:
+                out.append(f"{lab:22s} {kinds[t]:16s} {d[len(d)//2]/1e3:10.2f} {d[0]/1e3:8.2f}")
+    op_bytes, weight_sizes = _op_bytes(cfg)
+    per, scale = {}, {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        if not path:
+            continue
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == name]
+        copies = [float(r["Counter_Value"]) * 1024 for r in rows
+                  if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) * 1024 >= min(weight_sizes) / 4]
+        # each copy moves one weight tensor: match readings to sizes by rank
+        copies.sort()
+        sizes = sorted(weight_sizes * (len(copies) // max(len(weight_sizes), 1)))
+        if len(sizes) == len(copies) and copies:
+            scale[name] = sum(sizes) / sum(copies)
+        _, _, steps = _steps_in(rows, cfg)
+        out.append(f"{name}: {len(steps)} steps matched in {path}; copy-kernel scale "
+                   f"{scale.get(name, float('nan')):.4f} from {len(copies)} weight copies")
+        per[name] = {}
+        for t, lab in enumerate(labels):
+            v = sorted(float(s[t][0]["Counter_Value"]) for s in steps)
+            if v:
+                per[name][lab] = v[len(v) // 2] * 1024
+                out.append(f"  {lab:22s} median {v[len(v)//2]:12.2f} KiB")
+    traffic = None
+    if "FETCH_SIZE" in scale and "WRITE_SIZE" in scale:
+        hbm = {lab: per["FETCH_SIZE"][lab] * scale["FETCH_SIZE"] + per["WRITE_SIZE"][lab] * scale["WRITE_SIZE"]
+               for lab in op_bytes if lab in per["FETCH_SIZE"]}
+        out.append("HBM bytes per launch (scaled FETCH + WRITE) against algorithmic bytes:")
+        for lab, v in hbm.items():
+            out.append(f"  {lab:22s} {v:16,.0f}  {op_bytes[lab]:16,}  ratio {v / op_bytes[lab]:.4f}")
+        kern = kinds[labels.index(next(iter(hbm)))]
+        traffic = {"kernel": "kq_" + kern, "workload": _workload_name(cfg),
+                   "source_sha256_16": source_hash(kern),
+                   "fetch_scale": round(scale["FETCH_SIZE"], 5), "write_scale": round(scale["WRITE_SIZE"], 5),
+                   "hbm_bytes": {k: round(v) for k, v in hbm.items()},
+                   "algorithmic_bytes": op_bytes,
+                   "hbm_bytes_per_launch": round(sum(hbm.values()) / len(hbm)),
+                   "algorithmic_bytes_per_launch": round(sum(op_bytes.values()) / len(op_bytes))}
+    return "\n".join(out), traffic
+
+
+def _workload_name(cfg: int) -> str:
+    from kq_inputs import WORKLOADS
+
+    return WORKLOADS[cfg]["name"]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if
+    the kernel source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic_json: "):
+            d = json.loads(line[len("traffic_json: "):])
+            if d.get("source_sha256_16") == source_hash(kernel):
+                return d
+    return None
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,7 +449,20 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", type=int, default=None, help="measure only this workload")
+    ap.add_argument("--summarize", action="store_true",
+                    help="summarise rocprofv3 CSV output of a run of this script (no GPU)")
+    ap.add_argument("--trace-csv", default=None)
+    ap.add_argument("--fetch-csv", default=None)
+    ap.add_argument("--write-csv", default=None)
     args = ap.parse_args(argv)
+
+    if args.summarize:
+        cfg = 1 if args.only is None else args.only
+        text, traffic = summarize(cfg, args.trace_csv, args.fetch_csv, args.write_csv)
+        print(text)
+        if traffic:
+            print("traffic_json: " + json.dumps(traffic))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the k-quant "
@@ -302,9 +489,9 @@ def main(argv=None):
         wl, ms, durs = measure(cfg, steps, warm, use_graph)
         per_op = []
         for i, op in enumerate(wl.ops):
-            label, kind, avg_ms, med_ms = [d for d in durs if d[0] == op["label"]][0]
+            label, kind, avg_ms = [d for d in durs if d[0] == op["label"]][0]
             e = {"op": op["label"], "kernel": "kq_" + op["op"], "shape": [op["m"], op["k"], op.get("batch", op.get("n"))],
-                 "avg_us": round(avg_ms * 1e3, 2), "median_us": round(med_ms * 1e3, 2)}
+                 "avg_us": round(avg_ms * 1e3, 2)}
             if op["op"] == "mmq_q4k":
                 tops = wl.op_ops(i) / (avg_ms * 1e-3) / 1e12
                 e["tops"] = round(tops, 2)
@@ -327,10 +514,13 @@ def main(argv=None):
             tot_b = sum(wl.op_bytes(i) for i in range(len(wl.ops)))
             tot_t = sum([d for d in durs if d[0] == op["label"]][0][2] for op in wl.ops) * 1e-3
             achieved = tot_b / tot_t / 1e9
+            tr = read_traffic("gemv_q4k", wl.wl["name"])
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                        "traffic": tr["hbm_bytes_per_launch"] if tr else None,
+                        "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled)",
                         "kernel": "kq_gemv_q4k",
-                        "algorithmic_bytes_per_step": tot_b,
+                        "algorithmic_bytes_per_launch": round(tot_b / len(wl.ops)),
                         "avg_launch_us": round(tot_t * 1e6 / len(wl.ops), 2)}
             result = {
                 "metric": METRIC,
@@ -346,7 +536,8 @@ def main(argv=None):
                 "dtype": "int8",
                 "data": "synthetic",
                 "config": {"workload": wl.wl["name"],
-                           "shapes": "attn_out 4096x4096, gate 14336x4096, up 14336x4096, down 4096x14336",
+                           "shapes": "attn_out 4096x4096; gate and up 14336x4096 each, one launch over "
+                                     "their contiguous 28672 rows; down 4096x14336",
                            "batch": 1, "weight_format": "Q4_K", "activation_format": "q8_1",
                            "hip_graphs": use_graph},
                 "roofline": roofline,

@@ -90,7 +90,7 @@ int kq_quantize_q8_1(const float* x, void* xq, int64_t rows, int64_t k, void* st
  * Q4_K x q8_1 matrix-vector product for 1..4 activation vectors, with an
  * optional residual added when each output is written.
  *   w         [m][k/256] Q4_K superblocks (144 bytes), 16-byte aligned.
- *   xq        [batch][k/32] q8_1 blocks (from kq_quantize_q8_1), 4-byte aligned.
+ *   xq        [batch][k/32] q8_1 blocks (from kq_quantize_q8_1), 16-byte aligned.
  *   y         out: f32 [batch][m], 4-byte aligned.
  *   residual  NULL, or f32 [batch][m], 4-byte aligned; y == residual is
  *             allowed (in place); any other overlap is an error.
@@ -119,7 +119,7 @@ int kq_gemv_q6k(const void* w, const void* xq, float* y, const float* residual,
 /*
  * Q4_K x q8_1 matrix-matrix product for n tokens on the int8 matrix cores.
  *   w    [m][k/256] Q4_K superblocks, 16-byte aligned.
- *   xq   [n][k/32] q8_1 blocks, 4-byte aligned.
+ *   xq   [n][k/32] q8_1 blocks, 16-byte aligned.
  *   y    out: f32 [n][m], 4-byte aligned; must not overlap w or xq.
  *   m >= 0, n >= 0, k > 0, k % 256 == 0, k <= KQ_MAX_K.
  * Same value per output as kq_gemv_q4k without a residual.

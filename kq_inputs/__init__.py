@@ -113,6 +113,13 @@ WORKLOADS = {
             dict(op="gemv_q4k", label="up", w="up", x="x_ffn", m=14336, k=4096, batch=1),
             dict(op="gemv_q4k", label="down", w="down", x="x_down", m=4096, k=14336, batch=1),
         ],
+        # gate and up share one q8_1 activation; laid out as one contiguous
+        # 28672-row matrix they are one launch
+        bench_ops=[
+            dict(op="gemv_q4k", label="attn_out", w="attn_out", x="x_attn", m=4096, k=4096, batch=1),
+            dict(op="gemv_q4k", label="gate|up", w=["gate", "up"], x="x_ffn", m=28672, k=4096, batch=1),
+            dict(op="gemv_q4k", label="down", w="down", x="x_down", m=4096, k=14336, batch=1),
+        ],
     ),
     2: dict(
         name="llama3_8b_decode_gemv_q4k_b4",

@@ -3,26 +3,33 @@
 // The decode matmul reads every weight byte once, so the kernel is bound by
 // HBM bandwidth (minfer "The CUDA backend" 2.2: decode is weight-streaming
 // bound; cajeta "One model, start to last token" 4: bytes per second against
-// the memory bus is a decode kernel's only figure of merit).
+// the memory bus is a decode kernel's only figure of merit).  On gfx950 the
+// vector ALU work per weight byte is the other limit, so the decode is laid
+// out to keep the per-lane instruction count low.
 //
 // Layout of the work:
-//   * a workgroup of 4 wavefronts owns 4*RPW consecutive output rows, each
-//     wavefront RPW rows that it streams concurrently;
-//   * inside a wavefront, 8 groups of 8 lanes take 8 consecutive superblocks
-//     of a row per pass, so one pass is a contiguous 1152-byte read;
-//     lane k of a group loads the 16-byte slice k of the 128 code bytes
-//     (both nibbles: 16 values of sub-block 2c and 16 of sub-block 2c+1,
-//     c = k/2) plus the 16-byte superblock header (d, dmin, packed scales);
-//   * the q8_1 activation is restaged once per workgroup into LDS as plain
-//     int8 codes plus, per (32-block, 16-value half), the pair
-//     {d8, d8 * sum of the half's codes}; chunks of superblocks are staged in
-//     turn when the whole row does not fit the LDS budget;
+//   * a wavefront streams row pairs: lanes 0..31 one row, lanes 32..63 the
+//     next; RPW pairs per wavefront, WAVES wavefronts per workgroup;
+//   * in a half-wave, 8 groups of 4 lanes take 8 consecutive superblocks per
+//     pass; lane t of a group loads the 16-byte code slices [16t, 16t+16) and
+//     [64+16t, 64+16t+16) plus the 16-byte header, i.e. 16 values of each of
+//     sub-blocks 2c, 2c+1, 2c+4, 2c+5 (c = t/2, values 16h..16h+15, h = t%2),
+//     so every lane decodes the same mix of low (j < 4) and high (j >= 4)
+//     six-bit fields and the code has no lane-dependent branches;
+//   * the loads of the first DEPTH passes are issued before anything else and
+//     every later pass is requested DEPTH passes ahead (a register ring), so
+//     HBM latency overlaps the activation staging and the arithmetic;
+//   * the q8_1 activation is restaged once per workgroup into LDS: per
+//     superblock the 16-byte slices in the order the lanes read them, and per
+//     lane the four d8 values and the four d8 * (sum of the slice's codes);
+//     when the row does not fit the LDS budget it is staged in chunks of whole
+//     passes;
 //   * integer dots with v_dot4_i32_i8 (4-bit codes are non-negative bytes),
-//     then per lane: d*(sc*A*d8) - dmin*(m*d8*Bq), accumulated in a private
-//     f32 register over the whole row; the minimum term uses the q8 codes
+//     then per lane sum_j d8_j*(sc_j*A_j) and sum_j m_j*(d8_j*Bq_j) in f32 and
+//     acc += d*first - dmin*second; the minimum term uses the q8 codes
 //     (leone-cuda "CUDA kernel design": minimum correction formed from the
 //     same lane-local codes);
-//   * one fixed xor-butterfly over the 64 lanes per row and batch column,
+//   * one fixed xor-butterfly over the 32 lanes of a row per batch column,
 //     then the optional residual is added when the row is written
 //     (leone-cuda "CUDA kernel design": residual epilogue, same f32 addition
 //     as the separate add it replaces).
@@ -31,61 +38,182 @@
 #include "kq_device.h"
 
 namespace kq {
-namespace {
+namespace gemv4 {
 
-constexpr int kWaves = 4;
-
-struct HalfScale {  // per (q8_1 block, 16-value half)
-    float d8;
-    float d8_bq;    // d8 * (sum of the half's 16 codes), exact in f32
+struct Slice {      // one lane's share of one superblock of one row
+    uint4 hdr;      // d, dmin, 12 scale bytes
+    uint4 qa;       // code bytes [16t, 16t+16)
+    uint4 qb;       // code bytes [64+16t, 64+16t+16)
 };
 
-template <int BATCH>
+// LDS layout of one staged column (schunk superblocks):
+//   codes [schunk][256]   quad 4r + t (16 bytes) = the slice lane t reads as
+//                         its r-th block: r = 0, 1, 2, 3 <-> blocks 2c, 2c+1,
+//                         2c+4, 2c+5, values 16h..16h+15;
+//   slot  [schunk][4][8]  per lane t: d8 of its four blocks, then
+//                         d8 * (sum of the slice's 16 codes) for each.
+constexpr int kLdsPerSb = 256 + 4 * 8 * 4;
+
+__device__ __forceinline__ int quad_of(int jj) {   // slice r of lane 2c (h = 0) of block jj
+    const int hiA = jj >> 2, c = (jj >> 1) & 1, e = jj & 1;
+    return 4 * (2 * hiA + e) + 2 * c;
+}
+
+// Stage blocks [j0, j0 + nbc) of every column (nbc a multiple of 8): one
+// thread per q8_1 block, the loads of U blocks in flight before any is used.
+// Ends with a barrier.
+template <int BATCH, int NT>
 __device__ __forceinline__ void stage_activation(const uint8_t* __restrict__ xq, int nb_row,
-                                                 int j0, int nbc, int cap, int8_t* codes,
-                                                 HalfScale* hs) {
-    // blocks [j0, j0 + nbc) of every batch column; column stride = cap blocks
-    for (int idx = threadIdx.x; idx < BATCH * nbc; idx += blockDim.x) {
-        const int bb = idx / nbc;
-        const int j = idx - bb * nbc;
-        const uint32_t* blk =
-            (const uint32_t*)(xq + ((int64_t)bb * nb_row + j0 + j) * kQ81Bytes);
-        const uint32_t hdr = blk[0];
-        uint32_t c[8];
+                                                 int j0, int nbc, int schunk, uint8_t* lds) {
+    constexpr int U = 2;
+    uint8_t* codes = lds;
+    float* slots = (float*)(lds + BATCH * schunk * 256);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = blk[1 + i];
-        const float d8 = half_bits_to_float(hdr);
-        int s0 = dot4(c[0], 0x01010101u, dot4(c[1], 0x01010101u, 0));
-        s0 = dot4(c[2], 0x01010101u, dot4(c[3], 0x01010101u, s0));
-        int s1 = dot4(c[4], 0x01010101u, dot4(c[5], 0x01010101u, 0));
-        s1 = dot4(c[6], 0x01010101u, dot4(c[7], 0x01010101u, s1));
-        uint4* dst = (uint4*)(codes + (bb * cap + j) * 32);
-        dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
-        dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
-        HalfScale* h = hs + (bb * cap + j) * 2;
-        h[0] = HalfScale{d8, d8 * (float)s0};
-        h[1] = HalfScale{d8, d8 * (float)s1};
+    for (int bb = 0; bb < BATCH; ++bb) {
+        const uint32_t* col = (const uint32_t*)(xq + ((int64_t)bb * nb_row + j0) * kQ81Bytes);
+        for (int base = 0; base < nbc; base += NT * U) {
+            uint32_t c[U][9];
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const int j = base + i * NT + (int)threadIdx.x;
+                if (j < nbc) {
+#pragma unroll
+                    for (int e = 0; e < 9; ++e) c[i][e] = col[j * 9 + e];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const int j = base + i * NT + (int)threadIdx.x;
+                if (j < nbc) {
+                    const int sb = j >> 3, jj = j & 7;
+                    const float d8 = half_bits_to_float(c[i][0]);
+                    const int s0 = dot4(c[i][1], 0x01010101u, dot4(c[i][2], 0x01010101u,
+                                   dot4(c[i][3], 0x01010101u, dot4(c[i][4], 0x01010101u, 0))));
+                    const int s1 = dot4(c[i][5], 0x01010101u, dot4(c[i][6], 0x01010101u,
+                                   dot4(c[i][7], 0x01010101u, dot4(c[i][8], 0x01010101u, 0))));
+                    const int q0 = quad_of(jj);
+                    uint8_t* cs = codes + (bb * schunk + sb) * 256 + 16 * q0;
+                    *(uint4*)cs = make_uint4(c[i][1], c[i][2], c[i][3], c[i][4]);
+                    *(uint4*)(cs + 16) = make_uint4(c[i][5], c[i][6], c[i][7], c[i][8]);
+                    const int r = q0 >> 2, t0 = q0 & 3;   // slice index and lane (h = 0)
+                    float* sl = slots + ((bb * schunk + sb) * 4 + t0) * 8;
+                    sl[r] = d8;
+                    sl[4 + r] = d8 * (float)s0;
+                    sl[8 + r] = d8;                       // lane t0 + 1 (h = 1)
+                    sl[12 + r] = d8 * (float)s1;
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+
+template <int RPW>
+__device__ __forceinline__ void load_pass(Slice (&s)[RPW], const uint8_t* const (&rowp)[RPW],
+                                          int sb, int S, int t) {
+    const int sbc = min(sb, S - 1);  // lanes past the row end reload a valid superblock
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const uint8_t* p = rowp[i] + sbc * kQ4KBytes;
+        s[i].hdr = load16(p);
+        s[i].qa = load16(p + 16 + 16 * t);
+        s[i].qb = load16(p + 80 + 16 * t);
     }
 }
 
+__device__ __forceinline__ int dot16(uint4 w, uint4 a) {
+    return dot4(w.w, a.w, dot4(w.z, a.z, dot4(w.y, a.y, dot4(w.x, a.x, 0))));
+}
+
 template <int BATCH, int RPW>
-__global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t* __restrict__ w,
-                                                       const uint8_t* __restrict__ xq,
-                                                       float* y, const float* residual,
-                                                       int m, int S, int schunk) {
+__device__ __forceinline__ void compute_pass(const Slice (&s)[RPW], float (&acc)[RPW][BATCH],
+                                             const uint8_t* lds, int schunk, int sl, int t) {
+    // activation slices of this lane for every column: read once, used by all rows
+    const uint8_t* codes = lds;
+    const float* slots = (const float*)(lds + BATCH * schunk * 256);
+    uint4 a[BATCH][4];
+    float4 d8v[BATCH], dbq[BATCH];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+        const uint8_t* cs = codes + (b * schunk + sl) * 256 + 16 * t;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[b][r] = *(const uint4*)(cs + 64 * r);
+        const float4* sp = (const float4*)(slots + ((b * schunk + sl) * 4 + t) * 8);
+        d8v[b] = sp[0];
+        dbq[b] = sp[1];
+    }
+    const uint32_t sh = 16u * (uint32_t)(t >> 1);   // byte 2c of the scale words
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const uint4 hdr = s[i].hdr;
+        const float d = half_bits_to_float(hdr.x);
+        const float dmin = half_bits_to_float(hdr.x >> 16);
+        // six-bit scales/mins: j = 2c, 2c+1 in the low six bits of bytes 0..3,
+        // j = 2c+4, 2c+5 in the nibbles of bytes 8..11 plus the top two bits
+        // of bytes 0..7
+        const int sc0 = (int)__builtin_amdgcn_ubfe(hdr.y, sh, 6);
+        const int sc1 = (int)__builtin_amdgcn_ubfe(hdr.y, sh + 8, 6);
+        const int sc2 = (int)(__builtin_amdgcn_ubfe(hdr.w, sh, 4) | (__builtin_amdgcn_ubfe(hdr.y, sh + 6, 2) << 4));
+        const int sc3 = (int)(__builtin_amdgcn_ubfe(hdr.w, sh + 8, 4) | (__builtin_amdgcn_ubfe(hdr.y, sh + 14, 2) << 4));
+        const float m0 = (float)__builtin_amdgcn_ubfe(hdr.z, sh, 6);
+        const float m1 = (float)__builtin_amdgcn_ubfe(hdr.z, sh + 8, 6);
+        const float m2 = (float)(__builtin_amdgcn_ubfe(hdr.w, sh + 4, 4) | (__builtin_amdgcn_ubfe(hdr.z, sh + 6, 2) << 4));
+        const float m3 = (float)(__builtin_amdgcn_ubfe(hdr.w, sh + 12, 4) | (__builtin_amdgcn_ubfe(hdr.z, sh + 14, 2) << 4));
+        const uint4 qa = s[i].qa, qb = s[i].qb;
+        const uint4 w0 = make_uint4(qa.x & 0x0f0f0f0fu, qa.y & 0x0f0f0f0fu, qa.z & 0x0f0f0f0fu, qa.w & 0x0f0f0f0fu);
+        const uint4 w1 = make_uint4((qa.x >> 4) & 0x0f0f0f0fu, (qa.y >> 4) & 0x0f0f0f0fu,
+                                    (qa.z >> 4) & 0x0f0f0f0fu, (qa.w >> 4) & 0x0f0f0f0fu);
+        const uint4 w2 = make_uint4(qb.x & 0x0f0f0f0fu, qb.y & 0x0f0f0f0fu, qb.z & 0x0f0f0f0fu, qb.w & 0x0f0f0f0fu);
+        const uint4 w3 = make_uint4((qb.x >> 4) & 0x0f0f0f0fu, (qb.y >> 4) & 0x0f0f0f0fu,
+                                    (qb.z >> 4) & 0x0f0f0f0fu, (qb.w >> 4) & 0x0f0f0f0fu);
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            const int A0 = dot16(w0, a[b][0]), A1 = dot16(w1, a[b][1]);
+            const int A2 = dot16(w2, a[b][2]), A3 = dot16(w3, a[b][3]);
+            float f = (float)__mul24(A0, sc0) * d8v[b].x;
+            f += (float)__mul24(A1, sc1) * d8v[b].y;
+            f += (float)__mul24(A2, sc2) * d8v[b].z;
+            f += (float)__mul24(A3, sc3) * d8v[b].w;
+            float g = m0 * dbq[b].x;
+            g += m1 * dbq[b].y;
+            g += m2 * dbq[b].z;
+            g += m3 * dbq[b].w;
+            acc[i][b] += d * f - dmin * g;
+        }
+    }
+}
+
+// Sum over the 32 lanes of a half-wavefront (fixed xor-butterfly order).
+__device__ __forceinline__ float half_wave_sum(float v) {
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+template <int BATCH, int RPW, int DEPTH, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __restrict__ w,
+                                                              const uint8_t* __restrict__ xq,
+                                                              float* y, const float* residual,
+                                                              int m, int S, int schunk) {
     extern __shared__ __align__(16) uint8_t smem[];
-    int8_t* codes = (int8_t*)smem;                                  // [BATCH][schunk*256]
-    HalfScale* hs = (HalfScale*)(smem + BATCH * schunk * kQK);       // [BATCH][schunk*8][2]
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int grp = lane >> 3;      // superblock within a pass
-    const int k8 = lane & 7;        // 16-byte code slice within the superblock
-    const int c = k8 >> 1;          // 64-value chunk: sub-blocks 2c (low nibbles), 2c+1 (high)
-    const int hh = k8 & 1;          // which 16 values of each sub-block
-    const int row0 = (blockIdx.x * kWaves + wave) * RPW;
+    const int half = lane >> 5;
+    const int grp = (lane >> 2) & 7;   // superblock within a pass
+    const int t = lane & 3;            // slice pair within the superblock
+    const int pair0 = (blockIdx.x * WAVES + wave) * RPW;   // first row pair of this wave
     const int64_t row_bytes = (int64_t)S * kQ4KBytes;
     const int nb_row = S * 8;
+    const int npass = (S + 7) >> 3;
+    const int chunk_passes = schunk >> 3;   // schunk is a multiple of 8 superblocks
+
+    const uint8_t* rowp[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int r = min(2 * (pair0 + i) + half, m - 1);   // clamped rows are computed, not stored
+        rowp[i] = w + (int64_t)r * row_bytes;
+    }
 
     float acc[RPW][BATCH];
 #pragma unroll
@@ -93,110 +221,86 @@ __global__ __launch_bounds__(256) void gemv_q4k_kernel(const uint8_t* __restrict
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) acc[i][b] = 0.0f;
 
-    for (int kc = 0; kc < S; kc += schunk) {
-        const int nsb = min(schunk, S - kc);
-        if (kc > 0) __syncthreads();
-        stage_activation<BATCH>(xq, nb_row, kc * 8, nsb * 8, schunk * 8, codes, hs);
-        __syncthreads();
+    Slice ring[DEPTH][RPW];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_pass<RPW>(ring[d], rowp, 8 * d + grp, S, t);
 
-        for (int sl = grp; sl < nsb; sl += 8) {
-            const int sb = kc + sl;
-            uint4 hdr[RPW], qs[RPW];
+    stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
+
+    for (int p0 = 0; p0 < npass; p0 += DEPTH) {
 #pragma unroll
-            for (int i = 0; i < RPW; ++i) {
-                const int r = min(row0 + i, m - 1);  // clamped rows are computed, not stored
-                const uint8_t* p = w + (int64_t)r * row_bytes + (int64_t)sb * kQ4KBytes;
-                hdr[i] = *(const uint4*)p;
-                qs[i] = *(const uint4*)(p + 16 + 16 * k8);
-            }
-            const int cbase = sl * 256 + 64 * c + 16 * hh;  // within the staged chunk
-            const int jl = sl * 8 + 2 * c;                  // local 32-block index of sub-block 2c
-#pragma unroll
-            for (int i = 0; i < RPW; ++i) {
-                const float d = half_bits_to_float(hdr[i].x);
-                const float dmin = half_bits_to_float(hdr[i].x >> 16);
-                const uint32_t h1 = hdr[i].y, h2 = hdr[i].z, h3 = hdr[i].w;
-                // six-bit scales/mins of sub-blocks 2c and 2c+1
-                uint32_t S4, M4;
-                if (c < 2) {
-                    S4 = h1 & 0x3f3f3f3fu;
-                    M4 = h2 & 0x3f3f3f3fu;
-                } else {
-                    S4 = (h3 & 0x0f0f0f0fu) | ((h1 >> 2) & 0x30303030u);
-                    M4 = ((h3 >> 4) & 0x0f0f0f0fu) | ((h2 >> 2) & 0x30303030u);
+        for (int d = 0; d < DEPTH; ++d) {
+            const int p = p0 + d;
+            if (p < npass) {
+                const int chunk = p / chunk_passes;
+                const int pl = p - chunk * chunk_passes;   // pass within the staged chunk
+                if (pl == 0 && p > 0) {                    // uniform over the workgroup
+                    __syncthreads();
+                    const int kc = chunk * schunk;
+                    stage_activation<BATCH, 64 * WAVES>(xq, nb_row, kc * 8, min(schunk, S - kc) * 8,
+                                                        schunk, smem);
                 }
-                const int sh = (c & 1) * 16;
-                const int sc_a = (S4 >> sh) & 0xff, sc_b = (S4 >> (sh + 8)) & 0xff;
-                const float m_a = (float)((M4 >> sh) & 0xff), m_b = (float)((M4 >> (sh + 8)) & 0xff);
-                const uint32_t lo0 = qs[i].x & 0x0f0f0f0fu, lo1 = qs[i].y & 0x0f0f0f0fu;
-                const uint32_t lo2 = qs[i].z & 0x0f0f0f0fu, lo3 = qs[i].w & 0x0f0f0f0fu;
-                const uint32_t hi0 = (qs[i].x >> 4) & 0x0f0f0f0fu, hi1 = (qs[i].y >> 4) & 0x0f0f0f0fu;
-                const uint32_t hi2 = (qs[i].z >> 4) & 0x0f0f0f0fu, hi3 = (qs[i].w >> 4) & 0x0f0f0f0fu;
-#pragma unroll
-                for (int b = 0; b < BATCH; ++b) {
-                    const int8_t* cb = codes + b * (schunk * kQK) + cbase;
-                    const uint4 alo = *(const uint4*)cb;
-                    const uint4 ahi = *(const uint4*)(cb + 32);
-                    int A_lo = dot4(lo0, alo.x, 0);
-                    A_lo = dot4(lo1, alo.y, A_lo);
-                    A_lo = dot4(lo2, alo.z, A_lo);
-                    A_lo = dot4(lo3, alo.w, A_lo);
-                    int A_hi = dot4(hi0, ahi.x, 0);
-                    A_hi = dot4(hi1, ahi.y, A_hi);
-                    A_hi = dot4(hi2, ahi.z, A_hi);
-                    A_hi = dot4(hi3, ahi.w, A_hi);
-                    const HalfScale sa = hs[(b * schunk * 8 + jl) * 2 + hh];
-                    const HalfScale sb2 = hs[(b * schunk * 8 + jl + 1) * 2 + hh];
-                    const float fa = (float)(A_lo * sc_a) * sa.d8 + (float)(A_hi * sc_b) * sb2.d8;
-                    const float fm = m_a * sa.d8_bq + m_b * sb2.d8_bq;
-                    acc[i][b] += d * fa - dmin * fm;
-                }
+                if (8 * p + grp < S)   // lanes past the row end add nothing
+                    compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pl + grp, t);
+                if (p + DEPTH < npass)
+                    load_pass<RPW>(ring[d], rowp, 8 * (p + DEPTH) + grp, S, t);
             }
         }
     }
 
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-        const int r = row0 + i;
+        const int r = 2 * (pair0 + i) + half;
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
-            const float t = wave_sum(acc[i][b]);
-            if (lane == 0 && r < m) {
+            const float v = half_wave_sum(acc[i][b]);
+            if ((lane & 31) == 0 && r < m) {
                 const int64_t o = (int64_t)b * m + r;
-                y[o] = residual ? residual[o] + t : t;
+                y[o] = residual ? residual[o] + v : v;
             }
         }
     }
 }
 
-template <int BATCH>
-hipError_t launch_batch(const void* w, const void* xq, float* y, const float* residual,
-                        int64_t m, int64_t k, int lds_limit, hipStream_t stream) {
-    constexpr int RPW = 2;
+template <int BATCH, int RPW, int DEPTH, int WAVES>
+hipError_t launch_variant(const void* w, const void* xq, float* y, const float* residual,
+                          int64_t m, int64_t k, int lds_budget, hipStream_t stream) {
     const int S = (int)(k / kQK);
-    // LDS per staged superblock and column: 256 code bytes + 8 blocks * 2 halves * 8 bytes
-    const int per_sb = BATCH * (kQK + 8 * 2 * (int)sizeof(HalfScale));
-    const int budget = lds_limit < 65536 ? lds_limit : 65536;
-    int schunk = budget / per_sb;
-    if (schunk > S) schunk = S;
-    if (schunk < 1) return hipErrorInvalidConfiguration;
+    const int per_sb = BATCH * kLdsPerSb;
+    const int budget = lds_budget;
+    int schunk = (budget / per_sb) & ~7;          // whole passes of 8 superblocks
+    const int s_round = (S + 7) & ~7;
+    if (schunk > s_round) schunk = s_round;
+    if (schunk < 8) return hipErrorInvalidConfiguration;
     const size_t lds = (size_t)schunk * per_sb;
-    const int rows_per_block = kWaves * RPW;
+    const int rows_per_block = WAVES * RPW * 2;
     const int64_t grid = (m + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL((gemv_q4k_kernel<BATCH, RPW>), dim3((unsigned)grid), dim3(64 * kWaves), lds,
-                       stream, (const uint8_t*)w, (const uint8_t*)xq, y, residual, (int)m, S, schunk);
+    hipLaunchKernelGGL((gemv_q4k_kernel<BATCH, RPW, DEPTH, WAVES>), dim3((unsigned)grid),
+                       dim3(64 * WAVES), lds, stream, (const uint8_t*)w, (const uint8_t*)xq, y,
+                       residual, (int)m, S, schunk);
     return hipGetLastError();
 }
 
-}  // namespace
+}  // namespace gemv4
 
 hipError_t launch_gemv_q4k(const void* w, const void* xq, float* y, const float* residual,
                            int64_t m, int64_t k, int batch, int lds_limit, hipStream_t stream) {
+    using namespace gemv4;
+    // Launch shapes measured on MI355X (rocprofv3 kernel traces over the
+    // Llama-3-8B decode shapes): two row pairs per wavefront for tall
+    // matrices, one pair and eight wavefronts otherwise; when the whole row
+    // of a batch fits the device's LDS it is staged in one piece.
+    const int64_t s_round = ((k / kQK) + 7) & ~7;
+    const int64_t whole = (int64_t)batch * kLdsPerSb * s_round;
+    const int one_piece = whole <= lds_limit ? lds_limit : 65536;
+    const bool tall = m >= 16384;
     switch (batch) {
-        case 1: return launch_batch<1>(w, xq, y, residual, m, k, lds_limit, stream);
-        case 2: return launch_batch<2>(w, xq, y, residual, m, k, lds_limit, stream);
-        case 3: return launch_batch<3>(w, xq, y, residual, m, k, lds_limit, stream);
-        case 4: return launch_batch<4>(w, xq, y, residual, m, k, lds_limit, stream);
+        case 1: return tall ? launch_variant<1, 2, 2, 4>(w, xq, y, residual, m, k, 65536, stream)
+                            : launch_variant<1, 1, 2, 8>(w, xq, y, residual, m, k, 65536, stream);
+        case 2: return launch_variant<2, 1, 2, 8>(w, xq, y, residual, m, k, one_piece, stream);
+        case 3: return launch_variant<3, 1, 2, 8>(w, xq, y, residual, m, k, one_piece, stream);
+        case 4: return whole > 65536 ? launch_variant<4, 1, 3, 8>(w, xq, y, residual, m, k, one_piece, stream)
+                                     : launch_variant<4, 2, 1, 8>(w, xq, y, residual, m, k, one_piece, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -10,8 +10,9 @@
 // two bytes before a superblock that starts at 2 (mod 4), which are the tail
 // of the previous superblock.
 //
-// Work layout (as the Q4_K GEMV): 4 wavefronts x RPW rows per workgroup;
-// 8 groups of 8 lanes take 8 consecutive superblocks of a row per pass.
+// Work layout (as the Q4_K GEMV): WAVES wavefronts x RPW rows per workgroup;
+// 8 groups of 8 lanes take 8 consecutive superblocks of a row per pass; the
+// raw loads of each pass are requested DEPTH passes ahead of their use.
 // Lane (h, q) of a group, h = 0..1, q = 0..3, owns values
 //   128h + 32g + 8q + i,   g = 0..3, i = 0..7,
 // which come from ql[64h + 8q + i] (g = 0, 2: low / high nibble),
@@ -30,48 +31,169 @@
 #include "kq_device.h"
 
 namespace kq {
-namespace {
+namespace gemv6 {
 
-constexpr int kWaves = 4;
+struct Raw {            // one lane's raw dwords of one superblock of one row
+    uint32_t l[3];      // ql, values g = 0 / 2
+    uint32_t l2[3];     // ql, values g = 1 / 3
+    uint32_t h[3];      // qh
+    uint32_t s[3];      // the half's 8 scale bytes (third dword only if misaligned)
+    uint32_t dpar;      // f16 d in the low half, byte parity of the superblock in bit 16
+};
 
-template <int BATCH>
+// LDS layout of one staged column (cap = 8 * schunk q8_1 blocks):
+//   codes [schunk][256]  per superblock: lane k = 4h + q finds the 8-value
+//                        pieces (block 4h+g, values 8q..8q+7) of g = 0, 1 in
+//                        bytes [16k, 16k+16) and of g = 2, 3 in
+//                        [128+16k, 128+16k+16), so the 8 lanes of a group read
+//                        8 distinct 16-byte bank quads;
+//   d8    [cap]          per block.
+constexpr int kLdsPerSb = 256 + 8 * 4;
+
+// Stage blocks [j0, j0 + nbc) of every column (nbc a multiple of 8): one
+// thread per q8_1 block, the loads of U blocks in flight before any is used.
+// Ends with a barrier.
+template <int BATCH, int NT>
 __device__ __forceinline__ void stage_activation(const uint8_t* __restrict__ xq, int nb_row,
-                                                 int j0, int nbc, int cap, int8_t* codes,
-                                                 float* d8s) {
-    for (int idx = threadIdx.x; idx < BATCH * nbc; idx += blockDim.x) {
-        const int bb = idx / nbc;
-        const int j = idx - bb * nbc;
-        const uint32_t* blk =
-            (const uint32_t*)(xq + ((int64_t)bb * nb_row + j0 + j) * kQ81Bytes);
-        uint32_t c[8];
+                                                 int j0, int nbc, int schunk, uint8_t* lds) {
+    constexpr int U = 2;
+    const int cap = schunk * 8;
+    uint8_t* codes = lds;
+    float* d8s = (float*)(lds + BATCH * schunk * 256);
+    const int total = BATCH * nbc;
+    for (int base = 0; base < total; base += NT * U) {
+        uint32_t c[U][9];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = blk[1 + i];
-        uint4* dst = (uint4*)(codes + (bb * cap + j) * 32);
-        dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
-        dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
-        d8s[bb * cap + j] = half_bits_to_float(blk[0]);
+        for (int i = 0; i < U; ++i) {
+            const int idx = base + i * NT + (int)threadIdx.x;
+            if (idx < total) {
+                const int bb = idx / nbc;
+                const int j = idx - bb * nbc;
+                const uint32_t* blk = (const uint32_t*)(xq + ((int64_t)bb * nb_row + j0 + j) * kQ81Bytes);
+#pragma unroll
+                for (int e = 0; e < 9; ++e) c[i][e] = blk[e];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int idx = base + i * NT + (int)threadIdx.x;
+            if (idx < total) {
+                const int bb = idx / nbc;
+                const int j = idx - bb * nbc;
+                const int sb = j >> 3, jj = j & 7, h = jj >> 2, g = jj & 3;
+                uint8_t* cs = codes + (bb * schunk + sb) * 256 + ((g < 2) ? 0 : 128) + 8 * (g & 1);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)   // 8-value piece q goes to lane 4h + q
+                    *(uint2*)(cs + 16 * (4 * h + q)) = make_uint2(c[i][1 + 2 * q], c[i][2 + 2 * q]);
+                d8s[bb * cap + j] = half_bits_to_float(c[i][0]);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Three aligned dwords covering the 8 bytes at offset `off` of a superblock
+// starting at `sb` with sb % 4 == par: [off - par, off - par + 12).  For the
+// offsets used here the range starts at most 2 bytes before the superblock
+// (the tail of the previous one) and ends before byte 197 of it.
+__device__ __forceinline__ void load3(uint32_t (&d)[3], const uint8_t* sb, int par, int off) {
+    const uint32_t* p = (const uint32_t*)(sb + off - par);
+    d[0] = p[0];
+    d[1] = p[1];
+    d[2] = p[2];
+}
+
+template <int RPW>
+__device__ __forceinline__ void load_pass(Raw (&r)[RPW], const uint8_t* __restrict__ w, int row0,
+                                          int m, int64_t row_bytes, int sb, int S, int h, int q) {
+    const int sbc = min(sb, S - 1);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int row = min(row0 + i, m - 1);
+        const int64_t off = (int64_t)row * row_bytes + (int64_t)sbc * kQ6KBytes;
+        const uint8_t* p = w + off;
+        const int par = (int)(off & 3);
+        load3(r[i].l, p, par, 64 * h + 8 * q);
+        load3(r[i].l2, p, par, 64 * h + 32 + 8 * q);
+        load3(r[i].h, p, par, 128 + 32 * h + 8 * q);
+        const uint32_t* ps = (const uint32_t*)(p + 192 + 8 * h - par);
+        r[i].s[0] = ps[0];
+        r[i].s[1] = ps[1];
+        r[i].s[2] = par ? ps[2] : 0u;  // only when the bytes straddle
+        r[i].dpar = (uint32_t)*(const uint16_t*)(p + 208) | ((uint32_t)par << 15);
     }
 }
 
-// Eight bytes starting at byte offset `off` of a superblock that starts at
-// `sb` (2-byte aligned, sb_par = sb & 3 in {0, 2}).  Reads the three aligned
-// dwords [off - par, off - par + 12); for the offsets used here that range
-// ends before byte 197 of the superblock and starts at most 2 bytes before it.
-__device__ __forceinline__ uint2 load8_u(const uint8_t* sb, int sb_par, int off) {
-    const uint32_t* p = (const uint32_t*)(sb + off - sb_par);
-    const uint32_t a = p[0], b = p[1], c = p[2];
-    const uint32_t sh = (uint32_t)sb_par * 8u;
-    return make_uint2(__builtin_amdgcn_alignbit(b, a, sh), __builtin_amdgcn_alignbit(c, b, sh));
+template <int BATCH, int RPW>
+__device__ __forceinline__ void compute_pass(const Raw (&r)[RPW], float (&acc)[RPW][BATCH],
+                                             const uint8_t* lds, int schunk, int sl, int h, int q) {
+    const uint8_t* codes = lds;
+    const float* d8s = (const float*)(lds + BATCH * schunk * 256);
+    const int k = 4 * h + q;
+    uint2 a[BATCH][4];
+    float db[BATCH][4];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+        const uint8_t* cs = codes + (b * schunk + sl) * 256;
+        const uint4 lo = *(const uint4*)(cs + 16 * k);
+        const uint4 hi = *(const uint4*)(cs + 128 + 16 * k);
+        a[b][0] = make_uint2(lo.x, lo.y);
+        a[b][1] = make_uint2(lo.z, lo.w);
+        a[b][2] = make_uint2(hi.x, hi.y);
+        a[b][3] = make_uint2(hi.z, hi.w);
+        const float4 d4 = *(const float4*)(d8s + (b * schunk + sl) * 8 + 4 * h);
+        db[b][0] = d4.x; db[b][1] = d4.y; db[b][2] = d4.z; db[b][3] = d4.w;
+    }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const uint32_t sh = (r[i].dpar >> 16) * 16u;   // 0 or 16 bits
+        const uint32_t L0 = __builtin_amdgcn_alignbit(r[i].l[1], r[i].l[0], sh);
+        const uint32_t L1 = __builtin_amdgcn_alignbit(r[i].l[2], r[i].l[1], sh);
+        const uint32_t M0 = __builtin_amdgcn_alignbit(r[i].l2[1], r[i].l2[0], sh);
+        const uint32_t M1 = __builtin_amdgcn_alignbit(r[i].l2[2], r[i].l2[1], sh);
+        const uint32_t H0 = __builtin_amdgcn_alignbit(r[i].h[1], r[i].h[0], sh);
+        const uint32_t H1 = __builtin_amdgcn_alignbit(r[i].h[2], r[i].h[1], sh);
+        const uint32_t S0 = __builtin_amdgcn_alignbit(r[i].s[1], r[i].s[0], sh);
+        const uint32_t S1 = __builtin_amdgcn_alignbit(r[i].s[2], r[i].s[1], sh);
+        const float dq = half_bits_to_float(r[i].dpar) * 0.25f;
+        // scale of group g: signed byte 2g + (q >> 1) of the half's 8 scale bytes
+        const uint32_t so = 8u * (uint32_t)(q >> 1);
+        int sc[4];
+        sc[0] = __builtin_amdgcn_sbfe((int)S0, so, 8);
+        sc[1] = __builtin_amdgcn_sbfe((int)S0, so + 16u, 8);
+        sc[2] = __builtin_amdgcn_sbfe((int)S1, so, 8);
+        sc[3] = __builtin_amdgcn_sbfe((int)S1, so + 16u, 8);
+        // 4*(q6 - 32) per byte: ((low nibble | high bits << 4) << 2) ^ 0x80
+        uint32_t v[4][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t l = t ? L1 : L0;
+            const uint32_t l2 = t ? M1 : M0;
+            const uint32_t hb = t ? H1 : H0;
+            v[0][t] = (((l << 2) & 0x3c3c3c3cu) | ((hb << 6) & 0xc0c0c0c0u)) ^ 0x80808080u;
+            v[1][t] = (((l2 << 2) & 0x3c3c3c3cu) | ((hb << 4) & 0xc0c0c0c0u)) ^ 0x80808080u;
+            v[2][t] = (((l >> 2) & 0x3c3c3c3cu) | ((hb << 2) & 0xc0c0c0c0u)) ^ 0x80808080u;
+            v[3][t] = (((l2 >> 2) & 0x3c3c3c3cu) | (hb & 0xc0c0c0c0u)) ^ 0x80808080u;
+        }
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            float t = 0.0f;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int A4 = dot4(v[g][1], a[b][g].y, dot4(v[g][0], a[b][g].x, 0));
+                t += (float)__mul24(A4, sc[g]) * db[b][g];
+            }
+            acc[i][b] += dq * t;
+        }
+    }
 }
 
-template <int BATCH, int RPW>
-__global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t* __restrict__ w,
-                                                       const uint8_t* __restrict__ xq,
-                                                       float* y, const float* residual,
-                                                       int m, int S, int schunk) {
+template <int BATCH, int RPW, int DEPTH, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __restrict__ w,
+                                                              const uint8_t* __restrict__ xq,
+                                                              float* y, const float* residual,
+                                                              int m, int S, int schunk) {
     extern __shared__ __align__(16) uint8_t smem[];
-    int8_t* codes = (int8_t*)smem;                             // [BATCH][schunk*256]
-    float* d8s = (float*)(smem + BATCH * schunk * kQK);         // [BATCH][schunk*8]
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -79,9 +201,11 @@ __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t* __restrict
     const int k8 = lane & 7;
     const int h = k8 >> 2;          // 128-value half of the superblock
     const int q = k8 & 3;           // 8-value slice within each 32-value group
-    const int row0 = (blockIdx.x * kWaves + wave) * RPW;
+    const int row0 = (blockIdx.x * WAVES + wave) * RPW;
     const int64_t row_bytes = (int64_t)S * kQ6KBytes;
     const int nb_row = S * 8;
+    const int npass = (S + 7) >> 3;
+    const int chunk_passes = schunk >> 3;
 
     float acc[RPW][BATCH];
 #pragma unroll
@@ -89,68 +213,30 @@ __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t* __restrict
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) acc[i][b] = 0.0f;
 
-    for (int kc = 0; kc < S; kc += schunk) {
-        const int nsb = min(schunk, S - kc);
-        if (kc > 0) __syncthreads();
-        stage_activation<BATCH>(xq, nb_row, kc * 8, nsb * 8, schunk * 8, codes, d8s);
-        __syncthreads();
+    Raw ring[DEPTH][RPW];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        load_pass<RPW>(ring[d], w, row0, m, row_bytes, 8 * d + grp, S, h, q);
 
-        for (int sl = grp; sl < nsb; sl += 8) {
-            const int sbi = kc + sl;
-            uint2 L[RPW], L2[RPW], H[RPW], SC[RPW];
-            uint32_t DH[RPW];
+    stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
+
+    for (int p0 = 0; p0 < npass; p0 += DEPTH) {
 #pragma unroll
-            for (int i = 0; i < RPW; ++i) {
-                const int r = min(row0 + i, m - 1);
-                const int64_t off = (int64_t)r * row_bytes + (int64_t)sbi * kQ6KBytes;
-                const uint8_t* sb = w + off;
-                const int par = (int)(off & 3);
-                L[i] = load8_u(sb, par, 64 * h + 8 * q);
-                L2[i] = load8_u(sb, par, 64 * h + 32 + 8 * q);
-                H[i] = load8_u(sb, par, 128 + 32 * h + 8 * q);
-                // the 8 scale bytes of this half: [192 + 8h, 200 + 8h)
-                const uint32_t* ps = (const uint32_t*)(sb + 192 + 8 * h - par);
-                const uint32_t s0 = ps[0], s1 = ps[1];
-                const uint32_t s2 = par ? ps[2] : 0u;  // only when the bytes straddle
-                SC[i] = make_uint2(__builtin_amdgcn_alignbit(s1, s0, (uint32_t)par * 8u),
-                                   __builtin_amdgcn_alignbit(s2, s1, (uint32_t)par * 8u));
-                DH[i] = *(const uint16_t*)(sb + 208);
-            }
-            const int cbase = sl * 256 + 128 * h + 8 * q;
-            const int jl = sl * 8 + 4 * h;
-#pragma unroll
-            for (int i = 0; i < RPW; ++i) {
-                const float dq = half_bits_to_float(DH[i]) * 0.25f;
-                // scale of group g: byte 2g + (q >> 1) of the half's 8 scale bytes
-                const uint64_t s64 = (uint64_t)SC[i].x | ((uint64_t)SC[i].y << 32);
-                int sc[4];
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    sc[g] = (int)(int8_t)(uint8_t)(s64 >> (8 * (2 * g + (q >> 1))));
-                uint32_t v[4][2];
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const uint32_t l = t ? L[i].y : L[i].x;
-                    const uint32_t l2 = t ? L2[i].y : L2[i].x;
-                    const uint32_t hb = t ? H[i].y : H[i].x;
-                    v[0][t] = (((l << 2) & 0x3c3c3c3cu) | ((hb << 6) & 0xc0c0c0c0u)) ^ 0x80808080u;
-                    v[1][t] = (((l2 << 2) & 0x3c3c3c3cu) | ((hb << 4) & 0xc0c0c0c0u)) ^ 0x80808080u;
-                    v[2][t] = (((l >> 2) & 0x3c3c3c3cu) | ((hb << 2) & 0xc0c0c0c0u)) ^ 0x80808080u;
-                    v[3][t] = (((l2 >> 2) & 0x3c3c3c3cu) | (hb & 0xc0c0c0c0u)) ^ 0x80808080u;
+        for (int d = 0; d < DEPTH; ++d) {
+            const int p = p0 + d;
+            if (p < npass) {
+                const int chunk = p / chunk_passes;
+                const int pl = p - chunk * chunk_passes;
+                if (pl == 0 && p > 0) {
+                    __syncthreads();
+                    const int kc = chunk * schunk;
+                    stage_activation<BATCH, 64 * WAVES>(xq, nb_row, kc * 8, min(schunk, S - kc) * 8,
+                                                        schunk, smem);
                 }
-#pragma unroll
-                for (int b = 0; b < BATCH; ++b) {
-                    const int8_t* cb = codes + b * (schunk * kQK) + cbase;
-                    const float* db = d8s + b * (schunk * 8) + jl;
-                    float t = 0.0f;
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const uint2 a = *(const uint2*)(cb + 32 * g);
-                        const int A4 = dot4(v[g][1], a.y, dot4(v[g][0], a.x, 0));
-                        t += (float)__mul24(A4, sc[g]) * db[g];
-                    }
-                    acc[i][b] += dq * t;
-                }
+                if (8 * p + grp < S)
+                    compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pl + grp, h, q);
+                if (p + DEPTH < npass)
+                    load_pass<RPW>(ring[d], w, row0, m, row_bytes, 8 * (p + DEPTH) + grp, S, h, q);
             }
         }
     }
@@ -169,33 +255,37 @@ __global__ __launch_bounds__(256) void gemv_q6k_kernel(const uint8_t* __restrict
     }
 }
 
-template <int BATCH>
-hipError_t launch_batch(const void* w, const void* xq, float* y, const float* residual,
-                        int64_t m, int64_t k, int lds_limit, hipStream_t stream) {
-    constexpr int RPW = 2;
+template <int BATCH, int RPW, int DEPTH, int WAVES>
+hipError_t launch_variant(const void* w, const void* xq, float* y, const float* residual,
+                          int64_t m, int64_t k, int lds_budget, hipStream_t stream) {
     const int S = (int)(k / kQK);
-    const int per_sb = BATCH * (kQK + 8 * (int)sizeof(float));
-    const int budget = lds_limit < 65536 ? lds_limit : 65536;
-    int schunk = budget / per_sb;
-    if (schunk > S) schunk = S;
-    if (schunk < 1) return hipErrorInvalidConfiguration;
+    const int per_sb = BATCH * kLdsPerSb;
+    const int budget = lds_budget;
+    int schunk = (budget / per_sb) & ~7;
+    const int s_round = (S + 7) & ~7;
+    if (schunk > s_round) schunk = s_round;
+    if (schunk < 8) return hipErrorInvalidConfiguration;
     const size_t lds = (size_t)schunk * per_sb;
-    const int rows_per_block = kWaves * RPW;
+    const int rows_per_block = WAVES * RPW;
     const int64_t grid = (m + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL((gemv_q6k_kernel<BATCH, RPW>), dim3((unsigned)grid), dim3(64 * kWaves), lds,
-                       stream, (const uint8_t*)w, (const uint8_t*)xq, y, residual, (int)m, S, schunk);
+    hipLaunchKernelGGL((gemv_q6k_kernel<BATCH, RPW, DEPTH, WAVES>), dim3((unsigned)grid),
+                       dim3(64 * WAVES), lds, stream, (const uint8_t*)w, (const uint8_t*)xq, y,
+                       residual, (int)m, S, schunk);
     return hipGetLastError();
 }
 
-}  // namespace
+}  // namespace gemv6
 
 hipError_t launch_gemv_q6k(const void* w, const void* xq, float* y, const float* residual,
                            int64_t m, int64_t k, int batch, int lds_limit, hipStream_t stream) {
+    using namespace gemv6;
+    // Launch shapes measured on MI355X (rocprofv3 kernel traces over the
+    // 128256 x 4096 output head): four rows per wavefront, one pass ahead.
     switch (batch) {
-        case 1: return launch_batch<1>(w, xq, y, residual, m, k, lds_limit, stream);
-        case 2: return launch_batch<2>(w, xq, y, residual, m, k, lds_limit, stream);
-        case 3: return launch_batch<3>(w, xq, y, residual, m, k, lds_limit, stream);
-        case 4: return launch_batch<4>(w, xq, y, residual, m, k, lds_limit, stream);
+        case 1: return launch_variant<1, 4, 2, 4>(w, xq, y, residual, m, k, 65536, stream);
+        case 2: return launch_variant<2, 4, 1, 4>(w, xq, y, residual, m, k, 65536, stream);
+        case 3: return launch_variant<3, 4, 1, 4>(w, xq, y, residual, m, k, 65536, stream);
+        case 4: return launch_variant<4, 4, 1, 4>(w, xq, y, residual, m, k, 65536, stream);
         default: return hipErrorInvalidValue;
     }
 }

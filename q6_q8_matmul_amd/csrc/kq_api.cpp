@@ -92,9 +92,10 @@ int gemv_common(const char* fn, int wbytes, const void* w, const void* xq, float
         return fail(KQ_ERR_ARG, "%s: m=%lld out of range [0, %d]", fn, (long long)m, KQ_MAX_ROWS);
     if (batch < 1 || batch > 4)
         return fail(KQ_ERR_ARG, "%s: batch=%d must be in [1, 4]", fn, (int)batch);
-    if (!aligned(w, 16) || !aligned(xq, 4) || !aligned(y, 4) || (residual && !aligned(residual, 4)))
-        return fail(KQ_ERR_ARG, "%s: misaligned pointer (w=%p needs 16, xq=%p y=%p residual=%p need 4)",
-                    fn, w, xq, (void*)y, (const void*)residual);
+    if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(y, 4) || (residual && !aligned(residual, 4)))
+        return fail(KQ_ERR_ARG,
+                    "%s: misaligned pointer (w=%p xq=%p need 16, y=%p residual=%p need 4)", fn, w,
+                    xq, (void*)y, (const void*)residual);
     const int64_t wn = m * (k / 256) * wbytes;
     const int64_t xn = (int64_t)batch * (k / 32) * 36;
     const int64_t yn = (int64_t)batch * m * 4;
@@ -157,8 +158,8 @@ int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, in
     if (m < 0 || m > KQ_MAX_ROWS || n < 0 || n > 65535LL * 128)
         return fail(KQ_ERR_ARG, "%s: m=%lld or n=%lld out of range (m <= %d, n <= %lld)", fn,
                     (long long)m, (long long)n, KQ_MAX_ROWS, 65535LL * 128);
-    if (!aligned(w, 16) || !aligned(xq, 4) || !aligned(y, 4))
-        return fail(KQ_ERR_ARG, "%s: misaligned pointer (w=%p needs 16, xq=%p y=%p need 4)", fn, w,
+    if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(y, 4))
+        return fail(KQ_ERR_ARG, "%s: misaligned pointer (w=%p xq=%p need 16, y=%p needs 4)", fn, w,
                     xq, (void*)y);
     const int64_t yn = n * m * 4;
     if (overlap(y, yn, w, m * (k / 256) * 144) || overlap(y, yn, xq, n * (k / 32) * 36))

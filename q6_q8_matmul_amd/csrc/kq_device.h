@@ -22,6 +22,14 @@ __device__ __forceinline__ uint32_t float_to_half_bits(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Plain 16-byte load (global_load_dwordx4).
+__device__ __forceinline__ uint4 load16(const void* p) {
+    const u32x4_t v = *(const u32x4_t*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }

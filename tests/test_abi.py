@@ -85,6 +85,7 @@ def test_quantize_rejects(kq, args, needle):
     ((W, X, Y, None, 8, 256, 5, None), "batch=5"),
     ((W + 8, X, Y, None, 8, 256, 1, None), "misaligned"),
     ((W, X + 1, Y, None, 8, 256, 1, None), "misaligned"),
+    ((W, X + 4, Y, None, 8, 256, 1, None), "misaligned"),
     ((W, X, Y + 2, None, 8, 256, 1, None), "misaligned"),
     ((W, X, Y, R + 2, 8, 256, 1, None), "misaligned"),
     ((W, X, W + 16, None, 8, 256, 1, None), "overlaps"),
@@ -105,6 +106,7 @@ def test_gemv_rejects(kq, fn, args, needle):
     ((W, X, Y, 8, -1, 256, None), "n=-1"),
     ((W, X, Y, 8, 65535 * 128 + 1, 256, None), "out of range"),
     ((W + 4, X, Y, 8, 8, 256, None), "misaligned"),
+    ((W, X + 4, Y, 8, 8, 256, None), "misaligned"),
     ((W, X, W, 8, 8, 256, None), "overlaps"),
 ])
 def test_mmq_rejects(kq, args, needle):
