@@ -121,7 +121,8 @@ int kq_gemv_q6k(const void* w, const void* xq, float* y, const float* residual,
  *   w    [m][k/256] Q4_K superblocks, 16-byte aligned.
  *   xq   [n][k/32] q8_1 blocks, 16-byte aligned.
  *   y    out: f32 [n][m], 4-byte aligned; must not overlap w or xq.
- *   m >= 0, n >= 0, k > 0, k % 256 == 0, k <= KQ_MAX_K.
+ *   m >= 0, n >= 0, k > 0, k % 256 == 0, k <= KQ_MAX_K, n <= 65535*128;
+ *   w and xq are each smaller than 4 GiB (m*k/256*144 and n*k/32*36 bytes).
  * Same value per output as kq_gemv_q4k without a residual.
  */
 int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,

@@ -161,8 +161,12 @@ int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, in
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(y, 4))
         return fail(KQ_ERR_ARG, "%s: misaligned pointer (w=%p xq=%p need 16, y=%p needs 4)", fn, w,
                     xq, (void*)y);
+    const int64_t wbytes = m * (k / 256) * 144, xbytes = n * (k / 32) * 36;
+    if (wbytes >= (1LL << 32) || xbytes >= (1LL << 32))
+        return fail(KQ_ERR_ARG, "%s: w (%lld bytes) or xq (%lld bytes) is 4 GiB or larger", fn,
+                    (long long)wbytes, (long long)xbytes);
     const int64_t yn = n * m * 4;
-    if (overlap(y, yn, w, m * (k / 256) * 144) || overlap(y, yn, xq, n * (k / 32) * 36))
+    if (overlap(y, yn, w, wbytes) || overlap(y, yn, xq, xbytes))
         return fail(KQ_ERR_ARG, "%s: output y=%p overlaps an input (w=%p, xq=%p)", fn, (void*)y, w, xq);
     if (m == 0 || n == 0) return ok();
     if (int rc = check_device(fn, nullptr)) return rc;

@@ -14,14 +14,18 @@
 // tokens; each wavefront a 64 x 64 block of four 32 x 32 MFMA tiles.  The K
 // loop walks one superblock (256 values, 8 q8_1 blocks) at a time:
 //   * raw Q4_K superblocks of the 128 rows -> LDS (16-byte loads);
-//     per row and sub-block the f32 pair (D, Mn) -> LDS;
+//     per row and sub-block the f32 pair (D, -Mn) -> LDS;
 //   * q8_1 blocks of the 128 tokens -> LDS as int8 codes (rows padded to
 //     272 bytes against bank conflicts) plus per (token, block) d8 and
 //     d8*Bq;
-//   * per block: nibbles -> int8 operand in registers, 4 MFMAs, scale
-//     epilogue into a per-superblock f32 partial; the partials are added to
-//     the output accumulator once per superblock, so each output sees about
-//     8 + k/256 f32 additions in sequence.
+//   * per pair of blocks (the low and high nibbles of the same 32 code
+//     bytes): nibbles -> two int8 operands in registers, two int8 MFMAs
+//     give the exact block dots; one f32 MFMA forms both blocks' scale outer
+//     products D (x) d8, another accumulates the minimum terms; the VALU only
+//     converts the dots and applies the scales (2 instructions per output
+//     and block).  Per-superblock partials are added to the output
+//     accumulator once per superblock, so each output sees about
+//     12 + k/256 f32 roundings in sequence.
 // Outputs beyond m or n are computed from clamped (valid) rows/tokens and not
 // stored.  No atomics; results are bitwise reproducible.
 #include "kq_device.h"
@@ -31,24 +35,26 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v32f __attribute__((ext_vector_type(32)));
 
 constexpr int BM = 128;            // weight rows per workgroup
 constexpr int BN = 128;            // tokens per workgroup
 constexpr int kCodeStride = 272;   // LDS bytes per token row of codes (256 + 16 pad)
+constexpr int kTokStride = 9;      // floats per token in the d8 / z planes (8 + 1 pad)
 
 struct Smem {
     uint8_t wraw[BM * kQ4KBytes];        // raw superblocks, 144 bytes per row
-    float dsc[8][BM];                    // D = d*sc   per (block, row)
-    float msc[8][BM];                    // Mn = dmin*m per (block, row)
+    float dsc[8][BM];                    // D = d*sc    per (block, row)
+    float nmn[8][BM];                    // -Mn = -dmin*m per (block, row)
     int8_t codes[BN * kCodeStride];      // q8 codes per token
-    float d8[BN][8];                     // per (token, block)
-    float z[BN][8];                      // d8 * Bq
+    float d8[BN * kTokStride];           // per (token, block)
+    float z[BN * kTokStride];            // d8 * (sum of the block's codes)
 };
 
-__global__ __launch_bounds__(256) void mmq_q4k_kernel(const uint8_t* __restrict__ w,
-                                                      const uint8_t* __restrict__ xq,
-                                                      float* __restrict__ y, int M, int N,
-                                                      int S) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq,
+                    float* __restrict__ y, int M, int N, int S) {
     __shared__ __align__(16) Smem sm;
 
     const int tid = threadIdx.x;
@@ -90,7 +96,7 @@ __global__ __launch_bounds__(256) void mmq_q4k_kernel(const uint8_t* __restrict_
                 const uint32_t s4 = j < 4 ? lowS : hiS, m4 = j < 4 ? lowM : hiM;
                 const int sh = 8 * (j & 3);
                 sm.dsc[j][tid] = d * (float)((s4 >> sh) & 0xff);
-                sm.msc[j][tid] = dmin * (float)((m4 >> sh) & 0xff);
+                sm.nmn[j][tid] = -(dmin * (float)((m4 >> sh) & 0xff));
             }
         }
         // ---- activations: 128 tokens x 8 q8_1 blocks
@@ -108,12 +114,19 @@ __global__ __launch_bounds__(256) void mmq_q4k_kernel(const uint8_t* __restrict_
             uint4* dst = (uint4*)(sm.codes + t * kCodeStride + 32 * j);
             dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
             dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
-            sm.d8[t][j] = d8;
-            sm.z[t][j] = d8 * (float)s;
+            sm.d8[t * kTokStride + j] = d8;
+            sm.z[t * kTokStride + j] = d8 * (float)s;
         }
         __syncthreads();
 
-        float part[2][2][16];
+        // Per-superblock partial of every output.  Each pair of blocks
+        // (2p, 2p+1) -- the low and high nibbles of the same code bytes --
+        // contributes, per 32 x 32 tile:
+        //   part += (-Mn) (x) z        f32 MFMA, K = 2 (the two blocks)
+        //   S     = D (x) d8           f32 MFMA, two outer products
+        //   part += float(A_2p) * S_2p + float(A_2p+1) * S_2p+1   (VALU)
+        // with A the exact int32 block dots from the int8 MFMA.
+        v16f part[2][2];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -121,53 +134,52 @@ __global__ __launch_bounds__(256) void mmq_q4k_kernel(const uint8_t* __restrict_
 #pragma unroll
                 for (int i = 0; i < 16; ++i) part[a][b][i] = 0.0f;
 
-#pragma unroll 2
-        for (int j = 0; j < 8; ++j) {
-            const int c = j >> 1, hi = j & 1;
-            // A operands: weight rows (l32) of the wave's two 32-row tiles
-            v4i A[2];
+#pragma unroll 1
+        for (int pp = 0; pp < 4; ++pp) {
+            const int jl = 2 * pp + h2;   // this lane's block within the pair for the f32 MFMAs
+            v4i A[2][2];
+            float Dp[2], Mp[2];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 const int r = wm * 64 + mt * 32 + l32;
-                const uint4 q = *(const uint4*)(sm.wraw + r * kQ4KBytes + 16 + 32 * c + 16 * h2);
-                const uint32_t sft = hi ? 4u : 0u;
-                A[mt] = v4i{(int)((q.x >> sft) & 0x0f0f0f0fu), (int)((q.y >> sft) & 0x0f0f0f0fu),
-                            (int)((q.z >> sft) & 0x0f0f0f0fu), (int)((q.w >> sft) & 0x0f0f0f0fu)};
+                const uint4 q = *(const uint4*)(sm.wraw + r * kQ4KBytes + 16 + 32 * pp + 16 * h2);
+                A[mt][0] = v4i{(int)(q.x & 0x0f0f0f0fu), (int)(q.y & 0x0f0f0f0fu),
+                               (int)(q.z & 0x0f0f0f0fu), (int)(q.w & 0x0f0f0f0fu)};
+                A[mt][1] = v4i{(int)((q.x >> 4) & 0x0f0f0f0fu), (int)((q.y >> 4) & 0x0f0f0f0fu),
+                               (int)((q.z >> 4) & 0x0f0f0f0fu), (int)((q.w >> 4) & 0x0f0f0f0fu)};
+                Dp[mt] = sm.dsc[jl][r];
+                Mp[mt] = sm.nmn[jl][r];
             }
-            // B operands: tokens (l32) of the wave's two 32-token tiles
-            v4i B[2];
-            float d8n[2], zn[2];
+            v4i B[2][2];
+            float dp[2], zp[2];
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
                 const int t = wn * 64 + nt * 32 + l32;
-                const uint4 a = *(const uint4*)(sm.codes + t * kCodeStride + 32 * j + 16 * h2);
-                B[nt] = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
-                d8n[nt] = sm.d8[t][j];
-                zn[nt] = sm.z[t][j];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const uint4 a = *(const uint4*)(sm.codes + t * kCodeStride + 32 * (2 * pp + e) + 16 * h2);
+                    B[nt][e] = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+                }
+                dp[nt] = sm.d8[t * kTokStride + jl];
+                zp[nt] = sm.z[t * kTokStride + jl];
             }
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                // rows of this lane's 16 outputs: 8*(i/4) + 4*h2 + (i%4)
-                float Dm[16], Mm[16];
-#pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) {
-                    const int rb = wm * 64 + mt * 32 + 8 * a4 + 4 * h2;
-                    const float4 dv = *(const float4*)&sm.dsc[j][rb];
-                    const float4 mv = *(const float4*)&sm.msc[j][rb];
-                    Dm[4 * a4 + 0] = dv.x; Dm[4 * a4 + 1] = dv.y; Dm[4 * a4 + 2] = dv.z; Dm[4 * a4 + 3] = dv.w;
-                    Mm[4 * a4 + 0] = mv.x; Mm[4 * a4 + 1] = mv.y; Mm[4 * a4 + 2] = mv.z; Mm[4 * a4 + 3] = mv.w;
-                }
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
-                    v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-                    const v16i r = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mt], B[nt], zero, 0, 0, 0);
+                    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+                    const v32f zf = {};
+                    const v16i R0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mt][0], B[nt][0], zero, 0, 0, 0);
+                    const v16i R1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mt][1], B[nt][1], zero, 0, 0, 0);
+                    const v32f S = __builtin_amdgcn_mfma_f32_32x32x1f32(Dp[mt], dp[nt], zf, 0, 0, 0);
+                    v16f pt = __builtin_amdgcn_mfma_f32_32x32x2f32(Mp[mt], zp[nt], part[mt][nt], 0, 0, 0);
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const float s = Dm[i] * d8n[nt];
-                        part[mt][nt][i] += (float)r[i] * s - Mm[i] * zn[nt];
+                        pt[i] += (float)R0[i] * S[i];
+                        pt[i] += (float)R1[i] * S[16 + i];
                     }
+                    part[mt][nt] = pt;
                 }
-            }
         }
 #pragma unroll
         for (int a = 0; a < 2; ++a)

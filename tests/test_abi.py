@@ -108,6 +108,8 @@ def test_gemv_rejects(kq, fn, args, needle):
     ((W + 4, X, Y, 8, 8, 256, None), "misaligned"),
     ((W, X + 4, Y, 8, 8, 256, None), "misaligned"),
     ((W, X, W, 8, 8, 256, None), "overlaps"),
+    ((W, X, Y, 1 << 24, 8, 65536, None), "4 GiB"),
+    ((W, X, Y, 8, 1 << 20, 65536, None), "4 GiB"),
 ])
 def test_mmq_rejects(kq, args, needle):
     rc = kq.lib().kq_mmq_q4k(*args)
