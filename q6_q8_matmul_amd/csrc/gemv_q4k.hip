@@ -19,6 +19,10 @@
 //   * the loads of the first DEPTH passes are issued before anything else and
 //     every later pass is requested DEPTH passes ahead (a register ring), so
 //     HBM latency overlaps the activation staging and the arithmetic;
+//   * when the whole activation fits in LDS the grid is persistent: a few
+//     workgroups per compute unit stage it once and walk the row groups
+//     (blockIdx.x, blockIdx.x + gridDim.x, ...), and the load ring runs on
+//     across row groups, so the memory pipe never drains between them;
 //   * the q8_1 activation is restaged once per workgroup into LDS: per
 //     superblock the 16-byte slices in the order the lanes read them, and per
 //     lane the four d8 values and the four d8 * (sum of the slice's codes);
@@ -36,6 +40,9 @@
 // No atomics; the reduction order is fixed, so results are bitwise
 // reproducible.
 #include "kq_device.h"
+
+#include <algorithm>
+#include <atomic>
 
 namespace kq {
 namespace gemv4 {
@@ -190,7 +197,47 @@ __device__ __forceinline__ float half_wave_sum(float v) {
     return v;
 }
 
-template <int BATCH, int RPW, int DEPTH, int WAVES>
+// Row pointers of row group g for this lane (rows past m are clamped: they
+// are computed, not stored).
+template <int RPW>
+__device__ __forceinline__ void group_rows(const uint8_t* (&rowp)[RPW], const uint8_t* w, int g,
+                                           int waves, int wave, int half, int m,
+                                           int64_t row_bytes) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int r = min(2 * ((g * waves + wave) * RPW + i) + half, m - 1);
+        rowp[i] = w + (int64_t)r * row_bytes;
+    }
+}
+
+// Half-wavefront sums of the accumulators, residual add and store (lane 0 of
+// each half), then reset.
+template <int BATCH, int RPW>
+__device__ __forceinline__ void finish_rows(float (&acc)[RPW][BATCH], float* y,
+                                            const float* residual, int pair0, int half, int lane,
+                                            int m) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int r = 2 * (pair0 + i) + half;
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            const float v = half_wave_sum(acc[i][b]);
+            if ((lane & 31) == 0 && r < m) {
+                const int64_t o = (int64_t)b * m + r;
+                y[o] = residual ? residual[o] + v : v;
+            }
+            acc[i][b] = 0.0f;
+        }
+    }
+}
+
+// PERSIST = false: one workgroup per WAVES*RPW row pairs, every workgroup
+// stages the activation (in chunks if needed).
+// PERSIST = true (only when the whole activation fits in LDS): a grid of a
+// few workgroups per compute unit stages it once and walks the row groups
+// blockIdx.x, blockIdx.x + gridDim.x, ...; the load ring runs across group
+// boundaries.
+template <int BATCH, int RPW, int DEPTH, int WAVES, bool PERSIST>
 __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __restrict__ w,
                                                               const uint8_t* __restrict__ xq,
                                                               float* y, const float* residual,
@@ -202,18 +249,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __r
     const int half = lane >> 5;
     const int grp = (lane >> 2) & 7;   // superblock within a pass
     const int t = lane & 3;            // slice pair within the superblock
-    const int pair0 = (blockIdx.x * WAVES + wave) * RPW;   // first row pair of this wave
     const int64_t row_bytes = (int64_t)S * kQ4KBytes;
     const int nb_row = S * 8;
     const int npass = (S + 7) >> 3;
-    const int chunk_passes = schunk >> 3;   // schunk is a multiple of 8 superblocks
-
-    const uint8_t* rowp[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int r = min(2 * (pair0 + i) + half, m - 1);   // clamped rows are computed, not stored
-        rowp[i] = w + (int64_t)r * row_bytes;
-    }
 
     float acc[RPW][BATCH];
 #pragma unroll
@@ -222,60 +260,115 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __r
         for (int b = 0; b < BATCH; ++b) acc[i][b] = 0.0f;
 
     Slice ring[DEPTH][RPW];
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) load_pass<RPW>(ring[d], rowp, 8 * d + grp, S, t);
-
-    stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
-
-    for (int p0 = 0; p0 < npass; p0 += DEPTH) {
+    const uint8_t* rowp[RPW];
+    if constexpr (PERSIST) {
+        const int pairs_per_group = WAVES * RPW;
+        const int ngroups = (m + 2 * pairs_per_group - 1) / (2 * pairs_per_group);
+        const int nitems = ((ngroups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x) * npass;
+        // (group, pass) of the next item to load and of the next to compute
+        int gl = blockIdx.x, pl = 0;
+        group_rows<RPW>(rowp, w, gl, WAVES, wave, half, m, row_bytes);
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
-            const int p = p0 + d;
-            if (p < npass) {
-                const int chunk = p / chunk_passes;
-                const int pl = p - chunk * chunk_passes;   // pass within the staged chunk
-                if (pl == 0 && p > 0) {                    // uniform over the workgroup
-                    __syncthreads();
-                    const int kc = chunk * schunk;
-                    stage_activation<BATCH, 64 * WAVES>(xq, nb_row, kc * 8, min(schunk, S - kc) * 8,
-                                                        schunk, smem);
+            if (d < nitems) {
+                load_pass<RPW>(ring[d], rowp, 8 * pl + grp, S, t);
+                if (++pl == npass) {
+                    pl = 0;
+                    gl += gridDim.x;
+                    group_rows<RPW>(rowp, w, gl, WAVES, wave, half, m, row_bytes);
                 }
-                if (8 * p + grp < S)   // lanes past the row end add nothing
-                    compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pl + grp, t);
-                if (p + DEPTH < npass)
-                    load_pass<RPW>(ring[d], rowp, 8 * (p + DEPTH) + grp, S, t);
             }
         }
-    }
+        stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, S * 8, schunk, smem);
+        int gc = blockIdx.x, pc = 0;
+        for (int it0 = 0; it0 < nitems; it0 += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int it = it0 + d;
+                if (it < nitems) {
+                    if (8 * pc + grp < S)   // lanes past the row end add nothing
+                        compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pc + grp, t);
+                    if (it + DEPTH < nitems) {
+                        load_pass<RPW>(ring[d], rowp, 8 * pl + grp, S, t);
+                        if (++pl == npass) {
+                            pl = 0;
+                            gl += gridDim.x;
+                            group_rows<RPW>(rowp, w, gl, WAVES, wave, half, m, row_bytes);
+                        }
+                    }
+                    if (++pc == npass) {
+                        finish_rows<BATCH, RPW>(acc, y, residual, (gc * WAVES + wave) * RPW, half,
+                                                lane, m);
+                        pc = 0;
+                        gc += gridDim.x;
+                    }
+                }
+            }
+        }
+    } else {
+        const int pair0 = (blockIdx.x * WAVES + wave) * RPW;   // first row pair of this wave
+        const int chunk_passes = schunk >> 3;   // schunk is a multiple of 8 superblocks
+        group_rows<RPW>(rowp, w, blockIdx.x, WAVES, wave, half, m, row_bytes);
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) load_pass<RPW>(ring[d], rowp, 8 * d + grp, S, t);
 
+        stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
+
+        for (int p0 = 0; p0 < npass; p0 += DEPTH) {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int r = 2 * (pair0 + i) + half;
-#pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
-            const float v = half_wave_sum(acc[i][b]);
-            if ((lane & 31) == 0 && r < m) {
-                const int64_t o = (int64_t)b * m + r;
-                y[o] = residual ? residual[o] + v : v;
+            for (int d = 0; d < DEPTH; ++d) {
+                const int p = p0 + d;
+                if (p < npass) {
+                    const int chunk = p / chunk_passes;
+                    const int pl = p - chunk * chunk_passes;   // pass within the staged chunk
+                    if (pl == 0 && p > 0) {                    // uniform over the workgroup
+                        __syncthreads();
+                        const int kc = chunk * schunk;
+                        stage_activation<BATCH, 64 * WAVES>(xq, nb_row, kc * 8,
+                                                            min(schunk, S - kc) * 8, schunk, smem);
+                    }
+                    if (8 * p + grp < S)   // lanes past the row end add nothing
+                        compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pl + grp, t);
+                    if (p + DEPTH < npass)
+                        load_pass<RPW>(ring[d], rowp, 8 * (p + DEPTH) + grp, S, t);
+                }
             }
         }
+        finish_rows<BATCH, RPW>(acc, y, residual, pair0, half, lane, m);
     }
 }
 
+// Launch one variant.  `persist_per_cu` > 0 asks for the persistent form with
+// that many workgroups per compute unit (capped by occupancy); it is used
+// only when the whole activation fits in one LDS piece.
 template <int BATCH, int RPW, int DEPTH, int WAVES>
 hipError_t launch_variant(const void* w, const void* xq, float* y, const float* residual,
-                          int64_t m, int64_t k, int lds_budget, hipStream_t stream) {
+                          int64_t m, int64_t k, int lds_budget, int cus, int persist_per_cu,
+                          hipStream_t stream) {
     const int S = (int)(k / kQK);
     const int per_sb = BATCH * kLdsPerSb;
-    const int budget = lds_budget;
-    int schunk = (budget / per_sb) & ~7;          // whole passes of 8 superblocks
+    int schunk = (lds_budget / per_sb) & ~7;      // whole passes of 8 superblocks
     const int s_round = (S + 7) & ~7;
     if (schunk > s_round) schunk = s_round;
     if (schunk < 8) return hipErrorInvalidConfiguration;
     const size_t lds = (size_t)schunk * per_sb;
     const int rows_per_block = WAVES * RPW * 2;
-    const int64_t grid = (m + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL((gemv_q4k_kernel<BATCH, RPW, DEPTH, WAVES>), dim3((unsigned)grid),
+    const int64_t ngroups = (m + rows_per_block - 1) / rows_per_block;
+    if (persist_per_cu > 0 && schunk >= S) {
+        auto kern = gemv_q4k_kernel<BATCH, RPW, DEPTH, WAVES, true>;
+        static std::atomic<int> occ{0};
+        int o = occ.load(std::memory_order_relaxed);
+        if (o == 0) {
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, 64 * WAVES, lds) != hipSuccess || o < 1)
+                o = 1;
+            occ.store(o, std::memory_order_relaxed);
+        }
+        const int64_t grid = std::min<int64_t>(ngroups, (int64_t)cus * std::min(o, persist_per_cu));
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WAVES), lds, stream,
+                           (const uint8_t*)w, (const uint8_t*)xq, y, residual, (int)m, S, schunk);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((gemv_q4k_kernel<BATCH, RPW, DEPTH, WAVES, false>), dim3((unsigned)ngroups),
                        dim3(64 * WAVES), lds, stream, (const uint8_t*)w, (const uint8_t*)xq, y,
                        residual, (int)m, S, schunk);
     return hipGetLastError();
@@ -284,23 +377,30 @@ hipError_t launch_variant(const void* w, const void* xq, float* y, const float* 
 }  // namespace gemv4
 
 hipError_t launch_gemv_q4k(const void* w, const void* xq, float* y, const float* residual,
-                           int64_t m, int64_t k, int batch, int lds_limit, hipStream_t stream) {
+                           int64_t m, int64_t k, int batch, int lds_limit, int cus,
+                           hipStream_t stream) {
     using namespace gemv4;
-    // Launch shapes measured on MI355X (rocprofv3 kernel traces over the
-    // Llama-3-8B decode shapes): two row pairs per wavefront for tall
-    // matrices, one pair and eight wavefronts otherwise; when the whole row
-    // of a batch fits the device's LDS it is staged in one piece.
-    const int64_t s_round = ((k / kQK) + 7) & ~7;
+    // Launch shapes measured on MI355X (back-to-back launches over rotating
+    // weight copies, Llama-3-8B decode shapes).  Batch 1: one row pair per
+    // wavefront, one pass ahead, persistent grid -- eight wavefronts and three
+    // workgroups per CU for tall or long rows (gate|up 28672x4096: 12.3 us,
+    // down 4096x14336: 9.4 us), else four wavefronts and four workgroups
+    // (4096x4096: 4.8 us).  Batches 2-4 use the four-wavefront persistent
+    // form (QKV 6144x4096 at batch 4: 8.8 us) unless the activation only fits
+    // in several LDS pieces or needs more than 64 KB, where three passes in
+    // flight over eight wavefronts per row group work better.
+    const int S = (int)(k / kQK);
+    const int64_t s_round = (S + 7) & ~7;
     const int64_t whole = (int64_t)batch * kLdsPerSb * s_round;
     const int one_piece = whole <= lds_limit ? lds_limit : 65536;
-    const bool tall = m >= 16384;
+    const bool big = m >= 16384 || S > 16;
     switch (batch) {
-        case 1: return tall ? launch_variant<1, 2, 2, 4>(w, xq, y, residual, m, k, 65536, stream)
-                            : launch_variant<1, 1, 2, 8>(w, xq, y, residual, m, k, 65536, stream);
-        case 2: return launch_variant<2, 1, 2, 8>(w, xq, y, residual, m, k, one_piece, stream);
-        case 3: return launch_variant<3, 1, 2, 8>(w, xq, y, residual, m, k, one_piece, stream);
-        case 4: return whole > 65536 ? launch_variant<4, 1, 3, 8>(w, xq, y, residual, m, k, one_piece, stream)
-                                     : launch_variant<4, 2, 1, 8>(w, xq, y, residual, m, k, one_piece, stream);
+        case 1: return big ? launch_variant<1, 1, 1, 8>(w, xq, y, residual, m, k, 65536, cus, 3, stream)
+                           : launch_variant<1, 1, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 4, stream);
+        case 2: return launch_variant<2, 1, 1, 4>(w, xq, y, residual, m, k, one_piece, cus, 6, stream);
+        case 3: return launch_variant<3, 1, 1, 4>(w, xq, y, residual, m, k, one_piece, cus, 6, stream);
+        case 4: return whole > 65536 ? launch_variant<4, 1, 3, 8>(w, xq, y, residual, m, k, one_piece, cus, 0, stream)
+                                     : launch_variant<4, 1, 1, 4>(w, xq, y, residual, m, k, one_piece, cus, 6, stream);
         default: return hipErrorInvalidValue;
     }
 }

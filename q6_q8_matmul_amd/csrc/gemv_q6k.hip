@@ -10,9 +10,12 @@
 // two bytes before a superblock that starts at 2 (mod 4), which are the tail
 // of the previous superblock.
 //
-// Work layout (as the Q4_K GEMV): WAVES wavefronts x RPW rows per workgroup;
+// Work layout (as the Q4_K GEMV): WAVES wavefronts x RPW rows per row group;
 // 8 groups of 8 lanes take 8 consecutive superblocks of a row per pass; the
-// raw loads of each pass are requested DEPTH passes ahead of their use.
+// raw loads of each pass are requested DEPTH passes ahead of their use.  When
+// the activation fits in LDS the grid is persistent (a few workgroups per
+// compute unit walk the row groups) and the load ring runs on across row
+// groups.
 // Lane (h, q) of a group, h = 0..1, q = 0..3, owns values
 //   128h + 32g + 8q + i,   g = 0..3, i = 0..7,
 // which come from ql[64h + 8q + i] (g = 0, 2: low / high nibble),
@@ -29,6 +32,9 @@
 // optional residual add on the row write (leone-cuda "CUDA kernel design":
 // Q6_K GEMV with residual epilogue, fixed reduction order, no atomics).
 #include "kq_device.h"
+
+#include <algorithm>
+#include <atomic>
 
 namespace kq {
 namespace gemv6 {
@@ -188,7 +194,34 @@ __device__ __forceinline__ void compute_pass(const Raw (&r)[RPW], float (&acc)[R
     }
 }
 
-template <int BATCH, int RPW, int DEPTH, int WAVES>
+// Sum of each (row, column) accumulator over the wavefront, residual add and
+// store (lane 0).
+template <int BATCH, int RPW>
+__device__ __forceinline__ void finish_rows(float (&acc)[RPW][BATCH], float* y,
+                                            const float* residual, int row0, int m, int lane) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int r = row0 + i;
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            const float t = wave_sum(acc[i][b]);
+            if (lane == 0 && r < m) {
+                const int64_t o = (int64_t)b * m + r;
+                y[o] = residual ? residual[o] + t : t;
+            }
+            acc[i][b] = 0.0f;
+        }
+    }
+}
+
+// PERSIST = false: one workgroup per WAVES*RPW rows; the activation is
+// staged (in chunks if needed) by every workgroup.
+// PERSIST = true (only when the whole activation fits in LDS): a grid of a
+// few workgroups per compute unit stages the activation once and walks the
+// row groups blockIdx.x, blockIdx.x + gridDim.x, ...; the load ring runs
+// across group boundaries, so a wavefront's next rows are already in flight
+// while it finishes the current ones.
+template <int BATCH, int RPW, int DEPTH, int WAVES, bool PERSIST>
 __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __restrict__ w,
                                                               const uint8_t* __restrict__ xq,
                                                               float* y, const float* residual,
@@ -201,11 +234,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __r
     const int k8 = lane & 7;
     const int h = k8 >> 2;          // 128-value half of the superblock
     const int q = k8 & 3;           // 8-value slice within each 32-value group
-    const int row0 = (blockIdx.x * WAVES + wave) * RPW;
     const int64_t row_bytes = (int64_t)S * kQ6KBytes;
     const int nb_row = S * 8;
     const int npass = (S + 7) >> 3;
-    const int chunk_passes = schunk >> 3;
 
     float acc[RPW][BATCH];
 #pragma unroll
@@ -214,61 +245,103 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __r
         for (int b = 0; b < BATCH; ++b) acc[i][b] = 0.0f;
 
     Raw ring[DEPTH][RPW];
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-        load_pass<RPW>(ring[d], w, row0, m, row_bytes, 8 * d + grp, S, h, q);
-
-    stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
-
-    for (int p0 = 0; p0 < npass; p0 += DEPTH) {
+    if constexpr (PERSIST) {
+        const int rows_per_group = WAVES * RPW;
+        const int ngroups = (m + rows_per_group - 1) / rows_per_group;
+        const int nitems = ((ngroups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x) * npass;
+        // (group, pass) of the next item to load and of the next to compute
+        int gl = blockIdx.x, pl = 0;
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
-            const int p = p0 + d;
-            if (p < npass) {
-                const int chunk = p / chunk_passes;
-                const int pl = p - chunk * chunk_passes;
-                if (pl == 0 && p > 0) {
-                    __syncthreads();
-                    const int kc = chunk * schunk;
-                    stage_activation<BATCH, 64 * WAVES>(xq, nb_row, kc * 8, min(schunk, S - kc) * 8,
-                                                        schunk, smem);
+            if (d < nitems) {
+                load_pass<RPW>(ring[d], w, (gl * WAVES + wave) * RPW, m, row_bytes, 8 * pl + grp, S, h, q);
+                if (++pl == npass) { pl = 0; gl += gridDim.x; }
+            }
+        }
+        stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, S * 8, schunk, smem);
+        int gc = blockIdx.x, pc = 0;
+        for (int it0 = 0; it0 < nitems; it0 += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                const int it = it0 + d;
+                if (it < nitems) {
+                    if (8 * pc + grp < S) compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pc + grp, h, q);
+                    if (it + DEPTH < nitems) {
+                        load_pass<RPW>(ring[d], w, (gl * WAVES + wave) * RPW, m, row_bytes, 8 * pl + grp, S, h, q);
+                        if (++pl == npass) { pl = 0; gl += gridDim.x; }
+                    }
+                    if (++pc == npass) {
+                        finish_rows<BATCH, RPW>(acc, y, residual, (gc * WAVES + wave) * RPW, m, lane);
+                        pc = 0;
+                        gc += gridDim.x;
+                    }
                 }
-                if (8 * p + grp < S)
-                    compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pl + grp, h, q);
-                if (p + DEPTH < npass)
-                    load_pass<RPW>(ring[d], w, row0, m, row_bytes, 8 * (p + DEPTH) + grp, S, h, q);
             }
         }
-    }
+    } else {
+        const int row0 = (blockIdx.x * WAVES + wave) * RPW;
+        const int chunk_passes = schunk >> 3;
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d)
+            load_pass<RPW>(ring[d], w, row0, m, row_bytes, 8 * d + grp, S, h, q);
 
+        stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
+
+        for (int p0 = 0; p0 < npass; p0 += DEPTH) {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int r = row0 + i;
-#pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
-            const float t = wave_sum(acc[i][b]);
-            if (lane == 0 && r < m) {
-                const int64_t o = (int64_t)b * m + r;
-                y[o] = residual ? residual[o] + t : t;
+            for (int d = 0; d < DEPTH; ++d) {
+                const int p = p0 + d;
+                if (p < npass) {
+                    const int chunk = p / chunk_passes;
+                    const int pl = p - chunk * chunk_passes;
+                    if (pl == 0 && p > 0) {
+                        __syncthreads();
+                        const int kc = chunk * schunk;
+                        stage_activation<BATCH, 64 * WAVES>(xq, nb_row, kc * 8, min(schunk, S - kc) * 8,
+                                                            schunk, smem);
+                    }
+                    if (8 * p + grp < S)
+                        compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pl + grp, h, q);
+                    if (p + DEPTH < npass)
+                        load_pass<RPW>(ring[d], w, row0, m, row_bytes, 8 * (p + DEPTH) + grp, S, h, q);
+                }
             }
         }
+        finish_rows<BATCH, RPW>(acc, y, residual, row0, m, lane);
     }
 }
 
+// Launch one variant.  `persist_per_cu` > 0 asks for the persistent form with
+// that many workgroups per compute unit (capped by occupancy); it is used
+// only when the whole activation fits in one LDS piece.
 template <int BATCH, int RPW, int DEPTH, int WAVES>
 hipError_t launch_variant(const void* w, const void* xq, float* y, const float* residual,
-                          int64_t m, int64_t k, int lds_budget, hipStream_t stream) {
+                          int64_t m, int64_t k, int lds_budget, int cus, int persist_per_cu,
+                          hipStream_t stream) {
     const int S = (int)(k / kQK);
     const int per_sb = BATCH * kLdsPerSb;
-    const int budget = lds_budget;
-    int schunk = (budget / per_sb) & ~7;
+    int schunk = (lds_budget / per_sb) & ~7;
     const int s_round = (S + 7) & ~7;
     if (schunk > s_round) schunk = s_round;
     if (schunk < 8) return hipErrorInvalidConfiguration;
     const size_t lds = (size_t)schunk * per_sb;
     const int rows_per_block = WAVES * RPW;
-    const int64_t grid = (m + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL((gemv_q6k_kernel<BATCH, RPW, DEPTH, WAVES>), dim3((unsigned)grid),
+    const int64_t ngroups = (m + rows_per_block - 1) / rows_per_block;
+    if (persist_per_cu > 0 && schunk >= S) {
+        auto kern = gemv_q6k_kernel<BATCH, RPW, DEPTH, WAVES, true>;
+        static std::atomic<int> occ{0};
+        int o = occ.load(std::memory_order_relaxed);
+        if (o == 0) {
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, 64 * WAVES, lds) != hipSuccess || o < 1)
+                o = 1;
+            occ.store(o, std::memory_order_relaxed);
+        }
+        const int64_t grid = std::min<int64_t>(ngroups, (int64_t)cus * std::min(o, persist_per_cu));
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WAVES), lds, stream,
+                           (const uint8_t*)w, (const uint8_t*)xq, y, residual, (int)m, S, schunk);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((gemv_q6k_kernel<BATCH, RPW, DEPTH, WAVES, false>), dim3((unsigned)ngroups),
                        dim3(64 * WAVES), lds, stream, (const uint8_t*)w, (const uint8_t*)xq, y,
                        residual, (int)m, S, schunk);
     return hipGetLastError();
@@ -277,15 +350,20 @@ hipError_t launch_variant(const void* w, const void* xq, float* y, const float* 
 }  // namespace gemv6
 
 hipError_t launch_gemv_q6k(const void* w, const void* xq, float* y, const float* residual,
-                           int64_t m, int64_t k, int batch, int lds_limit, hipStream_t stream) {
+                           int64_t m, int64_t k, int batch, int lds_limit, int cus,
+                           hipStream_t stream) {
     using namespace gemv6;
-    // Launch shapes measured on MI355X (rocprofv3 kernel traces over the
-    // 128256 x 4096 output head): four rows per wavefront, one pass ahead.
+    (void)lds_limit;
+    // Launch shape measured on MI355X over the 128256 x 4096 output head
+    // (back-to-back launches on two rotating weight copies): two rows per
+    // wavefront, one pass ahead, persistent grid of up to six workgroups per
+    // compute unit -- 85 us at batch 1 (94 us for one workgroup per row
+    // group), 124 us at batch 4 (160 us).
     switch (batch) {
-        case 1: return launch_variant<1, 4, 2, 4>(w, xq, y, residual, m, k, 65536, stream);
-        case 2: return launch_variant<2, 4, 1, 4>(w, xq, y, residual, m, k, 65536, stream);
-        case 3: return launch_variant<3, 4, 1, 4>(w, xq, y, residual, m, k, 65536, stream);
-        case 4: return launch_variant<4, 4, 1, 4>(w, xq, y, residual, m, k, 65536, stream);
+        case 1: return launch_variant<1, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
+        case 2: return launch_variant<2, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
+        case 3: return launch_variant<3, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
+        case 4: return launch_variant<4, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -45,8 +45,9 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 // Per device: 0 unknown, 1 gfx950, -1 other.  Also the LDS limit per block.
 std::atomic<int> g_arch[64];
 std::atomic<int> g_lds[64];
+std::atomic<int> g_cus[64];
 
-int check_device(const char* fn, int* lds_limit) {
+int check_device(const char* fn, int* lds_limit, int* cus = nullptr) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess || dev < 0)
@@ -61,6 +62,7 @@ int check_device(const char* fn, int* lds_limit) {
                         hipGetErrorString(e));
         state = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
         g_lds[dev].store((int)prop.sharedMemPerBlock, std::memory_order_relaxed);
+        g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
         g_arch[dev].store(state, std::memory_order_release);
         if (state < 0)
             return fail(KQ_ERR_UNSUPPORTED, "%s: device %d is %s, not gfx950", fn, dev,
@@ -68,6 +70,7 @@ int check_device(const char* fn, int* lds_limit) {
     }
     if (state < 0) return fail(KQ_ERR_UNSUPPORTED, "%s: device %d is not gfx950", fn, dev);
     if (lds_limit) *lds_limit = g_lds[dev].load(std::memory_order_relaxed);
+    if (cus) *cus = g_cus[dev].load(std::memory_order_relaxed);
     return KQ_OK;
 }
 
@@ -134,9 +137,10 @@ int kq_gemv_q4k(const void* w, const void* xq, float* y, const float* residual, 
     const char* fn = "kq_gemv_q4k";
     if (int rc = gemv_common(fn, 144, w, xq, y, residual, m, k, batch)) return rc;
     if (m == 0) return ok();
-    int lds = 0;
-    if (int rc = check_device(fn, &lds)) return rc;
-    return launched(fn, kq::launch_gemv_q4k(w, xq, y, residual, m, k, batch, lds, (hipStream_t)stream));
+    int lds = 0, cus = 0;
+    if (int rc = check_device(fn, &lds, &cus)) return rc;
+    return launched(fn, kq::launch_gemv_q4k(w, xq, y, residual, m, k, batch, lds, cus,
+                                            (hipStream_t)stream));
 }
 
 int kq_gemv_q6k(const void* w, const void* xq, float* y, const float* residual, int64_t m,
@@ -144,9 +148,10 @@ int kq_gemv_q6k(const void* w, const void* xq, float* y, const float* residual, 
     const char* fn = "kq_gemv_q6k";
     if (int rc = gemv_common(fn, 210, w, xq, y, residual, m, k, batch)) return rc;
     if (m == 0) return ok();
-    int lds = 0;
-    if (int rc = check_device(fn, &lds)) return rc;
-    return launched(fn, kq::launch_gemv_q6k(w, xq, y, residual, m, k, batch, lds, (hipStream_t)stream));
+    int lds = 0, cus = 0;
+    if (int rc = check_device(fn, &lds, &cus)) return rc;
+    return launched(fn, kq::launch_gemv_q6k(w, xq, y, residual, m, k, batch, lds, cus,
+                                            (hipStream_t)stream));
 }
 
 int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,

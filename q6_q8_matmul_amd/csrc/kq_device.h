@@ -46,9 +46,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 hipError_t launch_quantize_q8_1(const float* x, void* xq, int64_t rows, int64_t k,
                                 hipStream_t stream);
 hipError_t launch_gemv_q4k(const void* w, const void* xq, float* y, const float* residual,
-                           int64_t m, int64_t k, int batch, int lds_limit, hipStream_t stream);
+                           int64_t m, int64_t k, int batch, int lds_limit, int cus,
+                           hipStream_t stream);
 hipError_t launch_gemv_q6k(const void* w, const void* xq, float* y, const float* residual,
-                           int64_t m, int64_t k, int batch, int lds_limit, hipStream_t stream);
+                           int64_t m, int64_t k, int batch, int lds_limit, int cus,
+                           hipStream_t stream);
 hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                           int64_t k, hipStream_t stream);
 

@@ -129,7 +129,7 @@ SHAPES = [
     ("q4k", 300, 4352, 1, False),
     ("q6k", 1, 256, 1, False), ("q6k", 7, 768, 3, True), ("q6k", 13, 2304, 2, False),
     ("q6k", 1001, 1280, 4, True), ("q6k", 37, 14336, 4, True), ("q6k", 9, 32768, 4, False),
-    ("q6k", 300, 4352, 1, False),
+    ("q6k", 300, 4352, 1, False), ("q6k", 20001, 512, 3, True),
 ]
 
 
