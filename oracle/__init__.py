@@ -58,6 +58,11 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
         "kqo_matmul_factored": ([i32, p, p, p, i64, i64, i64, p], i32),
         "kqo_f32_to_f16_array": ([p, p, i64], None),
         "kqo_f16_to_f32_array": ([p, p, i64], None),
+        "kqo_exp_array": ([p, p, i64], None),
+        "kqo_silu_array": ([p, p, i64], None),
+        "kqo_rms_sumsq": ([p, i64], ctypes.c_float),
+        "kqo_rmsnorm_q8_1": ([p, p, p, ctypes.c_float, p, p, i64, i64], None),
+        "kqo_swiglu_q8_1": ([p, p, p, p, i64, i64], None),
         "kqo_set_threads": ([i32], None),
         "kqo_max_threads": ([], i32),
     }
@@ -145,6 +150,68 @@ def dequant_q8_1(xq: np.ndarray, rows: int, k: int) -> np.ndarray:
     out = np.empty((rows, k), dtype=np.float32)
     lib().kqo_dequant_q8_1(_ptr(xq), _ptr(out), rows, k)
     return out
+
+
+# ------------------------------------------------------------ producers ----
+
+def exp_f32(a) -> np.ndarray:
+    """The producers' exponential e(a) (Cody-Waite reduction, degree-7 Taylor)."""
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float32).ravel())
+    out = np.empty_like(a)
+    lib().kqo_exp_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def silu_f32(t) -> np.ndarray:
+    t = np.ascontiguousarray(np.asarray(t, dtype=np.float32).ravel())
+    out = np.empty_like(t)
+    lib().kqo_silu_array(_ptr(t), _ptr(out), t.size)
+    return out
+
+
+def rms_sumsq(h) -> float:
+    """Sum of squares of one row in the RMSNorm reduction order (n % 256 == 0)."""
+    h = np.ascontiguousarray(np.asarray(h, dtype=np.float32).ravel())
+    if h.size % 256:
+        raise ValueError("n must be a multiple of 256")
+    return float(lib().kqo_rms_sumsq(_ptr(h), h.size))
+
+
+def _rows2(a):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a[None, :] if a.ndim == 1 else a
+
+
+def rmsnorm_q8_1(x, g, eps: float, residual=None):
+    """RMSNorm (of x + residual when given) times g, and its q8_1 blocks.
+    Returns (y f32 [rows, n], xq uint8 [rows, n/32*36])."""
+    x = _rows2(x)
+    rows, n = x.shape
+    if n % 256:
+        raise ValueError("n must be a multiple of 256")
+    g = np.ascontiguousarray(g, dtype=np.float32).ravel()
+    assert g.size == n
+    res = None if residual is None else _rows2(residual)
+    if res is not None:
+        assert res.shape == x.shape
+    y = np.empty((rows, n), dtype=np.float32)
+    xq = np.empty((rows, (n // 32) * 36), dtype=np.uint8)
+    lib().kqo_rmsnorm_q8_1(_ptr(x), _ptr(res), _ptr(g), ctypes.c_float(eps), _ptr(y), _ptr(xq),
+                           rows, n)
+    return y, xq
+
+
+def swiglu_q8_1(gate, up):
+    """silu(gate) * up and its q8_1 blocks.  Returns (y, xq)."""
+    gate, up = _rows2(gate), _rows2(up)
+    assert gate.shape == up.shape
+    rows, n = gate.shape
+    if n % 32:
+        raise ValueError("n must be a multiple of 32")
+    y = np.empty((rows, n), dtype=np.float32)
+    xq = np.empty((rows, (n // 32) * 36), dtype=np.uint8)
+    lib().kqo_swiglu_q8_1(_ptr(gate), _ptr(up), _ptr(y), _ptr(xq), rows, n)
+    return y, xq
 
 
 # -------------------------------------------------------------- weights ----

@@ -41,6 +41,27 @@
  *    "CUDA kernel design": Q4_K forms each minimum correction from the same
  *    lane-local codes).
  *
+ *  - The fused producers that emit q8_1 directly (leone-cuda "CUDA kernel
+ *    design": RMSNorm and SwiGLU write their q8_1 blocks so that no
+ *    standalone quantisation precedes the next GEMV; RMSNorm uses sqrtf, not
+ *    an approximate reciprocal square root, and a fixed reduction order; the
+ *    residual variant normalises left + right).  The pages fix neither the
+ *    reduction order nor the exponential, so both are defined here and the
+ *    GPU must reproduce them bit for bit:
+ *      RMSNorm row of n values (n % 256 == 0): h = x (+ res), one f32 add;
+ *        ss: lane l = 0..255 accumulates fmaf(h_i, h_i, acc) over
+ *        i = l, l+256, l+512, ... in that order, then a pairwise tree over
+ *        the 256 lane sums (a[l] += a[l+h] for h = 128, 64, ..., 1);
+ *        r = 1 / sqrtf(ss / n + eps); y = (h * r) * g; q8_1 of y.
+ *      SwiGLU: y = (t / (1 + e(-t))) * u for gate t and up u; q8_1 of y.
+ *      e(a): +inf for a > 100, +0 for a < -110 (NaN passes through);
+ *        k = rintf(a * log2(e)); r = fmaf(-k, C1, a), r = fmaf(-k, C2, r)
+ *        with C1 = 0.693359375
+ *        (9 bits) and C2 = ln 2 - C1 rounded to f32 (Cody and Waite's
+ *        argument reduction); p = the degree-7 Taylor polynomial of exp at 0
+ *        (coefficients 1/j! rounded to f32) by Horner's rule with fmaf;
+ *        e = ldexpf(p, k).
+ *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC.
  */
 #include <math.h>
@@ -388,4 +409,81 @@ void kqo_f32_to_f16_array(const float* in, uint16_t* out, int64_t n) {
 
 void kqo_f16_to_f32_array(const uint16_t* in, float* out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = h2f(in[i]);
+}
+
+/* --------------------------------------------------------- producers ---- */
+
+/* e(a): Cody-Waite reduction by ln 2 and the degree-7 Taylor polynomial. */
+static float exp_f32(float a) {
+    if (a > 100.0f) return INFINITY;
+    if (a < -110.0f) return 0.0f;
+    float k = rintf(a * 1.44269504088896341f);
+    float r = fmaf(-k, 0.693359375f, a);
+    r = fmaf(-k, -2.12194440054690583e-4f, r);
+    float p = 1.0f / 5040.0f;
+    p = fmaf(p, r, 1.0f / 720.0f);
+    p = fmaf(p, r, 1.0f / 120.0f);
+    p = fmaf(p, r, 1.0f / 24.0f);
+    p = fmaf(p, r, 1.0f / 6.0f);
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    return ldexpf(p, (int)k);
+}
+
+static float silu_f32(float t) { return t / (1.0f + exp_f32(-t)); }
+
+void kqo_exp_array(const float* in, float* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = exp_f32(in[i]);
+}
+
+void kqo_silu_array(const float* in, float* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = silu_f32(in[i]);
+}
+
+/* Sum of squares of one row in the stated order (n % 256 == 0). */
+static float rms_sumsq(const float* h, int64_t n) {
+    float a[256];
+    for (int l = 0; l < 256; ++l) {
+        float acc = 0.0f;
+        for (int64_t i = l; i < n; i += 256) acc = fmaf(h[i], h[i], acc);
+        a[l] = acc;
+    }
+    for (int hh = 128; hh >= 1; hh >>= 1)
+        for (int l = 0; l < hh; ++l) a[l] = a[l] + a[l + hh];
+    return a[0];
+}
+
+float kqo_rms_sumsq(const float* h, int64_t n) { return rms_sumsq(h, n); }
+
+/* x, res (may be NULL), g: f32; y: f32 [rows][n]; xq (may be NULL): q8_1 of y. */
+void kqo_rmsnorm_q8_1(const float* x, const float* res, const float* g, float eps, float* y,
+                      uint8_t* xq, int64_t rows, int64_t n) {
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < rows; ++row) {
+        float* h = (float*)malloc((size_t)n * sizeof(float));
+        for (int64_t i = 0; i < n; ++i)
+            h[i] = res ? x[row * n + i] + res[row * n + i] : x[row * n + i];
+        float ss = rms_sumsq(h, n);
+        float r = 1.0f / sqrtf(ss / (float)n + eps);
+        float* yr = y + row * n;
+        for (int64_t i = 0; i < n; ++i) yr[i] = (h[i] * r) * g[i];
+        if (xq)
+            for (int64_t b = 0; b < n / 32; ++b)
+                quantize_block(yr + b * 32, xq + (row * (n / 32) + b) * 36);
+        free(h);
+    }
+}
+
+/* gate, up: f32 [rows][n]; y: f32; xq (may be NULL): q8_1 of y. */
+void kqo_swiglu_q8_1(const float* gate, const float* up, float* y, uint8_t* xq, int64_t rows,
+                     int64_t n) {
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < rows; ++row) {
+        float* yr = y + row * n;
+        for (int64_t i = 0; i < n; ++i) yr[i] = silu_f32(gate[row * n + i]) * up[row * n + i];
+        if (xq)
+            for (int64_t b = 0; b < n / 32; ++b)
+                quantize_block(yr + b * 32, xq + (row * (n / 32) + b) * 36);
+    }
 }

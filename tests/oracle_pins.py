@@ -447,3 +447,142 @@ PINS = [
     pin_q6k_scale_negation,
     pin_structure,
 ]
+
+
+# ------------------------------------------------------------- producers ----
+# leone-cuda "CUDA kernel design": RMSNorm and SwiGLU write their q8_1 blocks
+# themselves.  The reduction order and the exponential are this oracle's
+# readings (see the oracle's header); the pins below fix them to hand-worked
+# values, closed forms and the f64 definitions.
+
+def _q8_block_fields(xq_row, b):
+    blk = xq_row[36 * b: 36 * (b + 1)]
+    d_bits = int(blk[0]) | (int(blk[1]) << 8)
+    s_bits = int(blk[2]) | (int(blk[3]) << 8)
+    return d_bits, s_bits, blk[4:].view(np.int8)
+
+
+def pin_e8_rms_reduction_order(O):
+    g = load_golden("e8_rms_reduction_order.txt")
+    h = np.zeros(g["n"], dtype=np.float32)
+    for i, v in zip(g["nonzero_index"], g["nonzero_value"]):
+        h[i] = v
+    assert O.rms_sumsq(h) == g["sumsq"]
+
+
+def pin_e9_rmsnorm_constant_row(O):
+    g = load_golden("e9_rmsnorm_constant_row.txt")
+    n = g["n"]
+    x = np.full((1, n), g["x_fill"], dtype=np.float32)
+    y, xq = O.rmsnorm_q8_1(x, np.full(n, g["g_fill"], dtype=np.float32), g["eps"])
+    assert np.all(y == g["y"])
+    for b in range(n // 32):
+        d_bits, s_bits, codes = _q8_block_fields(xq[0], b)
+        assert d_bits == g["d_bits"] and s_bits == g["s_bits"]
+        assert np.all(codes == g["code"])
+
+
+def pin_e10_swiglu_saturated(O):
+    g = load_golden("e10_swiglu_saturated.txt")
+    gate = np.full((1, 64), g["gate"], dtype=np.float32)
+    gate[0, 32:] = 0.0
+    up = np.full((1, 64), g["up"], dtype=np.float32)
+    y, xq = O.swiglu_q8_1(gate, up)
+    assert np.all(y[0, :32] == g["y"]) and np.all(y[0, 32:] == 0.0)
+    d_bits, s_bits, codes = _q8_block_fields(xq[0], 0)
+    assert d_bits == g["d_bits"] and s_bits == g["s_bits"] and np.all(codes == g["code"])
+    d_bits, s_bits, codes = _q8_block_fields(xq[0], 1)
+    assert d_bits == 0 and s_bits == 0 and np.all(codes == 0)
+
+
+def pin_exp_vs_f64(O):
+    """e(a) within one ulp of exp over the whole normal range; exact at 0;
+    +inf above the range, +0 below, NaN through."""
+    a = np.concatenate([np.linspace(-87.0, 88.5, 400001), np.linspace(-1.0, 1.0, 20001)]).astype(np.float32)
+    got = O.exp_f32(a).astype(np.float64)
+    ref = np.exp(a.astype(np.float64))
+    ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
+    assert np.max(np.abs(got - ref) / ulp) <= 1.0
+    assert O.exp_f32([0.0])[0] == 1.0
+    sp = O.exp_f32([150.0, 100.5, -200.0, -110.5, np.nan])
+    assert sp[0] == np.inf and sp[1] == np.inf and sp[2] == 0.0 and sp[3] == 0.0 and np.isnan(sp[4])
+
+
+def pin_silu_vs_f64(O):
+    """silu(t) = t / (1 + exp(-t)) within a few ulp; silu(0) = 0; silu(t) = t
+    once exp(-t) is below half an ulp of 1; odd-part identity."""
+    t = np.linspace(-80.0, 80.0, 160001).astype(np.float32)
+    got = O.silu_f32(t).astype(np.float64)
+    td = t.astype(np.float64)
+    ref = td / (1.0 + np.exp(-td))
+    nz = np.abs(ref) > 1e-30
+    assert np.max(np.abs(got - ref)[nz] / np.abs(ref[nz])) < 4.0 * 2.0 ** -24
+    assert O.silu_f32([0.0])[0] == 0.0
+    big = np.array([17.0, 20.0, 33.5, 1e6], dtype=np.float32)
+    assert np.array_equal(O.silu_f32(big), big)
+    u = np.linspace(0.01, 30.0, 3001).astype(np.float32)
+    diff = O.silu_f32(u).astype(np.float64) - O.silu_f32(-u).astype(np.float64)
+    assert np.max(np.abs(diff - u) / u) < 4.0 * 2.0 ** -24
+
+
+def _rmsnorm_f64(x, g, eps, res=None):
+    h = x.astype(np.float64) + (0.0 if res is None else res.astype(np.float64))
+    r = 1.0 / np.sqrt(np.mean(h * h, axis=1, keepdims=True) + eps)
+    return h * r * g.astype(np.float64)
+
+
+def pin_rmsnorm_vs_f64(O):
+    """RMSNorm against its f64 definition (also with eps dominating and with a
+    residual), within the rounding of an n-term sum of squares and four f32
+    operations."""
+    for n, scale, eps in [(256, 1.0, 1e-5), (256, 1e-3, 1e-5), (4096, 1.0, 1e-6), (512, 30.0, 0.0)]:
+        x = activations(81, n, 3, n) * np.float32(scale)
+        res = activations(82, n, 3, n) * np.float32(scale)
+        g = (1.0 + 0.1 * activations(83, n, 1, n)[0]).astype(np.float32)
+        for r in (None, res):
+            y, _ = O.rmsnorm_q8_1(x, g, eps, residual=r)
+            ref = _rmsnorm_f64(x, g, eps, r)
+            bound = (n / 2 + 6) * 2.0 ** -24 * np.abs(ref) + 1e-37
+            assert np.all(np.abs(y - ref) <= bound), (n, scale, eps)
+
+
+def pin_rmsnorm_structure(O):
+    """The residual form equals RMSNorm of the f32 sum; eps = 0 RMSNorm is
+    invariant under power-of-two scaling; the q8_1 output is the quantiser
+    applied to y."""
+    n = 1024
+    x = activations(84, 0, 2, n)
+    res = activations(84, 1, 2, n)
+    g = (1.0 + 0.1 * activations(84, 2, 1, n)[0]).astype(np.float32)
+    y1, q1 = O.rmsnorm_q8_1(x, g, 1e-6, residual=res)
+    y2, q2 = O.rmsnorm_q8_1((x + res).astype(np.float32), g, 1e-6)
+    assert np.array_equal(y1, y2) and np.array_equal(q1, q2)
+    y3, _ = O.rmsnorm_q8_1(x, g, 0.0)
+    y4, _ = O.rmsnorm_q8_1(x * np.float32(2.0 ** -7), g, 0.0)
+    assert np.array_equal(y3, y4)
+    assert np.array_equal(q1, O.quantize_q8_1(y1))
+
+
+def pin_swiglu_structure(O):
+    """SwiGLU is silu(gate) * up elementwise, its q8_1 the quantiser of y, and
+    it agrees with the f64 definition."""
+    gate = activations(85, 0, 2, 512) * np.float32(4.0)
+    up = activations(85, 1, 2, 512)
+    y, xq = O.swiglu_q8_1(gate, up)
+    assert np.array_equal(y, (O.silu_f32(gate).reshape(gate.shape) * up).astype(np.float32))
+    assert np.array_equal(xq, O.quantize_q8_1(y))
+    gd = gate.astype(np.float64)
+    ref = gd / (1.0 + np.exp(-gd)) * up.astype(np.float64)
+    assert np.all(np.abs(y - ref) <= 6.0 * 2.0 ** -24 * np.abs(ref) + 1e-37)
+
+
+PINS += [
+    pin_e8_rms_reduction_order,
+    pin_e9_rmsnorm_constant_row,
+    pin_e10_swiglu_saturated,
+    pin_exp_vs_f64,
+    pin_silu_vs_f64,
+    pin_rmsnorm_vs_f64,
+    pin_rmsnorm_structure,
+    pin_swiglu_structure,
+]

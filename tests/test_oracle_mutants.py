@@ -53,6 +53,25 @@ MUTANTS = [
     ("last block dropped", "for (int64_t j = 0; j < k / 32; ++j) {", "for (int64_t j = 0; j < k / 32 - 1; ++j) {"),
     ("products in f32", "double p = (double)wr[32 * j + i] * (double)xr[32 * j + i];",
      "double p = (double)(wr[32 * j + i] * xr[32 * j + i]);"),
+    ("rms sum in natural order", "        a[l] = acc;",
+     "        a[l] = l ? 0.0f : ({float t = 0.0f; for (int64_t i = 0; i < n; ++i) t = fmaf(h[i], h[i], t); t;});"),
+    ("rms reciprocal dropped", "float r = 1.0f / sqrtf(ss / (float)n + eps);",
+     "float r = sqrtf(ss / (float)n + eps);"),
+    ("rms eps outside the root", "float r = 1.0f / sqrtf(ss / (float)n + eps);",
+     "float r = 1.0f / (sqrtf(ss / (float)n) + eps);"),
+    ("rms mean over n-1", "float r = 1.0f / sqrtf(ss / (float)n + eps);",
+     "float r = 1.0f / sqrtf(ss / (float)(n - 1) + eps);"),
+    ("rms residual dropped", "h[i] = res ? x[row * n + i] + res[row * n + i] : x[row * n + i];",
+     "h[i] = x[row * n + i];"),
+    ("rms gain dropped", "for (int64_t i = 0; i < n; ++i) yr[i] = (h[i] * r) * g[i];",
+     "for (int64_t i = 0; i < n; ++i) yr[i] = h[i] * r;"),
+    ("silu sign", "static float silu_f32(float t) { return t / (1.0f + exp_f32(-t)); }",
+     "static float silu_f32(float t) { return t / (1.0f + exp_f32(t)); }"),
+    ("exp degree 5", "    p = fmaf(p, r, 1.0f / 720.0f);", "    p = 0.0f;"),
+    ("exp second reduction constant dropped", "    r = fmaf(-k, -2.12194440054690583e-4f, r);", "    (void)0;"),
+    ("exp saturation at the wrong end", "    if (a < -110.0f) return 0.0f;", "    if (a < -110.0f) return INFINITY;"),
+    ("swiglu up dropped", "yr[i] = silu_f32(gate[row * n + i]) * up[row * n + i];",
+     "yr[i] = silu_f32(gate[row * n + i]);"),
 ]
 
 
