@@ -15,9 +15,10 @@ weights from HBM.  Inputs are resident in HBM before the timed region.
 
 The other workloads are measured the same way and reported under
 ``secondary``: batch-4 decode (fused QKV 6144x4096 and down 4096x14336 with
-residual), the Q6_K output head 128256x4096 (batch 1 and 4), and the
+residual), the Q6_K output head 128256x4096 (batch 1 and 4), the
 Qwen2-7B prefill MMQ at 2048 tokens (gate/up 18944x3584, down 3584x18944,
-QKV 4608x3584).
+QKV 4608x3584), and the fused producers RMSNorm -> q8_1 and SwiGLU -> q8_1
+at decode and prefill sizes next to a standalone quantisation.
 
 ``roofline`` describes the dominant kernel of the step, kq_gemv_q4k: its
 algorithmic bytes per launch (weights + q8_1 activation + f32 output) over
@@ -218,6 +219,76 @@ def kernel_durations(wl: Workload, target_ms: float = 20.0):
         out.append((label, kind, a.elapsed_time(b) / (reps * wl.ncopies)))
         del g
     return out
+
+
+def _graph_time_ms(fn, target_ms: float = 20.0, per_graph: int = 8):
+    """Average duration (ms) of fn(): a HIP graph holds per_graph launches back
+    to back; it is replayed between two events on the launching stream."""
+    import torch
+
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(per_graph):
+            fn()
+    stream = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    reps = max(3, min(500, int(target_ms / max(a.elapsed_time(b), 1e-3))))
+    a.record(stream)
+    for _ in range(reps):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (reps * per_graph)
+
+
+def measure_producers(cfg: int):
+    """Fused producers (RMSNorm -> q8_1, SwiGLU -> q8_1) of workload cfg, each
+    timed alone, with the f32 output written and with q8_1 only, next to the
+    standalone quantisation of an activation of the same size.  Inputs stay
+    in the caches between back-to-back launches (they are small next to the
+    weight streams)."""
+    import torch
+
+    import q6_q8_matmul_amd as kq
+    from kq_inputs import WORKLOADS, tensor
+
+    wl = WORKLOADS[cfg]
+    t = {name: torch.from_numpy(tensor(cfg, name)).cuda() for name, *_r in wl["tensors"]}
+    out = []
+    for op in wl["ops"]:
+        rows, n = op["rows"], op["n"]
+        xq = torch.empty((rows, n // 32 * 36), dtype=torch.uint8, device="cuda")
+        xq2 = torch.empty_like(xq)
+        y = torch.empty((rows, n), dtype=torch.float32, device="cuda")
+        if op["op"] == "rmsnorm_q8_1":
+            x, res, g = t[op["x"]], t[op["res"]], t[op["g"]]
+            fused = lambda yy: kq.kq_rmsnorm_q8_1(x, res, g, op["eps"], yy, xq, rows, n)
+            read = 2 * rows * n * 4 + n * 4
+        else:
+            gate, up = t[op["gate"]], t[op["up"]]
+            fused = lambda yy: kq.kq_swiglu_q8_1(gate, up, yy, xq, rows, n)
+            read = 2 * rows * n * 4
+        fused(y)
+        torch.cuda.synchronize()
+        ms_y = _graph_time_ms(lambda: fused(y))
+        ms_q = _graph_time_ms(lambda: fused(None))
+        ms_quant = _graph_time_ms(lambda: kq.kq_quantize_q8_1(y, xq2, rows, n))
+        qbytes = rows * n // 32 * 36
+        out.append({"op": op["label"], "kernel": "kq_" + op["op"], "shape": [rows, n],
+                    "avg_us": round(ms_y * 1e3, 2),
+                    "GBps": round((read + rows * n * 4 + qbytes) / (ms_y * 1e-3) / 1e9, 1),
+                    "avg_us_q8_1_only": round(ms_q * 1e3, 2),
+                    "standalone_quantize_avg_us": round(ms_quant * 1e3, 2)})
+    return {"workload": wl["name"], "kernels": out,
+            "note": "inputs cache-resident between back-to-back launches"}
 
 
 def measure(cfg: int, steps: int, warmup: int, use_graph: bool):
@@ -480,9 +551,14 @@ def main(argv=None):
 
     secondary = {}
     main_cfg = 1
-    cfgs = [args.only] if args.only is not None else ([1] if args.no_secondary else [1, 2, 3, 4])
+    cfgs = [args.only] if args.only is not None else ([1] if args.no_secondary else [1, 2, 3, 4, 5, 6])
     result = None
     for cfg in cfgs:
+        if cfg in (5, 6):
+            log(f"workload {cfg}: fused producers")
+            secondary[f"cfg{cfg}"] = measure_producers(cfg)
+            torch.cuda.empty_cache()
+            continue
         steps = args.steps if cfg != 4 else max(3, args.steps // 20)
         warm = args.warmup if cfg != 4 else max(1, args.warmup // 10)
         log(f"workload {cfg}: {steps} steps, {warm} warm-up, graphs={use_graph}")

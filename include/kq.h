@@ -15,6 +15,10 @@
  *     epilogue; cajeta "One model, start to last token" 4.1 and 4.2).
  *   - kq_mmq_q4k: the prefill matrix-matrix product over many tokens on the
  *     int8 matrix cores (minfer "The CUDA backend" 2.3, MMQ, and 3.2.6).
+ *   - kq_rmsnorm_q8_1 / kq_swiglu_q8_1: producers that write the q8_1 blocks
+ *     of their output themselves, so the GEMV that follows needs no separate
+ *     quantisation launch (leone-cuda "CUDA kernel design": RMSNorm and
+ *     SwiGLU write their q8_1 blocks; minfer "The CUDA backend" 2.2).
  *
  * Formats (little-endian; the pages give the sizes and field lists, the bit
  * positions are the public GGUF k-quant layout):
@@ -80,8 +84,9 @@ typedef enum {
  * id = 1/d (0 if d == 0); code = roundf(x*id) (half away from zero);
  * s = f32 pairwise-tree sum of the 32 source values (a[i] += a[i+h] for
  * h = 16, 8, 4, 2, 1); d and s stored as f16 rounded to nearest-even.
- * The result is bit-exact.  NaN/Inf inputs and blocks whose 1/d overflows
- * (amax < 127*2^-128) are outside the contract.
+ * The result is bit-exact.  In a block whose 1/d overflows (amax below
+ * 127*2^-128, where f16(d) is 0 anyway) nonzero values get +-127 and zeros
+ * get 0 (x*id is NaN there).  NaN/Inf inputs are outside the contract.
  * xq must not overlap x.
  */
 int kq_quantize_q8_1(const float* x, void* xq, int64_t rows, int64_t k, void* stream);
@@ -127,6 +132,48 @@ int kq_gemv_q6k(const void* w, const void* xq, float* y, const float* residual,
  */
 int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
                void* stream);
+
+/*
+ * RMSNorm of each row (optionally of x + res), times the gain g, written as
+ * q8_1 blocks and optionally as f32 (leone-cuda "CUDA kernel design": RMSNorm
+ * with a fixed reduction order and sqrtf, writing its q8_1 blocks; the
+ * residual form normalises left + right).
+ *   x    f32 [rows][n], 16-byte aligned.
+ *   res  NULL or f32 [rows][n], 16-byte aligned: h = x + res (one f32 add).
+ *   g    f32 [n] gain, 16-byte aligned.
+ *   eps  added to the mean square (eps > 0 keeps an all-zero row finite).
+ *   y    NULL (only q8_1 is written) or out: f32 [rows][n], 16-byte aligned.
+ *   xq   out: [rows][n/32] q8_1 blocks, 4-byte aligned.
+ *   rows >= 0, n > 0, n % 256 == 0, n <= KQ_MAX_K, rows*n/256 < 2^31.
+ * Per row: ss = sum of h*h in this order: lane l = 0..255 accumulates
+ * fmaf(h_i, h_i, acc) over i = l, l+256, ...; then a pairwise tree over the
+ * 256 lane sums (a[l] += a[l+h], h = 128 ... 1); r = 1 / sqrtf(ss/n + eps);
+ * y = (h*r)*g; xq = the q8_1 blocks of y exactly as kq_quantize_q8_1 makes
+ * them.  Every step is one IEEE f32 operation, so the outputs are fixed bit
+ * for bit.  y and xq must not overlap x, res, g or each other (every
+ * workgroup of a row reads the whole row).
+ */
+int kq_rmsnorm_q8_1(const float* x, const float* res, const float* g, float eps, float* y,
+                    void* xq, int64_t rows, int64_t n, void* stream);
+
+/*
+ * SwiGLU y = silu(gate) * up, written as q8_1 blocks and optionally as f32
+ * (leone-cuda "CUDA kernel design": SwiGLU writes its dense output and its
+ * q8_1 blocks in one elementwise kernel).
+ *   gate, up  f32 [rows][n], 16-byte aligned.
+ *   y    NULL or out: f32 [rows][n], 16-byte aligned.
+ *   xq   out: [rows][n/32] q8_1 blocks, 4-byte aligned.
+ *   rows >= 0, n > 0, n % 256 == 0, n <= KQ_MAX_K, rows*n/256 < 2^31.
+ * silu(t) = t / (1 + e(-t)) with e(a): +inf for a > 100, +0 for a < -110,
+ * else k = rint(a * log2 e), r = fma(-k, 0.693359375, a),
+ * r = fma(-k, C2, r) with C2 = ln 2 - 0.693359375 rounded to f32 (Cody and
+ * Waite's reduction), p = the degree-7 Taylor polynomial of exp at 0 in
+ * Horner form with fused multiply-adds (coefficients 1/j! rounded to f32),
+ * e = ldexp(p, k).  Every step is one IEEE f32 operation, so the outputs are
+ * fixed bit for bit.  y and xq must not overlap the inputs or each other.
+ */
+int kq_swiglu_q8_1(const float* gate, const float* up, float* y, void* xq, int64_t rows,
+                   int64_t n, void* stream);
 
 /* Text of the last error on this host thread ("" if none). */
 const char* kq_last_error(void);

@@ -18,7 +18,7 @@ Formats (byte layouts of one block, little-endian):
 Value distributions of the workloads: 4-bit codes uniform in 0..15, six-bit
 scales and mins uniform in 0..63, ``d``/``dmin`` = f16(|N(0,1)| * 2^-8),
 Q6_K ``ql``/``qh`` uniform bytes, Q6_K scales uniform in -32..31,
-activations and residuals N(0,1) in f32.
+activations and residuals N(0,1) in f32, normalisation gains 1 + 0.1 N(0,1).
 
 Uniform random bytes realise the Q4_K code and scale distributions exactly:
 every bit of the 128 code bytes belongs to exactly one 4-bit code, and every
@@ -82,6 +82,12 @@ def activations(seed: int, tensor_id: int, rows: int, k: int) -> np.ndarray:
 def residual(seed: int, tensor_id: int, rows: int, m: int) -> np.ndarray:
     """f32 N(0,1) residual stream, ``float32[rows, m]``."""
     return _rng(seed, tensor_id).standard_normal((rows, m), dtype=np.float32)
+
+
+def gain(seed: int, tensor_id: int, rows: int, n: int) -> np.ndarray:
+    """f32 normalisation gain 1 + 0.1*N(0,1), ``float32[rows, n]`` (rows = 1)."""
+    v = 1.0 + 0.1 * _rng(seed, tensor_id).standard_normal((rows, n))
+    return v.astype(np.float32)
 
 
 # --------------------------------------------------------------------------
@@ -165,6 +171,36 @@ WORKLOADS = {
             dict(op="mmq_q4k", label="qkv", w="qkv", x="x_in", m=4608, k=3584, n=2048),
         ],
     ),
+    # producers that emit q8_1 directly (RMSNorm of x + residual; SwiGLU),
+    # decode sizes of Llama-3-8B and prefill sizes of Qwen2-7B at 2048 tokens
+    5: dict(
+        name="llama3_8b_decode_producers_q8_1",
+        tensors=[
+            ("x", "act", 1, 4096),
+            ("res", "res", 1, 4096),
+            ("g", "gain", 1, 4096),
+            ("gate", "act", 1, 14336),
+            ("up", "act", 1, 14336),
+        ],
+        ops=[
+            dict(op="rmsnorm_q8_1", label="attn_norm", x="x", res="res", g="g", eps=1e-5, rows=1, n=4096),
+            dict(op="swiglu_q8_1", label="ffn_swiglu", gate="gate", up="up", rows=1, n=14336),
+        ],
+    ),
+    6: dict(
+        name="qwen2_7b_prefill_producers_q8_1_n2048",
+        tensors=[
+            ("x", "act", 2048, 3584),
+            ("res", "res", 2048, 3584),
+            ("g", "gain", 1, 3584),
+            ("gate", "act", 2048, 18944),
+            ("up", "act", 2048, 18944),
+        ],
+        ops=[
+            dict(op="rmsnorm_q8_1", label="attn_norm", x="x", res="res", g="g", eps=1e-6, rows=2048, n=3584),
+            dict(op="swiglu_q8_1", label="ffn_swiglu", gate="gate", up="up", rows=2048, n=18944),
+        ],
+    ),
 }
 
 
@@ -182,6 +218,8 @@ def tensor(cfg: int, name: str) -> np.ndarray:
             return activations(cfg, tid, a, b)
         if kind == "res":
             return residual(cfg, tid, a, b)
+        if kind == "gain":
+            return gain(cfg, tid, a, b)
         raise ValueError(kind)
     raise KeyError(f"workload {cfg} has no tensor {name!r}")
 

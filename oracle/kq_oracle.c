@@ -13,7 +13,9 @@
  *    codes, an f16 scale and an f16 source sum).  The pages fix the fields
  *    but not the arithmetic, which is taken here as: amax = max|x|;
  *    d = amax / 127 (f32, IEEE division); id = 1/d (0 when d == 0);
- *    q = roundf(x * id) clamped to [-127, 127] (round half away from zero);
+ *    q = roundf(x * id) clamped to [-127, 127] (round half away from zero),
+ *    and q = 0 where x * id is NaN (x = 0 in a block whose d is so small,
+ *    below 2^-128, that 1/d overflows; such a block's f16 d is 0);
  *    s = the f32 sum of the 32 source values taken as a pairwise tree
  *    (a[i] += a[i+h] for h = 16, 8, 4, 2, 1); f16(d) and f16(s) rounded to
  *    nearest-even.  Every f32 operation is a single IEEE operation.
@@ -126,6 +128,7 @@ static void quantize_block(const float* x, uint8_t* out) {
     float id = (d != 0.0f) ? 1.0f / d : 0.0f;
     for (int i = 0; i < 32; ++i) {
         float v = roundf(x[i] * id);
+        if (v != v) v = 0.0f; /* 0 * inf when 1/d overflows (d < 2^-128) */
         if (v > 127.0f) v = 127.0f;
         if (v < -127.0f) v = -127.0f;
         out[4 + i] = (uint8_t)(int8_t)v;

@@ -49,7 +49,10 @@ def lib() -> ctypes.CDLL:
         L.kq_gemv_q4k.argtypes = [p, p, p, p, i64, i64, i32, p]
         L.kq_gemv_q6k.argtypes = [p, p, p, p, i64, i64, i32, p]
         L.kq_mmq_q4k.argtypes = [p, p, p, i64, i64, i64, p]
-        for fn in (L.kq_quantize_q8_1, L.kq_gemv_q4k, L.kq_gemv_q6k, L.kq_mmq_q4k):
+        L.kq_rmsnorm_q8_1.argtypes = [p, p, p, ctypes.c_float, p, p, i64, i64, p]
+        L.kq_swiglu_q8_1.argtypes = [p, p, p, p, i64, i64, p]
+        for fn in (L.kq_quantize_q8_1, L.kq_gemv_q4k, L.kq_gemv_q6k, L.kq_mmq_q4k,
+                   L.kq_rmsnorm_q8_1, L.kq_swiglu_q8_1):
             fn.restype = ctypes.c_int
         L.kq_last_error.argtypes = []
         L.kq_last_error.restype = ctypes.c_char_p
@@ -111,6 +114,16 @@ def kq_mmq_q4k(w, xq, y, m: int, n: int, k: int, stream=None) -> None:
     _check(lib().kq_mmq_q4k(_ptr(w), _ptr(xq), _ptr(y), m, n, k, _stream(stream)))
 
 
+def kq_rmsnorm_q8_1(x, res, g, eps: float, y, xq, rows: int, n: int, stream=None) -> None:
+    _check(lib().kq_rmsnorm_q8_1(_ptr(x), _ptr(res), _ptr(g), ctypes.c_float(eps), _ptr(y),
+                                 _ptr(xq), rows, n, _stream(stream)))
+
+
+def kq_swiglu_q8_1(gate, up, y, xq, rows: int, n: int, stream=None) -> None:
+    _check(lib().kq_swiglu_q8_1(_ptr(gate), _ptr(up), _ptr(y), _ptr(xq), rows, n,
+                                _stream(stream)))
+
+
 # ------------------------------------------- allocating conveniences -------
 # These allocate the output with torch and call the entry point above.
 
@@ -158,3 +171,27 @@ def mmq_q4k(w, xq, m: int, n: int, k: int, out=None, stream=None):
     y = out if out is not None else torch.empty((n, m), dtype=torch.float32, device=w.device)
     kq_mmq_q4k(w, xq, y, m, n, k, stream)
     return y
+
+
+def rmsnorm_q8_1(x, g, eps: float, residual=None, want_y: bool = True, stream=None):
+    """RMSNorm(x [+ residual]) * g -> (y f32 [rows, n] or None, q8_1 uint8)."""
+    import torch
+
+    _require_cuda(x, g, residual)
+    rows, n = x.shape
+    xq = torch.empty((rows, (n // 32) * Q81_BYTES), dtype=torch.uint8, device=x.device)
+    y = torch.empty((rows, n), dtype=torch.float32, device=x.device) if want_y else None
+    kq_rmsnorm_q8_1(x, residual, g, eps, y, xq, rows, n, stream)
+    return y, xq
+
+
+def swiglu_q8_1(gate, up, want_y: bool = True, stream=None):
+    """silu(gate) * up -> (y f32 [rows, n] or None, q8_1 uint8)."""
+    import torch
+
+    _require_cuda(gate, up)
+    rows, n = gate.shape
+    xq = torch.empty((rows, (n // 32) * Q81_BYTES), dtype=torch.uint8, device=gate.device)
+    y = torch.empty((rows, n), dtype=torch.float32, device=gate.device) if want_y else None
+    kq_swiglu_q8_1(gate, up, y, xq, rows, n, stream)
+    return y, xq

@@ -178,6 +178,66 @@ int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, in
     return launched(fn, kq::launch_mmq_q4k(w, xq, y, m, n, k, (hipStream_t)stream));
 }
 
+static int producer_sizes(const char* fn, int64_t rows, int64_t n) {
+    if (n <= 0 || n % 256 != 0 || n > KQ_MAX_K)
+        return fail(KQ_ERR_ARG, "%s: n=%lld must be a positive multiple of 256 and <= %d", fn,
+                    (long long)n, KQ_MAX_K);
+    if (rows < 0 || rows > KQ_MAX_ROWS)
+        return fail(KQ_ERR_ARG, "%s: rows=%lld out of range [0, %d]", fn, (long long)rows,
+                    KQ_MAX_ROWS);
+    if (rows * (n / 256) >= 0x7fffffffLL)
+        return fail(KQ_ERR_ARG, "%s: rows*n=%lld too large for one launch", fn,
+                    (long long)(rows * n));
+    return KQ_OK;
+}
+
+int kq_rmsnorm_q8_1(const float* x, const float* res, const float* g, float eps, float* y,
+                    void* xq, int64_t rows, int64_t n, void* stream) {
+    const char* fn = "kq_rmsnorm_q8_1";
+    if (!x || !g || !xq)
+        return fail(KQ_ERR_ARG, "%s: null pointer (x=%p g=%p xq=%p)", fn, (const void*)x,
+                    (const void*)g, xq);
+    if (int rc = producer_sizes(fn, rows, n)) return rc;
+    if (!aligned(x, 16) || !aligned(g, 16) || (res && !aligned(res, 16)) || (y && !aligned(y, 16)) ||
+        !aligned(xq, 4))
+        return fail(KQ_ERR_ARG,
+                    "%s: misaligned pointer (x=%p res=%p g=%p y=%p need 16, xq=%p needs 4)", fn,
+                    (const void*)x, (const void*)res, (const void*)g, (void*)y, xq);
+    const int64_t fb = rows * n * 4, qb = rows * (n / 32) * 36;
+    const bool bad = overlap(xq, qb, x, fb) || overlap(xq, qb, g, n * 4) ||
+                     (res && overlap(xq, qb, res, fb)) ||
+                     (y && (overlap(y, fb, x, fb) || overlap(y, fb, g, n * 4) ||
+                            (res && overlap(y, fb, res, fb)) || overlap(y, fb, xq, qb)));
+    if (bad)
+        return fail(KQ_ERR_ARG, "%s: an output (y=%p, xq=%p) overlaps an input or the other output",
+                    fn, (void*)y, xq);
+    if (rows == 0) return ok();
+    if (int rc = check_device(fn, nullptr)) return rc;
+    return launched(fn, kq::launch_rmsnorm_q8_1(x, res, g, eps, y, xq, rows, n, (hipStream_t)stream));
+}
+
+int kq_swiglu_q8_1(const float* gate, const float* up, float* y, void* xq, int64_t rows,
+                   int64_t n, void* stream) {
+    const char* fn = "kq_swiglu_q8_1";
+    if (!gate || !up || !xq)
+        return fail(KQ_ERR_ARG, "%s: null pointer (gate=%p up=%p xq=%p)", fn, (const void*)gate,
+                    (const void*)up, xq);
+    if (int rc = producer_sizes(fn, rows, n)) return rc;
+    if (!aligned(gate, 16) || !aligned(up, 16) || (y && !aligned(y, 16)) || !aligned(xq, 4))
+        return fail(KQ_ERR_ARG, "%s: misaligned pointer (gate=%p up=%p y=%p need 16, xq=%p needs 4)",
+                    fn, (const void*)gate, (const void*)up, (void*)y, xq);
+    const int64_t fb = rows * n * 4, qb = rows * (n / 32) * 36;
+    const bool bad = overlap(xq, qb, gate, fb) || overlap(xq, qb, up, fb) ||
+                     (y && (overlap(y, fb, gate, fb) || overlap(y, fb, up, fb) ||
+                            overlap(y, fb, xq, qb)));
+    if (bad)
+        return fail(KQ_ERR_ARG, "%s: an output (y=%p, xq=%p) overlaps an input or the other output",
+                    fn, (void*)y, xq);
+    if (rows == 0) return ok();
+    if (int rc = check_device(fn, nullptr)) return rc;
+    return launched(fn, kq::launch_swiglu_q8_1(gate, up, y, xq, rows, n, (hipStream_t)stream));
+}
+
 const char* kq_last_error(void) { return g_err; }
 
 int kq_abi_version(void) { return 1; }

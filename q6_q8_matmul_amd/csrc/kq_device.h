@@ -42,6 +42,50 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// q8_1 quantisation of one 32-value block by eight consecutive lanes
+// (j = lane & 7 of an aligned group of 8, all active); lane j owns values
+// 4j .. 4j+3 in v and writes code dword j; lane 0 also writes the header
+// dword {f16 d, f16 s}.  amax -> d = amax/127 -> id = 1/d -> roundf(x*id)
+// clamped to +-127 (0 where x*id is NaN: a zero value in a block whose 1/d
+// overflows); the source sum is the pairwise tree a[i] += a[i+h]
+// (h = 16 ... 1), which the xor shuffles reproduce exactly because IEEE
+// addition is commutative (leone-cuda "CUDA kernel design": q8_1 blocks of
+// 32 signed codes, an f16 scale and an f16 source sum).
+__device__ __forceinline__ void quantize_block8(float4 v, int j, uint32_t* __restrict__ blk) {
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = fmaxf(a, __shfl_xor(a, 4, 8));
+    a = fmaxf(a, __shfl_xor(a, 2, 8));
+    a = fmaxf(a, __shfl_xor(a, 1, 8));
+
+    const float d = a / 127.0f;
+    const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+
+    auto code = [&](float t) -> uint32_t {
+        float q = roundf(t * id);
+        q = (q != q) ? 0.0f : q;   // 0 * inf when 1/d overflows (d < 2^-128)
+        q = fminf(fmaxf(q, -127.0f), 127.0f);
+        return (uint32_t)((int)q) & 0xffu;
+    };
+    const uint32_t packed = code(v.x) | (code(v.y) << 8) | (code(v.z) << 16) | (code(v.w) << 24);
+
+    // Source-sum tree.  Lane L holds a[4L..4L+3]; h = 16, 8, 4 pair lanes
+    // L and L^4, L^2, L^1; h = 2, 1 finish inside lane 0.
+    float4 o;
+    o.x = __shfl_xor(v.x, 4, 8); o.y = __shfl_xor(v.y, 4, 8);
+    o.z = __shfl_xor(v.z, 4, 8); o.w = __shfl_xor(v.w, 4, 8);
+    v.x = v.x + o.x; v.y = v.y + o.y; v.z = v.z + o.z; v.w = v.w + o.w;
+    o.x = __shfl_xor(v.x, 2, 8); o.y = __shfl_xor(v.y, 2, 8);
+    o.z = __shfl_xor(v.z, 2, 8); o.w = __shfl_xor(v.w, 2, 8);
+    v.x = v.x + o.x; v.y = v.y + o.y; v.z = v.z + o.z; v.w = v.w + o.w;
+    o.x = __shfl_xor(v.x, 1, 8); o.y = __shfl_xor(v.y, 1, 8);
+    o.z = __shfl_xor(v.z, 1, 8); o.w = __shfl_xor(v.w, 1, 8);
+    v.x = v.x + o.x; v.y = v.y + o.y; v.z = v.z + o.z; v.w = v.w + o.w;
+    const float s = (v.x + v.z) + (v.y + v.w);
+
+    blk[1 + j] = packed;
+    if (j == 0) blk[0] = float_to_half_bits(d) | (float_to_half_bits(s) << 16);
+}
+
 // Launchers (return the launch status).
 hipError_t launch_quantize_q8_1(const float* x, void* xq, int64_t rows, int64_t k,
                                 hipStream_t stream);
@@ -53,5 +97,9 @@ hipError_t launch_gemv_q6k(const void* w, const void* xq, float* y, const float*
                            hipStream_t stream);
 hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                           int64_t k, hipStream_t stream);
+hipError_t launch_rmsnorm_q8_1(const float* x, const float* res, const float* g, float eps,
+                               float* y, void* xq, int64_t rows, int64_t n, hipStream_t stream);
+hipError_t launch_swiglu_q8_1(const float* gate, const float* up, float* y, void* xq,
+                              int64_t rows, int64_t n, hipStream_t stream);
 
 }  // namespace kq

@@ -6,10 +6,8 @@
 //
 // Mapping: eight lanes per block, each lane owns four consecutive values
 // (one 16-byte load).  A wavefront therefore reads 1 KiB and writes 288
-// contiguous bytes (8 blocks).  The max and the source-sum tree run over the
-// eight lanes with xor shuffles; the tree adds a[i] + a[i+h] for
-// h = 16, 8, 4, 2, 1 exactly as its definition states, so the sum is the
-// same f32 value bit for bit (IEEE addition is commutative).
+// contiguous bytes (8 blocks).  The block routine (quantize_block8) runs the
+// max and the source-sum tree over the eight lanes with xor shuffles.
 #include "kq_device.h"
 
 namespace kq {
@@ -23,40 +21,7 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float4* __rest
     const int j = threadIdx.x & 7;
     if (blk >= nblocks) return;  // whole 8-lane groups leave together
 
-    float4 v = x[blk * 8 + j];
-
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    a = fmaxf(a, __shfl_xor(a, 4, 8));
-    a = fmaxf(a, __shfl_xor(a, 2, 8));
-    a = fmaxf(a, __shfl_xor(a, 1, 8));
-
-    const float d = a / 127.0f;
-    const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
-
-    auto code = [&](float t) -> uint32_t {
-        float q = roundf(t * id);
-        q = fminf(fmaxf(q, -127.0f), 127.0f);
-        return (uint32_t)((int)q) & 0xffu;
-    };
-    const uint32_t packed = code(v.x) | (code(v.y) << 8) | (code(v.z) << 16) | (code(v.w) << 24);
-
-    // Source-sum tree.  Lane L holds a[4L..4L+3]; h = 16, 8, 4 pair lanes
-    // L and L^4, L^2, L^1; h = 2, 1 finish inside lane 0.
-    float4 o;
-    o.x = __shfl_xor(v.x, 4, 8); o.y = __shfl_xor(v.y, 4, 8);
-    o.z = __shfl_xor(v.z, 4, 8); o.w = __shfl_xor(v.w, 4, 8);
-    v.x = v.x + o.x; v.y = v.y + o.y; v.z = v.z + o.z; v.w = v.w + o.w;
-    o.x = __shfl_xor(v.x, 2, 8); o.y = __shfl_xor(v.y, 2, 8);
-    o.z = __shfl_xor(v.z, 2, 8); o.w = __shfl_xor(v.w, 2, 8);
-    v.x = v.x + o.x; v.y = v.y + o.y; v.z = v.z + o.z; v.w = v.w + o.w;
-    o.x = __shfl_xor(v.x, 1, 8); o.y = __shfl_xor(v.y, 1, 8);
-    o.z = __shfl_xor(v.z, 1, 8); o.w = __shfl_xor(v.w, 1, 8);
-    v.x = v.x + o.x; v.y = v.y + o.y; v.z = v.z + o.z; v.w = v.w + o.w;
-    const float s = (v.x + v.z) + (v.y + v.w);
-
-    uint32_t* out = xq + blk * 9;
-    out[1 + j] = packed;
-    if (j == 0) out[0] = float_to_half_bits(d) | (float_to_half_bits(s) << 16);
+    quantize_block8(x[blk * 8 + j], j, xq + blk * 9);
 }
 
 }  // namespace

@@ -576,7 +576,18 @@ def pin_swiglu_structure(O):
     assert np.all(np.abs(y - ref) <= 6.0 * 2.0 ** -24 * np.abs(ref) + 1e-37)
 
 
+def pin_e11_q8_tiny_block(O):
+    g = load_golden("e11_q8_1_tiny_block.txt")
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0], x[0, 1] = g["x0"], g["x1"]
+    assert x[0, 0] == -(2.0 ** -122) and x[0, 1] == 2.0 ** -130
+    d_bits, s_bits, codes = _q8_block_fields(O.quantize_q8_1(x)[0], 0)
+    assert d_bits == g["d_bits"] and s_bits == g["s_bits"]
+    assert list(codes[:2]) == g["codes"] and np.all(codes[2:] == 0)
+
+
 PINS += [
+    pin_e11_q8_tiny_block,
     pin_e8_rms_reduction_order,
     pin_e9_rmsnorm_constant_row,
     pin_e10_swiglu_saturated,

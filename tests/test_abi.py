@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "kq_quantize_q8_1", "kq_gemv_q4k", "kq_gemv_q6k", "kq_mmq_q4k",
-        "kq_last_error", "kq_abi_version"])
+        "kq_rmsnorm_q8_1", "kq_swiglu_q8_1", "kq_last_error", "kq_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(kq):
@@ -142,3 +142,55 @@ def test_no_gpu_means_unsupported(kq):
     rc = kq.lib().kq_gemv_q4k(W, X, Y, None, 8, 256, 1, None)
     assert rc == kq.KQ_ERR_UNSUPPORTED
     assert "kq_gemv_q4k" in kq.kq_last_error()
+
+
+G = 0x100000
+Q = 0x200000
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((None, None, G, 1e-5, Y, Q, 1, 256, None), "null pointer"),
+    ((X, None, None, 1e-5, Y, Q, 1, 256, None), "null pointer"),
+    ((X, None, G, 1e-5, Y, None, 1, 256, None), "null pointer"),
+    ((X, None, G, 1e-5, Y, Q, 1, 288, None), "n=288"),
+    ((X, None, G, 1e-5, Y, Q, 1, 0, None), "n=0"),
+    ((X, None, G, 1e-5, Y, Q, -1, 256, None), "rows=-1"),
+    ((X + 4, None, G, 1e-5, Y, Q, 1, 256, None), "misaligned"),
+    ((X, R + 4, G, 1e-5, Y, Q, 1, 256, None), "misaligned"),
+    ((X, None, G, 1e-5, Y + 8, Q, 1, 256, None), "misaligned"),
+    ((X, None, G, 1e-5, Y, Q + 2, 1, 256, None), "misaligned"),
+    ((X, None, G, 1e-5, X, Q, 1, 256, None), "overlaps"),
+    ((X, R, G, 1e-5, R, Q, 1, 256, None), "overlaps"),
+    ((X, None, G, 1e-5, Y, X, 1, 256, None), "overlaps"),
+    ((X, None, G, 1e-5, Y, Y + 512, 1, 256, None), "overlaps"),
+])
+def test_rmsnorm_rejects(kq, args, needle):
+    rc = kq.lib().kq_rmsnorm_q8_1(*args)
+    assert rc == kq.KQ_ERR_ARG, kq.kq_last_error()
+    assert needle in kq.kq_last_error()
+    assert "kq_rmsnorm_q8_1" in kq.kq_last_error()
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((None, X, Y, Q, 1, 256, None), "null pointer"),
+    ((X, None, Y, Q, 1, 256, None), "null pointer"),
+    ((X, R, Y, None, 1, 256, None), "null pointer"),
+    ((X, R, Y, Q, 1, 32, None), "n=32"),
+    ((X, R, Y, Q, -2, 256, None), "rows=-2"),
+    ((X, R, Y, Q, 1 << 24, 65536, None), "too large"),
+    ((X + 4, R, Y, Q, 1, 256, None), "misaligned"),
+    ((X, R, Y + 4, Q, 1, 256, None), "misaligned"),
+    ((X, R, X, Q, 1, 256, None), "overlaps"),
+    ((X, R, Y, R + 16, 1, 256, None), "overlaps"),
+])
+def test_swiglu_rejects(kq, args, needle):
+    rc = kq.lib().kq_swiglu_q8_1(*args)
+    assert rc == kq.KQ_ERR_ARG, kq.kq_last_error()
+    assert needle in kq.kq_last_error()
+    assert "kq_swiglu_q8_1" in kq.kq_last_error()
+
+
+def test_producers_empty_and_no_fused_output(kq):
+    L = kq.lib()
+    assert L.kq_rmsnorm_q8_1(X, None, G, 1e-5, None, Q, 0, 4096, None) == kq.KQ_OK
+    assert L.kq_swiglu_q8_1(X, R, None, Q, 0, 14336, None) == kq.KQ_OK

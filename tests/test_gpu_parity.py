@@ -89,6 +89,21 @@ def test_quantize_ragged(kq, rows, k):
     assert np.array_equal(host(kq.quantize_q8_1(dev(x))), oracle.quantize_q8_1(x))
 
 
+def test_quantize_tiny_scale_blocks(kq):
+    """Blocks whose 1/d overflows (amax < 127 * 2^-128): zeros code 0,
+    nonzero values +-127, f16 d = 0 -- bit-exact with the oracle."""
+    say("quantize tiny-scale blocks")
+    rng = np.random.default_rng(17)
+    x = np.zeros((4, 256), dtype=np.float32)
+    x[0, :] = rng.standard_normal(256).astype(np.float32) * np.float32(1e-38)
+    x[1, ::3] = np.float32(-(2.0 ** -122))
+    x[1, 1::7] = np.float32(2.0 ** -140)
+    x[2, :] = np.float32(2.0 ** -149) * rng.integers(-3, 4, 256).astype(np.float32)
+    x[3, :] = rng.standard_normal(256).astype(np.float32) * np.float32(3e-37)
+    xq = host(kq.quantize_q8_1(dev(x)))
+    assert np.array_equal(xq, oracle.quantize_q8_1(x))
+
+
 # --------------------------------------------------------------- GEMVs -----
 
 def run_gemv(kq, kind, w, xq, m, k, batch, res=None, inplace=False):

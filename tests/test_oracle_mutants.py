@@ -70,6 +70,7 @@ MUTANTS = [
     ("exp degree 5", "    p = fmaf(p, r, 1.0f / 720.0f);", "    p = 0.0f;"),
     ("exp second reduction constant dropped", "    r = fmaf(-k, -2.12194440054690583e-4f, r);", "    (void)0;"),
     ("exp saturation at the wrong end", "    if (a < -110.0f) return 0.0f;", "    if (a < -110.0f) return INFINITY;"),
+    ("q8 NaN product coded -127", "if (v != v) v = 0.0f;", "if (v != v) v = -127.0f;"),
     ("swiglu up dropped", "yr[i] = silu_f32(gate[row * n + i]) * up[row * n + i];",
      "yr[i] = silu_f32(gate[row * n + i]);"),
 ]
