@@ -14,11 +14,12 @@ footprint exceeds twice the 256 MB Infinity Cache, so every step streams its
 weights from HBM.  Inputs are resident in HBM before the timed region.
 
 The other workloads are measured the same way and reported under
-``secondary``: batch-4 decode (fused QKV 6144x4096 and down 4096x14336 with
-residual), the Q6_K output head 128256x4096 (batch 1 and 4), the
+``secondary``: batch-4 and batch-8 decode (fused QKV 6144x4096 and down
+4096x14336 with residual), the Q6_K output head 128256x4096 (batch 1 and 4), the
 Qwen2-7B prefill MMQ at 2048 tokens (gate/up 18944x3584, down 3584x18944,
-QKV 4608x3584), and the fused producers RMSNorm -> q8_1 and SwiGLU -> q8_1
-at decode and prefill sizes next to a standalone quantisation.
+QKV 4608x3584), the fused producers RMSNorm -> q8_1 and SwiGLU -> q8_1
+at decode and prefill sizes next to a standalone quantisation, and separately
+stored q, k, v projections as three launches against one segmented launch.
 
 ``roofline`` describes the dominant kernel of the step, kq_gemv_q4k: its
 algorithmic bytes per launch (weights + q8_1 activation + f32 output) over
@@ -291,6 +292,62 @@ def measure_producers(cfg: int):
             "note": "inputs cache-resident between back-to-back launches"}
 
 
+def measure_segmented(cfg: int):
+    """Workload cfg's GEMVs share one activation: time them as separate
+    launches and as one segmented launch (kq_gemv_q4k_seg), each replayed as a
+    HIP graph over rotating weight copies."""
+    import torch
+
+    import q6_q8_matmul_amd as kq
+    from kq_inputs import WORKLOADS, tensor
+
+    wl = WORKLOADS[cfg]
+    ops = wl["ops"]
+    host = {op["w"]: tensor(cfg, op["w"]) for op in ops}
+    nbytes = sum(h.nbytes for h in host.values())
+    ncopy = copies_for(nbytes)
+    copies = [{n: torch.from_numpy(h).cuda() for n, h in host.items()}]
+    for _ in range(ncopy - 1):
+        copies.append({n: t.clone() for n, t in copies[0].items()})
+    x = torch.from_numpy(tensor(cfg, ops[0]["x"])).cuda()
+    xq = kq.quantize_q8_1(x)
+    k, batch = ops[0]["k"], ops[0]["batch"]
+    ys = [torch.empty((batch, op["m"]), dtype=torch.float32, device="cuda") for op in ops]
+    ms = [op["m"] for op in ops]
+
+    def run(c, seg):
+        ws = [copies[c][op["w"]] for op in ops]
+        if seg:
+            kq.kq_gemv_q4k_seg(ws, ms, ys, None, xq, k, batch)
+        else:
+            for w, y, m in zip(ws, ys, ms):
+                kq.kq_gemv_q4k(w, xq, y, None, m, k, batch)
+
+    out = {}
+    for seg in (False, True):
+        run(0, seg)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for c in range(ncopy):
+                run(c, seg)
+        stream = torch.cuda.current_stream()
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(20):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / (20 * ncopy) * 1e3
+        out["one_segmented_launch" if seg else "separate_launches"] = {
+            "us": round(us, 2), "weight_GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    return {"workload": wl["name"], "weight_bytes": nbytes, "weight_copies": ncopy, **out}
+
+
 def measure(cfg: int, steps: int, warmup: int, use_graph: bool):
     import torch
 
@@ -389,7 +446,7 @@ def _step_labels(cfg: int):
     return labels, kinds
 
 
-KERNEL_NAMES = {"quantize": "quantize_q8_1_kernel", "gemv_q4k": "gemv_q4k_kernel",
+KERNEL_NAMES = {"quantize": "quantize_q8_1_kernel", "gemv_q4k": "gemv_q4k_",   # _kernel or _persistent
                 "gemv_q6k": "gemv_q6k_kernel", "mmq_q4k": "mmq_q4k_kernel"}
 
 
@@ -551,12 +608,17 @@ def main(argv=None):
 
     secondary = {}
     main_cfg = 1
-    cfgs = [args.only] if args.only is not None else ([1] if args.no_secondary else [1, 2, 3, 4, 5, 6])
+    cfgs = [args.only] if args.only is not None else ([1] if args.no_secondary else [1, 2, 3, 4, 5, 6, 7, 8])
     result = None
     for cfg in cfgs:
         if cfg in (5, 6):
             log(f"workload {cfg}: fused producers")
             secondary[f"cfg{cfg}"] = measure_producers(cfg)
+            torch.cuda.empty_cache()
+            continue
+        if cfg == 8:
+            log(f"workload {cfg}: separate vs segmented GEMV launches")
+            secondary[f"cfg{cfg}"] = measure_segmented(cfg)
             torch.cuda.empty_cache()
             continue
         steps = args.steps if cfg != 4 else max(3, args.steps // 20)

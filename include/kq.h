@@ -10,7 +10,7 @@
  *     backend" 2.3: activations quantised once per matmul call by a small
  *     prepass before the GEMM).
  *   - kq_gemv_q4k / kq_gemv_q6k: the decode matrix-vector product at batch
- *     1..4, weight-streaming bound (minfer "The CUDA backend" 2.2 and 2.3,
+ *     1..8 (minfer decodes 2..8 tokens at once on this path), weight-streaming bound (minfer "The CUDA backend" 2.2 and 2.3,
  *     MMVQ; leone-cuda "CUDA kernel design": Q4_K and Q6_K GEMV, residual
  *     epilogue; cajeta "One model, start to last token" 4.1 and 4.2).
  *   - kq_mmq_q4k: the prefill matrix-matrix product over many tokens on the
@@ -74,6 +74,10 @@ typedef enum {
 #define KQ_MAX_K 65536
 /* Largest m / n / rows accepted (outputs are indexed with 32-bit rows). */
 #define KQ_MAX_ROWS 0x7fffffff
+/* Largest batch (activation columns) of one GEMV call. */
+#define KQ_MAX_BATCH 8
+/* Largest number of weight tensors of one segmented GEMV call. */
+#define KQ_MAX_SEGMENTS 8
 
 /*
  * Quantise f32 activations to q8_1.
@@ -92,14 +96,14 @@ typedef enum {
 int kq_quantize_q8_1(const float* x, void* xq, int64_t rows, int64_t k, void* stream);
 
 /*
- * Q4_K x q8_1 matrix-vector product for 1..4 activation vectors, with an
+ * Q4_K x q8_1 matrix-vector product for 1..8 activation vectors, with an
  * optional residual added when each output is written.
  *   w         [m][k/256] Q4_K superblocks (144 bytes), 16-byte aligned.
  *   xq        [batch][k/32] q8_1 blocks (from kq_quantize_q8_1), 16-byte aligned.
  *   y         out: f32 [batch][m], 4-byte aligned.
  *   residual  NULL, or f32 [batch][m], 4-byte aligned; y == residual is
  *             allowed (in place); any other overlap is an error.
- *   m >= 0;  k > 0, k % 256 == 0, k <= KQ_MAX_K;  1 <= batch <= 4.
+ *   m >= 0;  k > 0, k % 256 == 0, k <= KQ_MAX_K;  1 <= batch <= KQ_MAX_BATCH.
  * y[t][r] = residual[t][r] + sum over the k/32 blocks j of
  *           d8[t][j] * (d*sc_j * A - dmin*m_j * Bq), with A the integer dot of
  * the block's 4-bit codes with the q8 codes and Bq the sum of the q8 codes
@@ -110,7 +114,32 @@ int kq_gemv_q4k(const void* w, const void* xq, float* y, const float* residual,
                 int64_t m, int64_t k, int32_t batch, void* stream);
 
 /*
- * Q6_K x q8_1 matrix-vector product for 1..4 activation vectors, with an
+ * Several Q4_K GEMVs over one shared q8_1 activation in one launch -- e.g.
+ * separately stored q, k and v, or gate and up (leone-cuda "CUDA kernel
+ * design": QKV shares one quantisation, gate and up share one through the
+ * paired GEMV; cajeta "One model, start to last token" 4: the q|k|v and
+ * gate|up column segments run as one launch).
+ *   nseg       1 <= nseg <= KQ_MAX_SEGMENTS.
+ *   w, m, y    HOST arrays of nseg entries: device weights w[s]
+ *              ([m[s]][k/256] Q4_K, 16-byte aligned), row counts m[s] >= 0,
+ *              device outputs y[s] (f32 [batch][m[s]], 4-byte aligned); a
+ *              segment with m[s] == 0 is skipped and its pointers may be NULL.
+ *   residual   NULL, or a HOST array of nseg entries, each NULL or a device
+ *              f32 [batch][m[s]] (4-byte aligned) added on the row write;
+ *              y[s] == residual[s] is allowed.
+ *   xq, k, batch  shared by every segment, as in kq_gemv_q4k.
+ * Each y[s] equals what kq_gemv_q4k(w[s], xq, y[s], residual[s], m[s], k,
+ * batch) writes, bit for bit.  The host arrays are read during the call
+ * only.  No output may overlap any weight, another output or another
+ * segment's residual.  When the activation does not fit the kernel's LDS
+ * budget the segments run as consecutive launches on the same stream.
+ */
+int kq_gemv_q4k_seg(int32_t nseg, const void* const* w, const int64_t* m, float* const* y,
+                    const float* const* residual, const void* xq, int64_t k, int32_t batch,
+                    void* stream);
+
+/*
+ * Q6_K x q8_1 matrix-vector product for 1..8 activation vectors, with an
  * optional residual.  Same arguments and rules as kq_gemv_q4k except:
  *   w   [m][k/256] Q6_K superblocks (210 bytes), 16-byte aligned; the row
  *       stride 210*k/256 need not be a multiple of 16.

@@ -201,6 +201,38 @@ WORKLOADS = {
             dict(op="swiglu_q8_1", label="ffn_swiglu", gate="gate", up="up", rows=2048, n=18944),
         ],
     ),
+    # decode of eight sequences at once (minfer's decode range is 2..8 tokens)
+    7: dict(
+        name="llama3_8b_decode_gemv_q4k_b8",
+        tensors=[
+            ("qkv", "q4k", 6144, 4096),
+            ("down", "q4k", 4096, 14336),
+            ("x_qkv", "act", 8, 4096),
+            ("x_down", "act", 8, 14336),
+            ("res_down", "res", 8, 4096),
+        ],
+        ops=[
+            dict(op="gemv_q4k", label="qkv", w="qkv", x="x_qkv", m=6144, k=4096, batch=8),
+            dict(op="gemv_q4k", label="down+residual", w="down", x="x_down", m=4096, k=14336,
+                 batch=8, residual="res_down"),
+        ],
+    ),
+    # separately stored attention projections of Llama-3-8B (GGUF keeps q, k
+    # and v as three tensors): three launches, or one segmented launch
+    8: dict(
+        name="llama3_8b_decode_qkv_separate_b1",
+        tensors=[
+            ("q", "q4k", 4096, 4096),
+            ("k", "q4k", 1024, 4096),
+            ("v", "q4k", 1024, 4096),
+            ("x", "act", 1, 4096),
+        ],
+        ops=[
+            dict(op="gemv_q4k", label="q", w="q", x="x", m=4096, k=4096, batch=1),
+            dict(op="gemv_q4k", label="k", w="k", x="x", m=1024, k=4096, batch=1),
+            dict(op="gemv_q4k", label="v", w="v", x="x", m=1024, k=4096, batch=1),
+        ],
+    ),
 }
 
 

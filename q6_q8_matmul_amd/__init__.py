@@ -51,8 +51,9 @@ def lib() -> ctypes.CDLL:
         L.kq_mmq_q4k.argtypes = [p, p, p, i64, i64, i64, p]
         L.kq_rmsnorm_q8_1.argtypes = [p, p, p, ctypes.c_float, p, p, i64, i64, p]
         L.kq_swiglu_q8_1.argtypes = [p, p, p, p, i64, i64, p]
+        L.kq_gemv_q4k_seg.argtypes = [i32, p, p, p, p, p, i64, i32, p]
         for fn in (L.kq_quantize_q8_1, L.kq_gemv_q4k, L.kq_gemv_q6k, L.kq_mmq_q4k,
-                   L.kq_rmsnorm_q8_1, L.kq_swiglu_q8_1):
+                   L.kq_rmsnorm_q8_1, L.kq_swiglu_q8_1, L.kq_gemv_q4k_seg):
             fn.restype = ctypes.c_int
         L.kq_last_error.argtypes = []
         L.kq_last_error.restype = ctypes.c_char_p
@@ -112,6 +113,17 @@ def kq_gemv_q6k(w, xq, y, residual, m: int, k: int, batch: int, stream=None) -> 
 
 def kq_mmq_q4k(w, xq, y, m: int, n: int, k: int, stream=None) -> None:
     _check(lib().kq_mmq_q4k(_ptr(w), _ptr(xq), _ptr(y), m, n, k, _stream(stream)))
+
+
+def kq_gemv_q4k_seg(w, m, y, residual, xq, k: int, batch: int, stream=None) -> None:
+    """Segmented Q4_K GEMV: w, m, y (and residual, or None) are sequences of
+    equal length; their entries are tensors / device addresses / row counts."""
+    n = len(w)
+    W = (ctypes.c_void_p * n)(*[_ptr(t) for t in w])
+    M = (ctypes.c_int64 * n)(*[int(v) for v in m])
+    Y = (ctypes.c_void_p * n)(*[_ptr(t) for t in y])
+    R = None if residual is None else (ctypes.c_void_p * n)(*[_ptr(t) for t in residual])
+    _check(lib().kq_gemv_q4k_seg(n, W, M, Y, R, _ptr(xq), k, batch, _stream(stream)))
 
 
 def kq_rmsnorm_q8_1(x, res, g, eps: float, y, xq, rows: int, n: int, stream=None) -> None:
@@ -195,3 +207,15 @@ def swiglu_q8_1(gate, up, want_y: bool = True, stream=None):
     y = torch.empty((rows, n), dtype=torch.float32, device=gate.device) if want_y else None
     kq_swiglu_q8_1(gate, up, y, xq, rows, n, stream)
     return y, xq
+
+
+def gemv_q4k_seg(ws, ms, xq, k: int, batch: int, residuals=None, outs=None, stream=None):
+    """Several Q4_K GEMVs sharing one q8_1 activation in one launch; returns
+    the list of outputs f32 [batch, m[s]]."""
+    import torch
+
+    _require_cuda(xq, *ws)
+    ys = outs if outs is not None else [
+        torch.empty((batch, int(m)), dtype=torch.float32, device=xq.device) for m in ms]
+    kq_gemv_q4k_seg(ws, ms, ys, residuals, xq, k, batch, stream)
+    return ys

@@ -231,13 +231,65 @@ __device__ __forceinline__ void finish_rows(float (&acc)[RPW][BATCH], float* y,
     }
 }
 
-// PERSIST = false: one workgroup per WAVES*RPW row pairs, every workgroup
-// stages the activation (in chunks if needed).
-// PERSIST = true (only when the whole activation fits in LDS): a grid of a
-// few workgroups per compute unit stages it once and walks the row groups
-// blockIdx.x, blockIdx.x + gridDim.x, ...; the load ring runs across group
-// boundaries.
-template <int BATCH, int RPW, int DEPTH, int WAVES, bool PERSIST>
+// Weight tensors of one persistent launch: segment s has m[s] rows, weights
+// w[s], output y[s] and residual res[s] (or null); its row groups are
+// g0[s] .. g0[s+1]-1 of the launch.  All segments share the q8_1 activation,
+// k and the batch (leone-cuda "CUDA kernel design": QKV, and gate with up,
+// share one quantisation; cajeta "One model, start to last token" 4: the
+// paired q|k|v and gate|up launches).
+struct Segs {
+    int ngroups, n;
+    int g0[kMaxSegs + 1];
+    int m[kMaxSegs];
+    const uint8_t* w[kMaxSegs];
+    float* y[kMaxSegs];
+    const float* res[kMaxSegs];
+};
+
+// The one-tensor launch: a table of one row, kept small so the kernel reads
+// it with a few independent scalar loads.
+struct Seg1 {
+    const uint8_t* w;
+    float* y;
+    const float* res;
+    int m, ngroups;
+};
+
+// Position in the segment table of a stream of increasing row groups; it
+// advances only when a segment boundary is crossed, so the table is read once
+// per segment, not once per group.
+struct SegCursor {
+    int s, g0, g1, m;
+    const uint8_t* w;
+    float* y;
+    const float* res;
+};
+
+__device__ __forceinline__ void seg_seek(SegCursor& c, const Segs& sg, int g) {
+    while (g >= c.g1 && c.s + 1 < sg.n) {
+        ++c.s;
+        c.g0 = sg.g0[c.s];
+        c.g1 = sg.g0[c.s + 1];
+        c.m = sg.m[c.s];
+        c.w = sg.w[c.s];
+        c.y = sg.y[c.s];
+        c.res = sg.res[c.s];
+    }
+}
+__device__ __forceinline__ void seg_seek(SegCursor&, const Seg1&, int) {}
+
+__device__ __forceinline__ SegCursor seg_start(const Segs& sg, int g) {
+    SegCursor c{0, sg.g0[0], sg.g0[1], sg.m[0], sg.w[0], sg.y[0], sg.res[0]};
+    seg_seek(c, sg, g);
+    return c;
+}
+__device__ __forceinline__ SegCursor seg_start(const Seg1& t, int) {
+    return SegCursor{0, 0, t.ngroups, t.m, t.w, t.y, t.res};
+}
+
+// One workgroup per WAVES*RPW row pairs; every workgroup stages the
+// activation (in chunks when it exceeds the LDS budget).
+template <int BATCH, int RPW, int DEPTH, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __restrict__ w,
                                                               const uint8_t* __restrict__ xq,
                                                               float* y, const float* residual,
@@ -261,119 +313,193 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __r
 
     Slice ring[DEPTH][RPW];
     const uint8_t* rowp[RPW];
-    if constexpr (PERSIST) {
-        const int pairs_per_group = WAVES * RPW;
-        const int ngroups = (m + 2 * pairs_per_group - 1) / (2 * pairs_per_group);
-        const int nitems = ((ngroups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x) * npass;
-        // (group, pass) of the next item to load and of the next to compute
-        int gl = blockIdx.x, pl = 0;
-        group_rows<RPW>(rowp, w, gl, WAVES, wave, half, m, row_bytes);
+    const int pair0 = (blockIdx.x * WAVES + wave) * RPW;   // first row pair of this wave
+    const int chunk_passes = schunk >> 3;   // schunk is a multiple of 8 superblocks
+    group_rows<RPW>(rowp, w, blockIdx.x, WAVES, wave, half, m, row_bytes);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) load_pass<RPW>(ring[d], rowp, 8 * d + grp, S, t);
+
+    stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
+
+    for (int p0 = 0; p0 < npass; p0 += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
-            if (d < nitems) {
-                load_pass<RPW>(ring[d], rowp, 8 * pl + grp, S, t);
-                if (++pl == npass) {
-                    pl = 0;
-                    gl += gridDim.x;
-                    group_rows<RPW>(rowp, w, gl, WAVES, wave, half, m, row_bytes);
+            const int p = p0 + d;
+            if (p < npass) {
+                const int chunk = p / chunk_passes;
+                const int pl = p - chunk * chunk_passes;   // pass within the staged chunk
+                if (pl == 0 && p > 0) {                    // uniform over the workgroup
+                    __syncthreads();
+                    const int kc = chunk * schunk;
+                    stage_activation<BATCH, 64 * WAVES>(xq, nb_row, kc * 8,
+                                                        min(schunk, S - kc) * 8, schunk, smem);
                 }
+                if (8 * p + grp < S)   // lanes past the row end add nothing
+                    compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pl + grp, t);
+                if (p + DEPTH < npass)
+                    load_pass<RPW>(ring[d], rowp, 8 * (p + DEPTH) + grp, S, t);
             }
         }
-        stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, S * 8, schunk, smem);
-        int gc = blockIdx.x, pc = 0;
-        for (int it0 = 0; it0 < nitems; it0 += DEPTH) {
-#pragma unroll
-            for (int d = 0; d < DEPTH; ++d) {
-                const int it = it0 + d;
-                if (it < nitems) {
-                    if (8 * pc + grp < S)   // lanes past the row end add nothing
-                        compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pc + grp, t);
-                    if (it + DEPTH < nitems) {
-                        load_pass<RPW>(ring[d], rowp, 8 * pl + grp, S, t);
-                        if (++pl == npass) {
-                            pl = 0;
-                            gl += gridDim.x;
-                            group_rows<RPW>(rowp, w, gl, WAVES, wave, half, m, row_bytes);
-                        }
-                    }
-                    if (++pc == npass) {
-                        finish_rows<BATCH, RPW>(acc, y, residual, (gc * WAVES + wave) * RPW, half,
-                                                lane, m);
-                        pc = 0;
-                        gc += gridDim.x;
-                    }
-                }
-            }
-        }
-    } else {
-        const int pair0 = (blockIdx.x * WAVES + wave) * RPW;   // first row pair of this wave
-        const int chunk_passes = schunk >> 3;   // schunk is a multiple of 8 superblocks
-        group_rows<RPW>(rowp, w, blockIdx.x, WAVES, wave, half, m, row_bytes);
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) load_pass<RPW>(ring[d], rowp, 8 * d + grp, S, t);
+    }
+    finish_rows<BATCH, RPW>(acc, y, residual, pair0, half, lane, m);
+}
 
-        stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
+// Persistent form (the whole activation fits in LDS): a grid of a few
+// workgroups per compute unit stages the activation once and walks the row
+// groups blockIdx.x, blockIdx.x + gridDim.x, ... of all segments; the load
+// ring runs on across group (and segment) boundaries, so the memory pipe never
+// drains between them.
+template <int BATCH, int RPW, int DEPTH, int WAVES, class Tab>
+__global__ __launch_bounds__(64 * WAVES) void gemv_q4k_persistent(const Tab sg,
+                                                                  const uint8_t* __restrict__ xq,
+                                                                  int S, int schunk) {
+    extern __shared__ __align__(16) uint8_t smem[];
 
-        for (int p0 = 0; p0 < npass; p0 += DEPTH) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int half = lane >> 5;
+    const int grp = (lane >> 2) & 7;
+    const int t = lane & 3;
+    const int64_t row_bytes = (int64_t)S * kQ4KBytes;
+    const int nb_row = S * 8;
+    const int npass = (S + 7) >> 3;
+    const int ngroups = sg.ngroups;
+    const int nitems = ((ngroups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x) * npass;
+
+    float acc[RPW][BATCH];
 #pragma unroll
-            for (int d = 0; d < DEPTH; ++d) {
-                const int p = p0 + d;
-                if (p < npass) {
-                    const int chunk = p / chunk_passes;
-                    const int pl = p - chunk * chunk_passes;   // pass within the staged chunk
-                    if (pl == 0 && p > 0) {                    // uniform over the workgroup
-                        __syncthreads();
-                        const int kc = chunk * schunk;
-                        stage_activation<BATCH, 64 * WAVES>(xq, nb_row, kc * 8,
-                                                            min(schunk, S - kc) * 8, schunk, smem);
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) acc[i][b] = 0.0f;
+
+    Slice ring[DEPTH][RPW];
+    const uint8_t* rowp[RPW];
+    // (group, pass) of the next item to load and of the next to compute
+    int gl = blockIdx.x, pl = 0;
+    SegCursor cl = seg_start(sg, gl);
+    auto rows_of = [&](int g) {
+        seg_seek(cl, sg, g);
+        group_rows<RPW>(rowp, cl.w, g - cl.g0, WAVES, wave, half, cl.m, row_bytes);
+    };
+    rows_of(gl);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+        if (d < nitems) {
+            load_pass<RPW>(ring[d], rowp, 8 * pl + grp, S, t);
+            if (++pl == npass) {
+                pl = 0;
+                gl += gridDim.x;
+                if (gl < ngroups) rows_of(gl);
+            }
+        }
+    }
+    stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, S * 8, schunk, smem);
+    int gc = blockIdx.x, pc = 0;
+    SegCursor cc = seg_start(sg, gc);
+    for (int it0 = 0; it0 < nitems; it0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int it = it0 + d;
+            if (it < nitems) {
+                if (8 * pc + grp < S)   // lanes past the row end add nothing
+                    compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pc + grp, t);
+                if (it + DEPTH < nitems) {
+                    load_pass<RPW>(ring[d], rowp, 8 * pl + grp, S, t);
+                    if (++pl == npass) {
+                        pl = 0;
+                        gl += gridDim.x;
+                        if (gl < ngroups) rows_of(gl);
                     }
-                    if (8 * p + grp < S)   // lanes past the row end add nothing
-                        compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pl + grp, t);
-                    if (p + DEPTH < npass)
-                        load_pass<RPW>(ring[d], rowp, 8 * (p + DEPTH) + grp, S, t);
+                }
+                if (++pc == npass) {
+                    seg_seek(cc, sg, gc);
+                    finish_rows<BATCH, RPW>(acc, cc.y, cc.res, ((gc - cc.g0) * WAVES + wave) * RPW,
+                                            half, lane, cc.m);
+                    pc = 0;
+                    gc += gridDim.x;
                 }
             }
         }
-        finish_rows<BATCH, RPW>(acc, y, residual, pair0, half, lane, m);
     }
 }
 
-// Launch one variant.  `persist_per_cu` > 0 asks for the persistent form with
-// that many workgroups per compute unit (capped by occupancy); it is used
-// only when the whole activation fits in one LDS piece.
+// Occupancy of a persistent kernel, asked once per instantiation.
+template <class K>
+int occupancy(K kern, int threads, size_t lds) {
+    static std::atomic<int> occ{0};
+    int o = occ.load(std::memory_order_relaxed);
+    if (o == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, threads, lds) != hipSuccess || o < 1)
+            o = 1;
+        occ.store(o, std::memory_order_relaxed);
+    }
+    return o;
+}
+
+// Persistent launch over the row groups of table `tab` (one tensor or a
+// segment table).
+template <int BATCH, int RPW, int DEPTH, int WAVES, class Tab>
+hipError_t launch_persistent(const Tab& tab, const void* xq, int64_t k, int schunk, size_t lds,
+                             int cus, int per_cu, hipStream_t stream) {
+    if (tab.ngroups == 0) return hipSuccess;
+    auto kern = gemv_q4k_persistent<BATCH, RPW, DEPTH, WAVES, Tab>;
+    const int o = occupancy(kern, 64 * WAVES, lds);
+    const int grid = std::min(tab.ngroups, cus * std::min(o, per_cu));
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WAVES), lds, stream, tab,
+                       (const uint8_t*)xq, (int)(k / kQK), schunk);
+    return hipGetLastError();
+}
+
+// LDS chunk (superblocks per staged piece) of a batch under a budget; 0 if
+// not even one pass fits.
+template <int BATCH>
+int chunk_for(int64_t k, int lds_budget) {
+    const int S = (int)(k / kQK);
+    int schunk = (lds_budget / (BATCH * kLdsPerSb)) & ~7;      // whole passes of 8 superblocks
+    const int s_round = (S + 7) & ~7;
+    if (schunk > s_round) schunk = s_round;
+    return schunk < 8 ? 0 : schunk;
+}
+
+// Launch one variant on one weight tensor.  `persist_per_cu` > 0 asks for the
+// persistent form with that many workgroups per compute unit (capped by
+// occupancy); it is used only when the whole activation fits in one LDS
+// piece.
 template <int BATCH, int RPW, int DEPTH, int WAVES>
 hipError_t launch_variant(const void* w, const void* xq, float* y, const float* residual,
                           int64_t m, int64_t k, int lds_budget, int cus, int persist_per_cu,
                           hipStream_t stream) {
     const int S = (int)(k / kQK);
-    const int per_sb = BATCH * kLdsPerSb;
-    int schunk = (lds_budget / per_sb) & ~7;      // whole passes of 8 superblocks
-    const int s_round = (S + 7) & ~7;
-    if (schunk > s_round) schunk = s_round;
-    if (schunk < 8) return hipErrorInvalidConfiguration;
-    const size_t lds = (size_t)schunk * per_sb;
+    const int schunk = chunk_for<BATCH>(k, lds_budget);
+    if (schunk == 0) return hipErrorInvalidConfiguration;
+    const size_t lds = (size_t)schunk * BATCH * kLdsPerSb;
+    if (persist_per_cu > 0 && schunk >= S) {
+        const int rows_per_group = WAVES * RPW * 2;
+        const Seg1 tab{(const uint8_t*)w, y, residual, (int)m,
+                       (int)((m + rows_per_group - 1) / rows_per_group)};
+        return launch_persistent<BATCH, RPW, DEPTH, WAVES>(tab, xq, k, schunk, lds, cus,
+                                                           persist_per_cu, stream);
+    }
     const int rows_per_block = WAVES * RPW * 2;
     const int64_t ngroups = (m + rows_per_block - 1) / rows_per_block;
-    if (persist_per_cu > 0 && schunk >= S) {
-        auto kern = gemv_q4k_kernel<BATCH, RPW, DEPTH, WAVES, true>;
-        static std::atomic<int> occ{0};
-        int o = occ.load(std::memory_order_relaxed);
-        if (o == 0) {
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, 64 * WAVES, lds) != hipSuccess || o < 1)
-                o = 1;
-            occ.store(o, std::memory_order_relaxed);
-        }
-        const int64_t grid = std::min<int64_t>(ngroups, (int64_t)cus * std::min(o, persist_per_cu));
-        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WAVES), lds, stream,
-                           (const uint8_t*)w, (const uint8_t*)xq, y, residual, (int)m, S, schunk);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((gemv_q4k_kernel<BATCH, RPW, DEPTH, WAVES, false>), dim3((unsigned)ngroups),
+    hipLaunchKernelGGL((gemv_q4k_kernel<BATCH, RPW, DEPTH, WAVES>), dim3((unsigned)ngroups),
                        dim3(64 * WAVES), lds, stream, (const uint8_t*)w, (const uint8_t*)xq, y,
                        residual, (int)m, S, schunk);
     return hipGetLastError();
 }
 
+}  // namespace gemv4
+
+namespace gemv4 {
+// Batches 5..8 (decode of several sequences): the persistent four-wavefront
+// form when the activation fits in 64 KB of LDS, else the chunked form with
+// one pass in flight over eight wavefronts.
+template <int B>
+hipError_t wide(const void* w, const void* xq, float* y, const float* residual, int64_t m,
+                int64_t k, int64_t whole, int one_piece, int cus, hipStream_t stream) {
+    return whole > 65536 ? launch_variant<B, 1, 1, 8>(w, xq, y, residual, m, k, one_piece, cus, 0, stream)
+                         : launch_variant<B, 1, 1, 4>(w, xq, y, residual, m, k, one_piece, cus, 6, stream);
+}
 }  // namespace gemv4
 
 hipError_t launch_gemv_q4k(const void* w, const void* xq, float* y, const float* residual,
@@ -401,6 +527,71 @@ hipError_t launch_gemv_q4k(const void* w, const void* xq, float* y, const float*
         case 3: return launch_variant<3, 1, 1, 4>(w, xq, y, residual, m, k, one_piece, cus, 6, stream);
         case 4: return whole > 65536 ? launch_variant<4, 1, 3, 8>(w, xq, y, residual, m, k, one_piece, cus, 0, stream)
                                      : launch_variant<4, 1, 1, 4>(w, xq, y, residual, m, k, one_piece, cus, 6, stream);
+        case 5: return wide<5>(w, xq, y, residual, m, k, whole, one_piece, cus, stream);
+        case 6: return wide<6>(w, xq, y, residual, m, k, whole, one_piece, cus, stream);
+        case 7: return wide<7>(w, xq, y, residual, m, k, whole, one_piece, cus, stream);
+        case 8: return wide<8>(w, xq, y, residual, m, k, whole, one_piece, cus, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+namespace gemv4 {
+// Segments of one launch: persistent when the activation fits the budget,
+// else one ordinary launch per segment.
+template <int BATCH, int RPW, int DEPTH, int WAVES>
+hipError_t launch_segs(const Segs& sg, const void* xq, int64_t k, int lds_budget, int cus,
+                       int per_cu, int lds_limit, hipStream_t stream) {
+    const int S = (int)(k / kQK);
+    const int schunk = chunk_for<BATCH>(k, lds_budget);
+    if (schunk >= S && schunk > 0) {
+        Segs tab = sg;   // row groups of each segment, in segment order
+        const int rows_per_group = WAVES * RPW * 2;
+        tab.g0[0] = 0;
+        for (int s = 0; s < tab.n; ++s)
+            tab.g0[s + 1] = tab.g0[s] + (tab.m[s] + rows_per_group - 1) / rows_per_group;
+        tab.ngroups = tab.g0[tab.n];
+        return launch_persistent<BATCH, RPW, DEPTH, WAVES>(
+            tab, xq, k, schunk, (size_t)schunk * BATCH * kLdsPerSb, cus, per_cu, stream);
+    }
+    for (int s = 0; s < sg.n; ++s) {
+        if (sg.m[s] == 0) continue;
+        const hipError_t e = launch_gemv_q4k(sg.w[s], xq, sg.y[s], sg.res[s], sg.m[s], k, BATCH,
+                                             lds_limit, cus, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+}  // namespace gemv4
+
+hipError_t launch_gemv_q4k_seg(int nseg, const void* const* w, const int64_t* m, float* const* y,
+                               const float* const* residual, const void* xq, int64_t k, int batch,
+                               int lds_limit, int cus, hipStream_t stream) {
+    using namespace gemv4;
+    Segs sg = {};
+    sg.n = nseg;
+    int64_t total = 0;
+    for (int s = 0; s < nseg; ++s) {   // zero-row segments get no row groups
+        sg.w[s] = (const uint8_t*)w[s];
+        sg.y[s] = y[s];
+        sg.res[s] = residual ? residual[s] : nullptr;
+        sg.m[s] = (int)m[s];
+        total += m[s];
+    }
+    // the single-tensor launch shapes, chosen on the launch's total rows
+    const int S = (int)(k / kQK);
+    const int64_t whole = (int64_t)batch * kLdsPerSb * ((S + 7) & ~7);
+    const bool big = total >= 16384 || S > 16;
+    const int fit = whole > 65536 ? 0 : 65536;   // 0: one ordinary launch per segment
+    switch (batch) {
+        case 1: return big ? launch_segs<1, 1, 1, 8>(sg, xq, k, 65536, cus, 3, lds_limit, stream)
+                           : launch_segs<1, 1, 1, 4>(sg, xq, k, 65536, cus, 4, lds_limit, stream);
+        case 2: return launch_segs<2, 1, 1, 4>(sg, xq, k, fit, cus, 6, lds_limit, stream);
+        case 3: return launch_segs<3, 1, 1, 4>(sg, xq, k, fit, cus, 6, lds_limit, stream);
+        case 4: return launch_segs<4, 1, 1, 4>(sg, xq, k, fit, cus, 6, lds_limit, stream);
+        case 5: return launch_segs<5, 1, 1, 4>(sg, xq, k, fit, cus, 6, lds_limit, stream);
+        case 6: return launch_segs<6, 1, 1, 4>(sg, xq, k, fit, cus, 6, lds_limit, stream);
+        case 7: return launch_segs<7, 1, 1, 4>(sg, xq, k, fit, cus, 6, lds_limit, stream);
+        case 8: return launch_segs<8, 1, 1, 4>(sg, xq, k, fit, cus, 6, lds_limit, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -364,6 +364,10 @@ hipError_t launch_gemv_q6k(const void* w, const void* xq, float* y, const float*
         case 2: return launch_variant<2, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
         case 3: return launch_variant<3, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
         case 4: return launch_variant<4, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
+        case 5: return launch_variant<5, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
+        case 6: return launch_variant<6, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
+        case 7: return launch_variant<7, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
+        case 8: return launch_variant<8, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
         default: return hipErrorInvalidValue;
     }
 }

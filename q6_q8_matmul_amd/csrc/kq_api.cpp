@@ -93,8 +93,8 @@ int gemv_common(const char* fn, int wbytes, const void* w, const void* xq, float
     if (int rc = check_k(fn, k, 256)) return rc;
     if (m < 0 || m > KQ_MAX_ROWS)
         return fail(KQ_ERR_ARG, "%s: m=%lld out of range [0, %d]", fn, (long long)m, KQ_MAX_ROWS);
-    if (batch < 1 || batch > 4)
-        return fail(KQ_ERR_ARG, "%s: batch=%d must be in [1, 4]", fn, (int)batch);
+    if (batch < 1 || batch > KQ_MAX_BATCH)
+        return fail(KQ_ERR_ARG, "%s: batch=%d must be in [1, %d]", fn, (int)batch, KQ_MAX_BATCH);
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(y, 4) || (residual && !aligned(residual, 4)))
         return fail(KQ_ERR_ARG,
                     "%s: misaligned pointer (w=%p xq=%p need 16, y=%p residual=%p need 4)", fn, w,
@@ -141,6 +141,50 @@ int kq_gemv_q4k(const void* w, const void* xq, float* y, const float* residual, 
     if (int rc = check_device(fn, &lds, &cus)) return rc;
     return launched(fn, kq::launch_gemv_q4k(w, xq, y, residual, m, k, batch, lds, cus,
                                             (hipStream_t)stream));
+}
+
+int kq_gemv_q4k_seg(int32_t nseg, const void* const* w, const int64_t* m, float* const* y,
+                    const float* const* residual, const void* xq, int64_t k, int32_t batch,
+                    void* stream) {
+    const char* fn = "kq_gemv_q4k_seg";
+    if (nseg < 1 || nseg > KQ_MAX_SEGMENTS)
+        return fail(KQ_ERR_ARG, "%s: nseg=%d must be in [1, %d]", fn, (int)nseg, KQ_MAX_SEGMENTS);
+    if (!w || !m || !y)
+        return fail(KQ_ERR_ARG, "%s: null array (w=%p m=%p y=%p)", fn, (const void*)w,
+                    (const void*)m, (const void*)y);
+    if (!xq) return fail(KQ_ERR_ARG, "%s: null pointer (xq=%p)", fn, xq);
+    if (int rc = check_k(fn, k, 256)) return rc;
+    if (batch < 1 || batch > KQ_MAX_BATCH)
+        return fail(KQ_ERR_ARG, "%s: batch=%d must be in [1, %d]", fn, (int)batch, KQ_MAX_BATCH);
+    if (!aligned(xq, 16)) return fail(KQ_ERR_ARG, "%s: misaligned pointer (xq=%p needs 16)", fn, xq);
+    int64_t total = 0;
+    for (int s = 0; s < nseg; ++s) {
+        if (m[s] == 0) continue;   // skipped segment: its pointers are not used
+        const float* r = residual ? residual[s] : nullptr;
+        if (int rc = gemv_common(fn, 144, w[s], xq, y[s], r, m[s], k, batch)) return rc;
+        total += m[s];
+    }
+    if (total > KQ_MAX_ROWS)
+        return fail(KQ_ERR_ARG, "%s: %lld rows in all segments, more than %d", fn,
+                    (long long)total, KQ_MAX_ROWS);
+    for (int s = 0; s < nseg; ++s) {
+        if (m[s] == 0) continue;
+        const int64_t yn = (int64_t)batch * m[s] * 4;
+        for (int t = 0; t < nseg; ++t) {
+            if (m[t] == 0) continue;
+            const int64_t wt = m[t] * (k / 256) * 144, yt = (int64_t)batch * m[t] * 4;
+            const float* rt = residual ? residual[t] : nullptr;
+            if (overlap(y[s], yn, w[t], wt) || (t != s && overlap(y[s], yn, y[t], yt)) ||
+                (t != s && rt && overlap(y[s], yn, rt, yt)))
+                return fail(KQ_ERR_ARG, "%s: output y[%d]=%p overlaps a buffer of segment %d", fn,
+                            s, (void*)y[s], t);
+        }
+    }
+    if (total == 0) return ok();
+    int lds = 0, cus = 0;
+    if (int rc = check_device(fn, &lds, &cus)) return rc;
+    return launched(fn, kq::launch_gemv_q4k_seg(nseg, w, m, y, residual, xq, k, batch, lds, cus,
+                                                (hipStream_t)stream));
 }
 
 int kq_gemv_q6k(const void* w, const void* xq, float* y, const float* residual, int64_t m,

@@ -13,6 +13,7 @@ constexpr int kQK = 256;        // values per superblock
 constexpr int kQ4KBytes = 144;  // Q4_K superblock
 constexpr int kQ6KBytes = 210;  // Q6_K superblock
 constexpr int kQ81Bytes = 36;   // q8_1 block (32 values)
+constexpr int kMaxSegs = 8;     // weight segments of one segmented GEMV launch
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu));
@@ -92,6 +93,9 @@ hipError_t launch_quantize_q8_1(const float* x, void* xq, int64_t rows, int64_t 
 hipError_t launch_gemv_q4k(const void* w, const void* xq, float* y, const float* residual,
                            int64_t m, int64_t k, int batch, int lds_limit, int cus,
                            hipStream_t stream);
+hipError_t launch_gemv_q4k_seg(int nseg, const void* const* w, const int64_t* m, float* const* y,
+                               const float* const* residual, const void* xq, int64_t k, int batch,
+                               int lds_limit, int cus, hipStream_t stream);
 hipError_t launch_gemv_q6k(const void* w, const void* xq, float* y, const float* residual,
                            int64_t m, int64_t k, int batch, int lds_limit, int cus,
                            hipStream_t stream);

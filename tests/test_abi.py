@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "kq_quantize_q8_1", "kq_gemv_q4k", "kq_gemv_q6k", "kq_mmq_q4k",
-        "kq_rmsnorm_q8_1", "kq_swiglu_q8_1", "kq_last_error", "kq_abi_version"])
+        "kq_rmsnorm_q8_1", "kq_swiglu_q8_1", "kq_gemv_q4k_seg", "kq_last_error",
+        "kq_abi_version"])
 
 
 def test_library_exports_every_declared_symbol(kq):
@@ -82,7 +83,7 @@ def test_quantize_rejects(kq, args, needle):
     ((W, X, Y, None, 8, 256 * 257, 1, None), "k="),
     ((W, X, Y, None, -3, 256, 1, None), "m=-3"),
     ((W, X, Y, None, 8, 256, 0, None), "batch=0"),
-    ((W, X, Y, None, 8, 256, 5, None), "batch=5"),
+    ((W, X, Y, None, 8, 256, 9, None), "batch=9"),
     ((W + 8, X, Y, None, 8, 256, 1, None), "misaligned"),
     ((W, X + 1, Y, None, 8, 256, 1, None), "misaligned"),
     ((W, X + 4, Y, None, 8, 256, 1, None), "misaligned"),
@@ -128,8 +129,8 @@ def test_empty_inputs_launch_nothing(kq):
 
 
 def test_binding_raises_with_message(kq):
-    with pytest.raises(kq.KQError, match="batch=7"):
-        kq.kq_gemv_q4k(W, X, Y, None, 8, 256, 7, stream=0)
+    with pytest.raises(kq.KQError, match="batch=9"):
+        kq.kq_gemv_q4k(W, X, Y, None, 8, 256, 9, stream=0)
 
 
 def test_no_gpu_means_unsupported(kq):
@@ -194,3 +195,38 @@ def test_producers_empty_and_no_fused_output(kq):
     L = kq.lib()
     assert L.kq_rmsnorm_q8_1(X, None, G, 1e-5, None, Q, 0, 4096, None) == kq.KQ_OK
     assert L.kq_swiglu_q8_1(X, R, None, Q, 0, 14336, None) == kq.KQ_OK
+
+
+def _seg(kq, nseg, w, m, y, res, xq=X, k=256, batch=1):
+    import ctypes
+    n = len(w)
+    W = (ctypes.c_void_p * n)(*w)
+    M = (ctypes.c_int64 * n)(*m)
+    Y = (ctypes.c_void_p * n)(*y)
+    R = None if res is None else (ctypes.c_void_p * n)(*res)
+    return kq.lib().kq_gemv_q4k_seg(nseg, W, M, Y, R, xq, k, batch, None)
+
+
+@pytest.mark.parametrize("case,needle", [
+    ((0, [W], [8], [Y], None), "nseg=0"),
+    ((9, [W] * 9, [8] * 9, [Y + 4096 * i for i in range(9)], None), "nseg=9"),
+    ((2, [W, 0], [8, 8], [Y, Y + 4096], None), "null pointer"),
+    ((2, [W, W + 4], [8, 8], [Y, Y + 4096], None), "misaligned"),
+    ((2, [W, W + 16 * 4096], [8, -1], [Y, Y + 4096], None), "m=-1"),
+    ((2, [W, W + 16 * 4096], [8, 8], [Y, Y + 16], None), "overlaps"),
+    ((2, [W, W + 16 * 4096], [8, 8], [Y, W], None), "overlaps"),
+    ((2, [W, W + 16 * 4096], [8, 8], [Y, Y + 4096], [Y + 4096, 0]), "overlaps"),
+])
+def test_gemv_seg_rejects(kq, case, needle):
+    rc = _seg(kq, *case)
+    assert rc == kq.KQ_ERR_ARG, kq.kq_last_error()
+    assert needle in kq.kq_last_error()
+
+
+def test_gemv_seg_empty_and_null_arrays(kq):
+    assert _seg(kq, 2, [W, W + 16 * 4096], [0, 0], [Y, Y + 4096], None) == kq.KQ_OK
+    assert _seg(kq, 2, [0, 0], [0, 0], [0, 0], None) == kq.KQ_OK
+    rc = _seg(kq, 1, [W], [0], [Y], None, k=100)
+    assert rc == kq.KQ_ERR_ARG and "k=100" in kq.kq_last_error()
+    rc = kq.lib().kq_gemv_q4k_seg(1, None, None, None, None, X, 256, 1, None)
+    assert rc == kq.KQ_ERR_ARG and "null array" in kq.kq_last_error()

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from kq_inputs import WORKLOADS, random_case, tensor
+from kq_inputs import WORKLOADS, activations, random_case, residual, tensor
 from oracle_pins import _adversarial_blocks, _distinguishing_blocks
 
 pytestmark = pytest.mark.gpu
@@ -117,7 +117,7 @@ def run_gemv(kq, kind, w, xq, m, k, batch, res=None, inplace=False):
     return host(y)
 
 
-GEMV_OPS = [(c, i) for c in (0, 1, 2, 3) for i in range(len(WORKLOADS[c]["ops"]))]
+GEMV_OPS = [(c, i) for c in (0, 1, 2, 3, 7) for i in range(len(WORKLOADS[c]["ops"]))]
 
 
 @pytest.mark.parametrize("cfg,i", GEMV_OPS,
@@ -145,6 +145,10 @@ SHAPES = [
     ("q6k", 1, 256, 1, False), ("q6k", 7, 768, 3, True), ("q6k", 13, 2304, 2, False),
     ("q6k", 1001, 1280, 4, True), ("q6k", 37, 14336, 4, True), ("q6k", 9, 32768, 4, False),
     ("q6k", 300, 4352, 1, False), ("q6k", 20001, 512, 3, True),
+    # batches 5..8: persistent (activation fits) and chunked (it does not)
+    ("q4k", 1000, 4096, 8, True), ("q4k", 513, 2048, 5, False), ("q4k", 37, 14336, 6, True),
+    ("q4k", 130, 28672, 7, False), ("q6k", 1001, 4096, 8, True), ("q6k", 77, 768, 5, False),
+    ("q6k", 9, 32768, 8, False), ("q6k", 2000, 1024, 6, True),
 ]
 
 
@@ -281,10 +285,68 @@ def test_bad_arguments_launch_nothing(kq):
     y = torch.full((2, 64), 7.0, device="cuda")
     for call in (
         lambda: kq.kq_gemv_q4k(wd, xq, y, None, 64, 500, 2),
-        lambda: kq.kq_gemv_q4k(wd, xq, y, None, 64, 512, 5),
+        lambda: kq.kq_gemv_q4k(wd, xq, y, None, 64, 512, 9),
         lambda: kq.kq_gemv_q6k(wd, xq, y, y[:, 1:], 64, 512, 2),
         lambda: kq.kq_mmq_q4k(wd, xq, wd, 64, 2, 512),
     ):
         with pytest.raises(kq.KQError):
             call()
     assert torch.all(y == 7.0).item()
+
+
+# ----------------------------------------------------- segmented GEMV ----
+
+SEG_CASES = [
+    # (rows per segment, k, batch, residual on segments)
+    ((4096, 1024, 1024), 4096, 1, (False, False, False)),
+    ((4096, 1024, 1024), 4096, 4, (True, False, True)),
+    ((2048, 512, 512), 4096, 8, (False, True, False)),
+    ((0, 1, 7, 33, 300), 768, 3, (False, True, True, False, True)),
+    ((700, 300), 14336, 4, (True, False)),          # activation exceeds 64 KB: one launch per segment
+    ((14336, 14336), 4096, 1, (False, False)),      # gate and up as separate tensors
+]
+
+
+@pytest.mark.parametrize("ms,k,batch,res_on", SEG_CASES,
+                         ids=[f"{'-'.join(map(str, c[0]))}-k{c[1]}-b{c[2]}" for c in SEG_CASES])
+def test_gemv_seg_matches_single(kq, ms, k, batch, res_on):
+    say(f"segmented gemv m={ms} k={k} batch={batch}")
+    from kq_inputs import q4k_weights
+
+    x = activations(61, 0, batch, k)
+    xq_h = oracle.quantize_q8_1(x)
+    xq = dev(xq_h)
+    ws, res, ys_ref = [], [], []
+    for s, m in enumerate(ms):
+        wh = q4k_weights(61, 10 + s, m, k)
+        rh = residual(61, 30 + s, batch, m) if res_on[s] else None
+        ws.append(dev(wh))
+        res.append(dev(rh) if rh is not None else None)
+        if m:
+            y_ref, den = oracle.matmul("q4k", wh, xq_h, m, batch, k, residual=rh)
+            ys_ref.append((y_ref, den))
+        else:
+            ys_ref.append(None)
+    ys = kq.gemv_q4k_seg(ws, ms, xq, k, batch, residuals=res)
+    for s, m in enumerate(ms):
+        if not m:
+            continue
+        single = kq.gemv_q4k(ws[s], xq, m, k, batch, residual=res[s])
+        assert torch.equal(ys[s], single), f"segment {s} differs from the single-tensor call"
+        check_close(host(ys[s]), ys_ref[s][0], ys_ref[s][1], f"segment {s} m={m}")
+
+
+def test_gemv_seg_in_place_residual(kq):
+    say("segmented gemv, residual in place")
+    from kq_inputs import q4k_weights
+
+    k, batch, ms = 2048, 2, (1000, 24)
+    x = activations(62, 0, batch, k)
+    xq_h = oracle.quantize_q8_1(x)
+    ws = [dev(q4k_weights(62, 10 + s, m, k)) for s, m in enumerate(ms)]
+    rs = [residual(62, 30 + s, batch, m) for s, m in enumerate(ms)]
+    ys = [dev(r) for r in rs]
+    kq.gemv_q4k_seg(ws, ms, dev(xq_h), k, batch, residuals=ys, outs=ys)
+    for s, m in enumerate(ms):
+        y_ref, den = oracle.matmul("q4k", ws[s].cpu().numpy(), xq_h, m, batch, k, residual=rs[s])
+        check_close(host(ys[s]), y_ref, den, f"in place segment {s}")
