@@ -16,8 +16,9 @@ weights from HBM.  Inputs are resident in HBM before the timed region.
 The other workloads are measured the same way and reported under
 ``secondary``: batch-4 and batch-8 decode (fused QKV 6144x4096 and down
 4096x14336 with residual), the Q6_K output head 128256x4096 (batch 1 and 4), the
-Qwen2-7B prefill MMQ at 2048 tokens (gate/up 18944x3584, down 3584x18944,
-QKV 4608x3584), the fused producers RMSNorm -> q8_1 and SwiGLU -> q8_1
+Qwen2-7B prefill MMQ at 2048 tokens (Q4_K gate/up 18944x3584, down
+3584x18944, QKV 4608x3584; Q6_K v 512x3584 and down 3584x18944), the fused
+producers RMSNorm -> q8_1 and SwiGLU -> q8_1
 at decode and prefill sizes next to a standalone quantisation, and separately
 stored q, k, v projections as three launches against one segmented launch.
 
@@ -129,9 +130,10 @@ class Workload:
                             lambda fn=fn, w=w, xq=xq, y=y, res=res, op=op:
                             fn(w, xq, y, res, op["m"], op["k"], op["batch"])))
             else:
+                fn = kq.kq_mmq_q4k if op["op"] == "mmq_q4k" else kq.kq_mmq_q6k
                 out.append((op["label"], op["op"],
-                            lambda w=w, xq=xq, y=y, op=op:
-                            kq.kq_mmq_q4k(w, xq, y, op["m"], op["n"], op["k"])))
+                            lambda fn=fn, w=w, xq=xq, y=y, op=op:
+                            fn(w, xq, y, op["m"], op["n"], op["k"])))
         return out
 
     def step(self, c: int):
@@ -379,7 +381,7 @@ def cpu_baseline(wl: Workload, seconds: float):
         xq = {xn: oracle.quantize_q8_1(wl.host[xn]) for xn in wl.x}
         outs = []
         for op in wl.ops:
-            kind = "q4k" if op["op"] in ("gemv_q4k", "mmq_q4k") else "q6k"
+            kind = "q4k" if op["op"].endswith("q4k") else "q6k"
             rows = op.get("batch", op.get("n"))
             res = wl.host.get(op.get("residual")) if "residual" in op else None
             outs.append(oracle.matmul(kind, wl.host[op["w"]], xq[op["x"]], op["m"], rows, op["k"],
@@ -416,6 +418,7 @@ KERNEL_SOURCES = {
     "gemv_q4k": "q6_q8_matmul_amd/csrc/gemv_q4k.hip",
     "gemv_q6k": "q6_q8_matmul_amd/csrc/gemv_q6k.hip",
     "mmq_q4k": "q6_q8_matmul_amd/csrc/mmq_q4k.hip",
+    "mmq_q6k": "q6_q8_matmul_amd/csrc/mmq_q6k.hip",
     "quantize": "q6_q8_matmul_amd/csrc/quantize_q8_1.hip",
 }
 FETCH_SCALE_NOTE = ("FETCH_SIZE and WRITE_SIZE are scaled by bytes / counter reading of the "
@@ -447,7 +450,8 @@ def _step_labels(cfg: int):
 
 
 KERNEL_NAMES = {"quantize": "quantize_q8_1_kernel", "gemv_q4k": "gemv_q4k_",   # _kernel or _persistent
-                "gemv_q6k": "gemv_q6k_kernel", "mmq_q4k": "mmq_q4k_kernel"}
+                "gemv_q6k": "gemv_q6k_kernel", "mmq_q4k": "mmq_q4k_kernel",
+                "mmq_q6k": "mmq_q6k_kernel"}
 
 
 def _steps_in(rows, cfg):
@@ -608,7 +612,7 @@ def main(argv=None):
 
     secondary = {}
     main_cfg = 1
-    cfgs = [args.only] if args.only is not None else ([1] if args.no_secondary else [1, 2, 3, 4, 5, 6, 7, 8])
+    cfgs = [args.only] if args.only is not None else ([1] if args.no_secondary else [1, 2, 3, 4, 5, 6, 7, 8, 9])
     result = None
     for cfg in cfgs:
         if cfg in (5, 6):
@@ -621,8 +625,9 @@ def main(argv=None):
             secondary[f"cfg{cfg}"] = measure_segmented(cfg)
             torch.cuda.empty_cache()
             continue
-        steps = args.steps if cfg != 4 else max(3, args.steps // 20)
-        warm = args.warmup if cfg != 4 else max(1, args.warmup // 10)
+        prefill = cfg in (4, 9)
+        steps = args.steps if not prefill else max(3, args.steps // 20)
+        warm = args.warmup if not prefill else max(1, args.warmup // 10)
         log(f"workload {cfg}: {steps} steps, {warm} warm-up, graphs={use_graph}")
         wl, ms, durs = measure(cfg, steps, warm, use_graph)
         per_op = []
@@ -630,7 +635,7 @@ def main(argv=None):
             label, kind, avg_ms = [d for d in durs if d[0] == op["label"]][0]
             e = {"op": op["label"], "kernel": "kq_" + op["op"], "shape": [op["m"], op["k"], op.get("batch", op.get("n"))],
                  "avg_us": round(avg_ms * 1e3, 2)}
-            if op["op"] == "mmq_q4k":
+            if op["op"].startswith("mmq"):
                 tops = wl.op_ops(i) / (avg_ms * 1e-3) / 1e12
                 e["tops"] = round(tops, 2)
                 e["frac_int8_peak"] = round(tops / INT8_PEAK_TOPS, 4)
@@ -644,7 +649,7 @@ def main(argv=None):
         entry = {"workload": wl.wl["name"], "ms_per_step": round(ms, 5),
                  "weight_bytes_per_step": wl.weight_bytes_step, "weight_copies": wl.ncopies,
                  "step_weight_GBps": round(step_rate, 1), "kernels": per_op, "quantize": quant}
-        if cfg == 4:
+        if prefill:
             tot_ops = sum(wl.op_ops(i) for i in range(len(wl.ops)))
             entry["step_int8_TOPS"] = round(tot_ops / (ms * 1e-3) / 1e12, 2)
         if cfg == main_cfg:

@@ -13,8 +13,10 @@
  *     1..8 (minfer decodes 2..8 tokens at once on this path), weight-streaming bound (minfer "The CUDA backend" 2.2 and 2.3,
  *     MMVQ; leone-cuda "CUDA kernel design": Q4_K and Q6_K GEMV, residual
  *     epilogue; cajeta "One model, start to last token" 4.1 and 4.2).
- *   - kq_mmq_q4k: the prefill matrix-matrix product over many tokens on the
- *     int8 matrix cores (minfer "The CUDA backend" 2.3, MMQ, and 3.2.6).
+ *   - kq_mmq_q4k / kq_mmq_q6k: the prefill matrix-matrix product over many
+ *     tokens on the int8 matrix cores (minfer "The CUDA backend" 2.3, MMQ,
+ *     and 3.2.6; cajeta "One model, start to last token" 3: Q4_K and Q6_K
+ *     tiles).
  *   - kq_rmsnorm_q8_1 / kq_swiglu_q8_1: producers that write the q8_1 blocks
  *     of their output themselves, so the GEMV that follows needs no separate
  *     quantisation launch (leone-cuda "CUDA kernel design": RMSNorm and
@@ -160,6 +162,25 @@ int kq_gemv_q6k(const void* w, const void* xq, float* y, const float* residual,
  * Same value per output as kq_gemv_q4k without a residual.
  */
 int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
+               void* stream);
+
+/*
+ * Q6_K x q8_1 matrix-matrix product for n tokens on the int8 matrix cores:
+ * the prefill product of the Q6_K tensors of a mixed Q4_K/Q6_K model (cajeta
+ * "One model, start to last token" 3: the value projection and the down
+ * projection of half the layers are Q6_K and run on their own tensor-core
+ * tile; minfer "The CUDA backend" 2.3: integer tile products, scales applied
+ * after the integer loop).
+ *   w    [m][k/256] Q6_K superblocks (210 bytes), 16-byte aligned; the row
+ *        stride need not be a multiple of 16.
+ *   xq   [n][k/32] q8_1 blocks, 16-byte aligned.
+ *   y    out: f32 [n][m], 4-byte aligned; must not overlap w or xq.
+ *   m >= 0, n >= 0, k > 0, k % 256 == 0, k <= KQ_MAX_K, n <= 65535*128;
+ *   w and xq are each smaller than 4 GiB (m*k/256*210 and n*k/32*36 bytes).
+ * Every int8 scale value (-128..127) is accepted.  Same value per output as
+ * kq_gemv_q6k without a residual, up to f32 rounding order.
+ */
+int kq_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
                void* stream);
 
 /*

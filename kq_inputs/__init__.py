@@ -233,6 +233,21 @@ WORKLOADS = {
             dict(op="gemv_q4k", label="v", w="v", x="x", m=1024, k=4096, batch=1),
         ],
     ),
+    # the Q6_K tensors of the same prefill (a Q4_K_M model keeps the value
+    # projection and the down projection of half its layers in Q6_K)
+    9: dict(
+        name="qwen2_7b_prefill_mmq_q6k_n2048",
+        tensors=[
+            ("v", "q6k", 512, 3584),
+            ("down", "q6k", 3584, 18944),
+            ("x_in", "act", 2048, 3584),
+            ("x_down", "act", 2048, 18944),
+        ],
+        ops=[
+            dict(op="mmq_q6k", label="v", w="v", x="x_in", m=512, k=3584, n=2048),
+            dict(op="mmq_q6k", label="down", w="down", x="x_down", m=3584, k=18944, n=2048),
+        ],
+    ),
 }
 
 

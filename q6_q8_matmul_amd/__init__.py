@@ -49,11 +49,12 @@ def lib() -> ctypes.CDLL:
         L.kq_gemv_q4k.argtypes = [p, p, p, p, i64, i64, i32, p]
         L.kq_gemv_q6k.argtypes = [p, p, p, p, i64, i64, i32, p]
         L.kq_mmq_q4k.argtypes = [p, p, p, i64, i64, i64, p]
+        L.kq_mmq_q6k.argtypes = [p, p, p, i64, i64, i64, p]
         L.kq_rmsnorm_q8_1.argtypes = [p, p, p, ctypes.c_float, p, p, i64, i64, p]
         L.kq_swiglu_q8_1.argtypes = [p, p, p, p, i64, i64, p]
         L.kq_gemv_q4k_seg.argtypes = [i32, p, p, p, p, p, i64, i32, p]
         for fn in (L.kq_quantize_q8_1, L.kq_gemv_q4k, L.kq_gemv_q6k, L.kq_mmq_q4k,
-                   L.kq_rmsnorm_q8_1, L.kq_swiglu_q8_1, L.kq_gemv_q4k_seg):
+                   L.kq_mmq_q6k, L.kq_rmsnorm_q8_1, L.kq_swiglu_q8_1, L.kq_gemv_q4k_seg):
             fn.restype = ctypes.c_int
         L.kq_last_error.argtypes = []
         L.kq_last_error.restype = ctypes.c_char_p
@@ -113,6 +114,10 @@ def kq_gemv_q6k(w, xq, y, residual, m: int, k: int, batch: int, stream=None) -> 
 
 def kq_mmq_q4k(w, xq, y, m: int, n: int, k: int, stream=None) -> None:
     _check(lib().kq_mmq_q4k(_ptr(w), _ptr(xq), _ptr(y), m, n, k, _stream(stream)))
+
+
+def kq_mmq_q6k(w, xq, y, m: int, n: int, k: int, stream=None) -> None:
+    _check(lib().kq_mmq_q6k(_ptr(w), _ptr(xq), _ptr(y), m, n, k, _stream(stream)))
 
 
 def kq_gemv_q4k_seg(w, m, y, residual, xq, k: int, batch: int, stream=None) -> None:
@@ -182,6 +187,15 @@ def mmq_q4k(w, xq, m: int, n: int, k: int, out=None, stream=None):
     _require_cuda(w, xq)
     y = out if out is not None else torch.empty((n, m), dtype=torch.float32, device=w.device)
     kq_mmq_q4k(w, xq, y, m, n, k, stream)
+    return y
+
+
+def mmq_q6k(w, xq, m: int, n: int, k: int, out=None, stream=None):
+    import torch
+
+    _require_cuda(w, xq)
+    y = out if out is not None else torch.empty((n, m), dtype=torch.float32, device=w.device)
+    kq_mmq_q6k(w, xq, y, m, n, k, stream)
     return y
 
 

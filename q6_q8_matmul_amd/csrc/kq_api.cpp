@@ -198,9 +198,8 @@ int kq_gemv_q6k(const void* w, const void* xq, float* y, const float* residual, 
                                             (hipStream_t)stream));
 }
 
-int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
-               void* stream) {
-    const char* fn = "kq_mmq_q4k";
+static int mmq_common(const char* fn, int sb_bytes, const void* w, const void* xq, float* y,
+                      int64_t m, int64_t n, int64_t k) {
     if (!w || !xq || !y)
         return fail(KQ_ERR_ARG, "%s: null pointer (w=%p xq=%p y=%p)", fn, w, xq, (void*)y);
     if (int rc = check_k(fn, k, 256)) return rc;
@@ -210,16 +209,32 @@ int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, in
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(y, 4))
         return fail(KQ_ERR_ARG, "%s: misaligned pointer (w=%p xq=%p need 16, y=%p needs 4)", fn, w,
                     xq, (void*)y);
-    const int64_t wbytes = m * (k / 256) * 144, xbytes = n * (k / 32) * 36;
+    const int64_t wbytes = m * (k / 256) * sb_bytes, xbytes = n * (k / 32) * 36;
     if (wbytes >= (1LL << 32) || xbytes >= (1LL << 32))
         return fail(KQ_ERR_ARG, "%s: w (%lld bytes) or xq (%lld bytes) is 4 GiB or larger", fn,
                     (long long)wbytes, (long long)xbytes);
     const int64_t yn = n * m * 4;
     if (overlap(y, yn, w, wbytes) || overlap(y, yn, xq, xbytes))
         return fail(KQ_ERR_ARG, "%s: output y=%p overlaps an input (w=%p, xq=%p)", fn, (void*)y, w, xq);
+    return KQ_OK;
+}
+
+int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
+               void* stream) {
+    const char* fn = "kq_mmq_q4k";
+    if (int rc = mmq_common(fn, 144, w, xq, y, m, n, k)) return rc;
     if (m == 0 || n == 0) return ok();
     if (int rc = check_device(fn, nullptr)) return rc;
     return launched(fn, kq::launch_mmq_q4k(w, xq, y, m, n, k, (hipStream_t)stream));
+}
+
+int kq_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
+               void* stream) {
+    const char* fn = "kq_mmq_q6k";
+    if (int rc = mmq_common(fn, 210, w, xq, y, m, n, k)) return rc;
+    if (m == 0 || n == 0) return ok();
+    if (int rc = check_device(fn, nullptr)) return rc;
+    return launched(fn, kq::launch_mmq_q6k(w, xq, y, m, n, k, (hipStream_t)stream));
 }
 
 static int producer_sizes(const char* fn, int64_t rows, int64_t n) {

@@ -12,7 +12,8 @@
 //
 // Tiling: a workgroup (4 wavefronts, 2 x 2) computes 128 weight rows x 128
 // tokens; each wavefront a 64 x 64 block of four 32 x 32 MFMA tiles.  The K
-// loop walks one superblock (256 values, 8 q8_1 blocks) at a time:
+// loop walks one superblock (256 values, 8 q8_1 blocks) at a time, every
+// global load of a stage issued before the first LDS write:
 //   * raw Q4_K superblocks of the 128 rows -> LDS (16-byte loads);
 //     per row and sub-block the f32 pair (D, -Mn) -> LDS;
 //   * q8_1 blocks of the 128 tokens -> LDS as int8 codes (rows padded to
@@ -76,46 +77,73 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
     for (int sb = 0; sb < S; ++sb) {
-        // ---- stage raw weights: 128 rows x 9 chunks of 16 bytes
-        for (int idx = tid; idx < BM * 9; idx += 256) {
-            const int r = idx / 9, ch = idx - r * 9;
-            const int gr = min(m0 + r, M - 1);
-            const uint4 v = *(const uint4*)(w + (int64_t)gr * row_bytes + (int64_t)sb * kQ4KBytes + 16 * ch);
-            *(uint4*)(sm.wraw + r * kQ4KBytes + 16 * ch) = v;
-        }
-        // ---- (D, Mn) per row and sub-block, from the header
-        if (tid < BM) {
-            const int gr = min(m0 + tid, M - 1);
-            const uint4 hd = *(const uint4*)(w + (int64_t)gr * row_bytes + (int64_t)sb * kQ4KBytes);
-            const float d = half_bits_to_float(hd.x), dmin = half_bits_to_float(hd.x >> 16);
-            const uint32_t lowS = hd.y & 0x3f3f3f3fu, lowM = hd.z & 0x3f3f3f3fu;
-            const uint32_t hiS = (hd.w & 0x0f0f0f0fu) | ((hd.y >> 2) & 0x30303030u);
-            const uint32_t hiM = ((hd.w >> 4) & 0x0f0f0f0fu) | ((hd.z >> 2) & 0x30303030u);
+        // ---- staging, every global load issued before the first LDS write.
+        // Weights: two threads per row; thread (row, e) takes the 16-byte
+        // chunks e, e+2, ... of the row's 144-byte superblock (9 chunks); the
+        // even thread also decodes the header chunk into (D, -Mn) per
+        // sub-block.  Activations: 128 tokens x 8 q8_1 blocks, four (token,
+        // block) pairs per thread.
+        {
+            // recompute the staging addresses every superblock: kept live
+            // across the MFMA loop they would cost registers it needs
+            int ts = tid;
+            asm volatile("" : "+v"(ts));
+            const int rr = ts >> 1, e = ts & 1;
+            const int gr = min(m0 + rr, M - 1);
+            const uint8_t* p = w + (int64_t)gr * row_bytes + (int64_t)sb * kQ4KBytes;
+            uint4 cw[5];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t s4 = j < 4 ? lowS : hiS, m4 = j < 4 ? lowM : hiM;
-                const int sh = 8 * (j & 3);
-                sm.dsc[j][tid] = d * (float)((s4 >> sh) & 0xff);
-                sm.nmn[j][tid] = -(dmin * (float)((m4 >> sh) & 0xff));
+            for (int c = 0; c < 5; ++c) {
+                const int ch = e + 2 * c;
+                if (ch < 9) cw[c] = load16(p + 16 * ch);
             }
-        }
-        // ---- activations: 128 tokens x 8 q8_1 blocks
-        for (int idx = tid; idx < BN * 8; idx += 256) {
-            const int t = idx >> 3, j = idx & 7;
-            const int gt = min(n0 + t, N - 1);
-            const uint32_t* blk = (const uint32_t*)(xq + ((int64_t)gt * nb_row + sb * 8 + j) * kQ81Bytes);
-            uint32_t c[8];
+            uint4 c0[4], c1[4];
+            uint32_t hd[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) c[i] = blk[1 + i];
-            int s = 0;
+            for (int i = 0; i < 4; ++i) {
+                const int idx = ts + 256 * i;
+                const int t = idx >> 3, j = idx & 7;
+                const int gt = min(n0 + t, N - 1);
+                const uint8_t* blk = xq + ((int64_t)gt * nb_row + sb * 8 + j) * kQ81Bytes;
+                hd[i] = *(const uint32_t*)blk;
+                c0[i] = load16(blk + 4);
+                c1[i] = load16(blk + 20);
+            }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) s = dot4(c[i], 0x01010101u, s);
-            const float d8 = half_bits_to_float(blk[0]);
-            uint4* dst = (uint4*)(sm.codes + t * kCodeStride + 32 * j);
-            dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
-            dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
-            sm.d8[t * kTokStride + j] = d8;
-            sm.z[t * kTokStride + j] = d8 * (float)s;
+            for (int c = 0; c < 5; ++c) {
+                const int ch = e + 2 * c;
+                if (ch < 9) *(uint4*)(sm.wraw + rr * kQ4KBytes + 16 * ch) = cw[c];
+            }
+            if (e == 0) {   // (D, Mn) per sub-block from the header chunk
+                const uint4 hdr = cw[0];
+                const float d = half_bits_to_float(hdr.x), dmin = half_bits_to_float(hdr.x >> 16);
+                const uint32_t lowS = hdr.y & 0x3f3f3f3fu, lowM = hdr.z & 0x3f3f3f3fu;
+                const uint32_t hiS = (hdr.w & 0x0f0f0f0fu) | ((hdr.y >> 2) & 0x30303030u);
+                const uint32_t hiM = ((hdr.w >> 4) & 0x0f0f0f0fu) | ((hdr.z >> 2) & 0x30303030u);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t s4 = j < 4 ? lowS : hiS, m4 = j < 4 ? lowM : hiM;
+                    const int sh = 8 * (j & 3);
+                    sm.dsc[j][rr] = d * (float)((s4 >> sh) & 0xff);
+                    sm.nmn[j][rr] = -(dmin * (float)((m4 >> sh) & 0xff));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int idx = tid + 256 * i;
+                const int t = idx >> 3, j = idx & 7;
+                const uint32_t cc[8] = {c0[i].x, c0[i].y, c0[i].z, c0[i].w,
+                                        c1[i].x, c1[i].y, c1[i].z, c1[i].w};
+                int sum = 0;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) sum = dot4(cc[q], 0x01010101u, sum);
+                const float d8 = half_bits_to_float(hd[i]);
+                uint4* dst = (uint4*)(sm.codes + t * kCodeStride + 32 * j);
+                dst[0] = c0[i];
+                dst[1] = c1[i];
+                sm.d8[t * kTokStride + j] = d8;
+                sm.z[t * kTokStride + j] = d8 * (float)sum;
+            }
         }
         __syncthreads();
 

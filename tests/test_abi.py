@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "kq_quantize_q8_1", "kq_gemv_q4k", "kq_gemv_q6k", "kq_mmq_q4k",
+        "kq_quantize_q8_1", "kq_gemv_q4k", "kq_gemv_q6k", "kq_mmq_q4k", "kq_mmq_q6k",
         "kq_rmsnorm_q8_1", "kq_swiglu_q8_1", "kq_gemv_q4k_seg", "kq_last_error",
         "kq_abi_version"])
 
@@ -100,6 +100,7 @@ def test_gemv_rejects(kq, fn, args, needle):
     assert fn in kq.kq_last_error()
 
 
+@pytest.mark.parametrize("fn", ["kq_mmq_q4k", "kq_mmq_q6k"])
 @pytest.mark.parametrize("args,needle", [
     ((None, X, Y, 8, 8, 256, None), "null pointer"),
     ((W, X, Y, 8, 8, 100, None), "k=100"),
@@ -112,10 +113,17 @@ def test_gemv_rejects(kq, fn, args, needle):
     ((W, X, Y, 1 << 24, 8, 65536, None), "4 GiB"),
     ((W, X, Y, 8, 1 << 20, 65536, None), "4 GiB"),
 ])
-def test_mmq_rejects(kq, args, needle):
-    rc = kq.lib().kq_mmq_q4k(*args)
+def test_mmq_rejects(kq, fn, args, needle):
+    rc = getattr(kq.lib(), fn)(*args)
     assert rc == kq.KQ_ERR_ARG, kq.kq_last_error()
     assert needle in kq.kq_last_error()
+    assert fn in kq.kq_last_error()
+
+
+def test_mmq_q6k_size_guard_uses_its_block_size(kq):
+    # 100000 rows x 65536: 4.9e9 bytes of Q6_K (rejected), 3.4e9 of Q4_K
+    rc = kq.lib().kq_mmq_q6k(W, X, Y, 100000, 8, 65536, None)
+    assert rc == kq.KQ_ERR_ARG and "4 GiB" in kq.kq_last_error()
 
 
 def test_empty_inputs_launch_nothing(kq):
@@ -126,6 +134,8 @@ def test_empty_inputs_launch_nothing(kq):
     assert L.kq_gemv_q6k(W, X, Y, None, 0, 256, 4, None) == kq.KQ_OK
     assert L.kq_mmq_q4k(W, X, Y, 0, 16, 256, None) == kq.KQ_OK
     assert L.kq_mmq_q4k(W, X, Y, 16, 0, 256, None) == kq.KQ_OK
+    assert L.kq_mmq_q6k(W, X, Y, 0, 16, 256, None) == kq.KQ_OK
+    assert L.kq_mmq_q6k(W, X, Y, 16, 0, 256, None) == kq.KQ_OK
 
 
 def test_binding_raises_with_message(kq):

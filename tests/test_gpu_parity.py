@@ -206,17 +206,62 @@ def test_gemv_deterministic(kq, kind):
 # ----------------------------------------------------------------- MMQ -----
 
 MMQ_SHAPES = [(1, 1, 256), (5, 3, 512), (128, 128, 256), (200, 150, 1024), (129, 257, 768),
-              (300, 64, 3584), (64, 300, 2048)]
+              (300, 64, 3584), (64, 300, 2048), (131, 70, 18944)]
+MMQ_CASES = [(kind, *shape) for kind in ("q4k", "q6k") for shape in MMQ_SHAPES]
 
 
-@pytest.mark.parametrize("m,n,k", MMQ_SHAPES, ids=[f"m{m}-n{n}-k{k}" for m, n, k in MMQ_SHAPES])
-def test_mmq_full(kq, m, n, k):
-    say(f"mmq m={m} n={n} k={k}")
-    w, x, _ = random_case(m + 3 * n + k, "q4k", m, k, n)
+def mmq(kq, kind):
+    return kq.mmq_q4k if kind == "q4k" else kq.mmq_q6k
+
+
+@pytest.mark.parametrize("kind,m,n,k", MMQ_CASES, ids=[f"{c[0]}-m{c[1]}-n{c[2]}-k{c[3]}" for c in MMQ_CASES])
+def test_mmq_full(kq, kind, m, n, k):
+    say(f"mmq {kind} m={m} n={n} k={k}")
+    w, x, _ = random_case(m + 3 * n + k, kind, m, k, n)
     xq = oracle.quantize_q8_1(x)
-    y_ref, den = oracle.matmul("q4k", w, xq, m, n, k)
-    y = host(kq.mmq_q4k(dev(w), dev(xq), m, n, k))
-    check_close(y, y_ref, den, f"mmq m{m} n{n} k{k}")
+    y_ref, den = oracle.matmul(kind, w, xq, m, n, k)
+    y = host(mmq(kq, kind)(dev(w), dev(xq), m, n, k))
+    check_close(y, y_ref, den, f"mmq {kind} m{m} n{n} k{k}")
+
+
+def _q6k_extreme(m, k, rng, scale_choice, code_choice):
+    """Q6_K bytes with chosen int8 scales and 6-bit codes (placed at the
+    format's byte offsets: ql nibbles and qh bit pairs of every code equal)."""
+    s = k // 256
+    w = np.zeros((m, s, 210), dtype=np.uint8)
+    q = rng.choice(np.array(code_choice, dtype=np.uint8), size=(m, s, 1))
+    w[:, :, 0:128] = (q & 15) * 17                                  # both nibbles
+    w[:, :, 128:192] = ((q >> 4) & 3) * 0x55                        # all four bit pairs
+    w[:, :, 192:208] = rng.choice(np.array(scale_choice, dtype=np.int16), size=(m, s, 16)).astype(np.int8).view(np.uint8)
+    w[:, :, 208:210] = np.frombuffer(np.float16(0.25).tobytes(), dtype=np.uint8)
+    return w.reshape(m, s * 210)
+
+
+@pytest.mark.parametrize("case", ["max_product", "min_product", "full_range"])
+def test_mmq_q6k_extreme_scales(kq, case):
+    """Scales at the ends of the int8 range with the extreme codes: the
+    products sc*(q-32) reach 4096 and -4064, and the 32-value integer dots
+    reach 2^24 - 2^17 (every q8 code at +-127)."""
+    m, n, k = 160, 40, 1024
+    rng = np.random.default_rng({"max_product": 1, "min_product": 2, "full_range": 3}[case])
+    if case == "max_product":       # sc = -128, q = 0: (q-32)*sc = 4096
+        w = _q6k_extreme(m, k, rng, [-128], [0])
+    elif case == "min_product":     # sc = 127, q = 0: -4064; sc = -128, q = 63: -3968
+        w = _q6k_extreme(m, k, rng, [127, -128], [0, 63])
+    else:
+        w = _q6k_extreme(m, k, rng, list(range(-128, 128)), list(range(64)))
+        w.reshape(m, k // 256, 210)[:, :, 0:192] = rng.integers(0, 256, (m, k // 256, 192), dtype=np.uint8)
+    say(f"mmq q6k extreme scales ({case}) m={m} n={n} k={k}")
+    x = np.where(rng.random((n, k)) < 0.5, 1.0, -1.0).astype(np.float32)
+    x[0], x[1] = 1.0, -1.0   # every code +127 / -127: the largest dots
+    if case == "full_range":
+        x[2: n // 2] *= rng.standard_normal((n // 2 - 2, k)).astype(np.float32)
+    xq = oracle.quantize_q8_1(x)
+    y_ref, den = oracle.matmul("q6k", w, xq, m, n, k)
+    y = host(kq.mmq_q6k(dev(w), dev(xq), m, n, k))
+    check_close(y, y_ref, den, f"mmq q6k {case}")
+    g = host(kq.gemv_q6k(dev(w), dev(xq[:4]), m, k, 4))
+    check_close(g, y_ref[:4], den[:4], f"gemv q6k {case}")
 
 
 def _sample_pairs(m, n, rng, nrand=1500):
@@ -232,47 +277,55 @@ def _sample_pairs(m, n, rng, nrand=1500):
 MMQ_OPS = list(range(len(WORKLOADS[4]["ops"])))
 
 
-@pytest.mark.parametrize("i", MMQ_OPS, ids=[WORKLOADS[4]["ops"][i]["label"] for i in MMQ_OPS])
-def test_mmq_prefill_sampled(kq, i):
-    op = WORKLOADS[4]["ops"][i]
+PREFILL_OPS = [(c, i) for c in (4, 9) for i in range(len(WORKLOADS[c]["ops"]))]
+
+
+@pytest.mark.parametrize("cfg,i", PREFILL_OPS,
+                         ids=[f"cfg{c}-{WORKLOADS[c]['ops'][i]['label']}" for c, i in PREFILL_OPS])
+def test_mmq_prefill_sampled(kq, cfg, i):
+    op = WORKLOADS[cfg]["ops"][i]
+    kind = op["op"][-3:]
     m, n, k = op["m"], op["n"], op["k"]
-    say(f"mmq cfg4 {op['label']} m={m} n={n} k={k} (sampled)")
-    w = tensor(4, op["w"])
-    x = tensor(4, op["x"])
+    say(f"mmq {kind} cfg{cfg} {op['label']} m={m} n={n} k={k} (sampled)")
+    w = tensor(cfg, op["w"])
+    x = tensor(cfg, op["x"])
     xq_ref = oracle.quantize_q8_1(x)
     xd = dev(x)
     xq = kq.quantize_q8_1(xd)              # the path as the bench runs it
     assert np.array_equal(host(xq), xq_ref)
-    y = host(kq.mmq_q4k(dev(w), xq, m, n, k))
+    y = host(mmq(kq, kind)(dev(w), xq, m, n, k))
     tok, row = _sample_pairs(m, n, np.random.default_rng(i))
-    y_ref, den = oracle.matmul_pairs("q4k", w, xq_ref, m, n, k, tok, row)
-    check_close(y[tok, row], y_ref, den, f"cfg4 {op['label']} ({tok.size} outputs)")
+    y_ref, den = oracle.matmul_pairs(kind, w, xq_ref, m, n, k, tok, row)
+    check_close(y[tok, row], y_ref, den, f"cfg{cfg} {op['label']} ({tok.size} outputs)")
     assert np.all(np.isfinite(y))
 
 
-def test_mmq_matches_gemv_columns(kq):
+@pytest.mark.parametrize("kind", ["q4k", "q6k"])
+def test_mmq_matches_gemv_columns(kq, kind):
     m, n, k = 777, 5, 4096
-    say(f"mmq vs gemv m={m} n={n} k={k}")
-    w, x, _ = random_case(99, "q4k", m, k, n)
+    say(f"mmq {kind} vs gemv m={m} n={n} k={k}")
+    w, x, _ = random_case(99, kind, m, k, n)
     xq = oracle.quantize_q8_1(x)
     wd, xd = dev(w), dev(xq)
-    y = host(kq.mmq_q4k(wd, xd, m, n, k))
-    y_ref, den = oracle.matmul("q4k", w, xq, m, n, k)
+    y = host(mmq(kq, kind)(wd, xd, m, n, k))
+    y_ref, den = oracle.matmul(kind, w, xq, m, n, k)
+    gemv = kq.gemv_q4k if kind == "q4k" else kq.gemv_q6k
     for t in range(n):
-        g = host(kq.gemv_q4k(wd, xd[t:t + 1], m, k, 1))[0]
+        g = host(gemv(wd, xd[t:t + 1], m, k, 1))[0]
         check_close(g, y_ref[t], den[t], f"gemv token {t}")
         check_close(y[t], y_ref[t], den[t], f"mmq token {t}")
 
 
-def test_mmq_deterministic(kq):
+@pytest.mark.parametrize("kind", ["q4k", "q6k"])
+def test_mmq_deterministic(kq, kind):
     m, n, k = 512, 256, 3584
-    say(f"mmq determinism m={m} n={n} k={k}")
-    w, x, _ = random_case(6, "q4k", m, k, n)
+    say(f"mmq {kind} determinism m={m} n={n} k={k}")
+    w, x, _ = random_case(6, kind, m, k, n)
     xq = oracle.quantize_q8_1(x)
     wd, xd = dev(w), dev(xq)
-    a = host(kq.mmq_q4k(wd, xd, m, n, k))
+    a = host(mmq(kq, kind)(wd, xd, m, n, k))
     for _ in range(3):
-        assert np.array_equal(a, host(kq.mmq_q4k(wd, xd, m, n, k)))
+        assert np.array_equal(a, host(mmq(kq, kind)(wd, xd, m, n, k)))
 
 
 # ------------------------------------------------------ error handling ------
@@ -288,6 +341,8 @@ def test_bad_arguments_launch_nothing(kq):
         lambda: kq.kq_gemv_q4k(wd, xq, y, None, 64, 512, 9),
         lambda: kq.kq_gemv_q6k(wd, xq, y, y[:, 1:], 64, 512, 2),
         lambda: kq.kq_mmq_q4k(wd, xq, wd, 64, 2, 512),
+        lambda: kq.kq_mmq_q6k(wd, xq, wd, 64, 2, 512),
+        lambda: kq.kq_mmq_q6k(wd, xq, y, 64, 2, 500),
     ):
         with pytest.raises(kq.KQError):
             call()
