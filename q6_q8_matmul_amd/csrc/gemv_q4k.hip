@@ -56,10 +56,18 @@ struct Slice {      // one lane's share of one superblock of one row
 // LDS layout of one staged column (schunk superblocks):
 //   codes [schunk][256]   quad 4r + t (16 bytes) = the slice lane t reads as
 //                         its r-th block: r = 0, 1, 2, 3 <-> blocks 2c, 2c+1,
-//                         2c+4, 2c+5, values 16h..16h+15;
-//   slot  [schunk][4][8]  per lane t: d8 of its four blocks, then
-//                         d8 * (sum of the slice's 16 codes) for each.
+//                         2c+4, 2c+5, values 16h..16h+15; stored at quad
+//                         4(r ^ (sb & 3)) + t of superblock sb;
+//   d8p   [schunk][4]     float4 per lane t: d8 of its four blocks;
+//   zp    [schunk][4]     float4 per lane t: d8 * (sum of the slice's 16
+//                         codes) for each.
+// The sixteen lanes that one LDS cycle serves read superblocks sb .. sb+3 at
+// the same quad; the xor gives them four different quads, so each 16-byte
+// read touches 16 distinct bank groups (a 256-byte stride alone puts all
+// four superblocks on the same banks).
 constexpr int kLdsPerSb = 256 + 4 * 8 * 4;
+
+__device__ __forceinline__ int swz(int sb) { return 4 * (sb & 3); }
 
 __device__ __forceinline__ int quad_of(int jj) {   // slice r of lane 2c (h = 0) of block jj
     const int hiA = jj >> 2, c = (jj >> 1) & 1, e = jj & 1;
@@ -67,48 +75,51 @@ __device__ __forceinline__ int quad_of(int jj) {   // slice r of lane 2c (h = 0)
 }
 
 // Stage blocks [j0, j0 + nbc) of every column (nbc a multiple of 8): one
-// thread per q8_1 block, the loads of U blocks in flight before any is used.
-// Ends with a barrier.
-template <int BATCH, int NT>
+// thread per (column, q8_1 block), the loads of U blocks per thread in flight
+// before any is used.  Ends with a barrier.
+template <int BATCH, int NT, int U>
 __device__ __forceinline__ void stage_activation(const uint8_t* __restrict__ xq, int nb_row,
                                                  int j0, int nbc, int schunk, uint8_t* lds) {
-    constexpr int U = 2;
     uint8_t* codes = lds;
-    float* slots = (float*)(lds + BATCH * schunk * 256);
+    float* d8p = (float*)(lds + BATCH * schunk * 256);
+    float* zp = d8p + BATCH * schunk * 16;
+    const int total = BATCH * nbc;
+    for (int base = 0; base < total; base += NT * U) {
+        uint32_t c[U][9];
 #pragma unroll
-    for (int bb = 0; bb < BATCH; ++bb) {
-        const uint32_t* col = (const uint32_t*)(xq + ((int64_t)bb * nb_row + j0) * kQ81Bytes);
-        for (int base = 0; base < nbc; base += NT * U) {
-            uint32_t c[U][9];
+        for (int i = 0; i < U; ++i) {
+            const int idx = base + i * NT + (int)threadIdx.x;
+            if (idx < total) {
+                const int bb = BATCH == 1 ? 0 : idx / nbc;
+                const int j = idx - bb * nbc;
+                const uint32_t* blk = (const uint32_t*)(xq + ((int64_t)bb * nb_row + j0 + j) * kQ81Bytes);
 #pragma unroll
-            for (int i = 0; i < U; ++i) {
-                const int j = base + i * NT + (int)threadIdx.x;
-                if (j < nbc) {
-#pragma unroll
-                    for (int e = 0; e < 9; ++e) c[i][e] = col[j * 9 + e];
-                }
+                for (int e = 0; e < 9; ++e) c[i][e] = blk[e];
             }
+        }
 #pragma unroll
-            for (int i = 0; i < U; ++i) {
-                const int j = base + i * NT + (int)threadIdx.x;
-                if (j < nbc) {
-                    const int sb = j >> 3, jj = j & 7;
-                    const float d8 = half_bits_to_float(c[i][0]);
-                    const int s0 = dot4(c[i][1], 0x01010101u, dot4(c[i][2], 0x01010101u,
-                                   dot4(c[i][3], 0x01010101u, dot4(c[i][4], 0x01010101u, 0))));
-                    const int s1 = dot4(c[i][5], 0x01010101u, dot4(c[i][6], 0x01010101u,
-                                   dot4(c[i][7], 0x01010101u, dot4(c[i][8], 0x01010101u, 0))));
-                    const int q0 = quad_of(jj);
-                    uint8_t* cs = codes + (bb * schunk + sb) * 256 + 16 * q0;
-                    *(uint4*)cs = make_uint4(c[i][1], c[i][2], c[i][3], c[i][4]);
-                    *(uint4*)(cs + 16) = make_uint4(c[i][5], c[i][6], c[i][7], c[i][8]);
-                    const int r = q0 >> 2, t0 = q0 & 3;   // slice index and lane (h = 0)
-                    float* sl = slots + ((bb * schunk + sb) * 4 + t0) * 8;
-                    sl[r] = d8;
-                    sl[4 + r] = d8 * (float)s0;
-                    sl[8 + r] = d8;                       // lane t0 + 1 (h = 1)
-                    sl[12 + r] = d8 * (float)s1;
-                }
+        for (int i = 0; i < U; ++i) {
+            const int idx = base + i * NT + (int)threadIdx.x;
+            if (idx < total) {
+                const int bb = BATCH == 1 ? 0 : idx / nbc;
+                const int j = idx - bb * nbc;
+                const int sb = j >> 3, jj = j & 7;
+                const float d8 = half_bits_to_float(c[i][0]);
+                const int s0 = dot4(c[i][1], 0x01010101u, dot4(c[i][2], 0x01010101u,
+                               dot4(c[i][3], 0x01010101u, dot4(c[i][4], 0x01010101u, 0))));
+                const int s1 = dot4(c[i][5], 0x01010101u, dot4(c[i][6], 0x01010101u,
+                               dot4(c[i][7], 0x01010101u, dot4(c[i][8], 0x01010101u, 0))));
+                const int q0 = quad_of(jj);
+                uint8_t* cs = codes + (bb * schunk + sb) * 256 + 16 * (q0 ^ swz(sb));
+                *(uint4*)cs = make_uint4(c[i][1], c[i][2], c[i][3], c[i][4]);
+                *(uint4*)(cs + 16) = make_uint4(c[i][5], c[i][6], c[i][7], c[i][8]);
+                const int r = q0 >> 2, t0 = q0 & 3;   // slice index and lane (h = 0)
+                float* dp = d8p + ((bb * schunk + sb) * 4 + t0) * 4;
+                float* zq = zp + ((bb * schunk + sb) * 4 + t0) * 4;
+                dp[r] = d8;
+                zq[r] = d8 * (float)s0;
+                dp[4 + r] = d8;                       // lane t0 + 1 (h = 1)
+                zq[4 + r] = d8 * (float)s1;
             }
         }
     }
@@ -137,17 +148,18 @@ __device__ __forceinline__ void compute_pass(const Slice (&s)[RPW], float (&acc)
                                              const uint8_t* lds, int schunk, int sl, int t) {
     // activation slices of this lane for every column: read once, used by all rows
     const uint8_t* codes = lds;
-    const float* slots = (const float*)(lds + BATCH * schunk * 256);
+    const float4* d8p = (const float4*)(lds + BATCH * schunk * 256);
+    const float4* zp = d8p + BATCH * schunk * 4;
     uint4 a[BATCH][4];
     float4 d8v[BATCH], dbq[BATCH];
+    const int x = swz(sl);
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
-        const uint8_t* cs = codes + (b * schunk + sl) * 256 + 16 * t;
+        const uint8_t* cs = codes + (b * schunk + sl) * 256;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) a[b][r] = *(const uint4*)(cs + 64 * r);
-        const float4* sp = (const float4*)(slots + ((b * schunk + sl) * 4 + t) * 8);
-        d8v[b] = sp[0];
-        dbq[b] = sp[1];
+        for (int r = 0; r < 4; ++r) a[b][r] = *(const uint4*)(cs + 16 * ((4 * r + t) ^ x));
+        d8v[b] = d8p[(b * schunk + sl) * 4 + t];
+        dbq[b] = zp[(b * schunk + sl) * 4 + t];
     }
     const uint32_t sh = 16u * (uint32_t)(t >> 1);   // byte 2c of the scale words
 #pragma unroll
@@ -319,7 +331,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __r
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) load_pass<RPW>(ring[d], rowp, 8 * d + grp, S, t);
 
-    stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
+    stage_activation<BATCH, 64 * WAVES, (BATCH == 1 ? 2 : 4)>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
 
     for (int p0 = 0; p0 < npass; p0 += DEPTH) {
 #pragma unroll
@@ -331,7 +343,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __r
                 if (pl == 0 && p > 0) {                    // uniform over the workgroup
                     __syncthreads();
                     const int kc = chunk * schunk;
-                    stage_activation<BATCH, 64 * WAVES>(xq, nb_row, kc * 8,
+                    stage_activation<BATCH, 64 * WAVES, (BATCH == 1 ? 2 : 4)>(xq, nb_row, kc * 8,
                                                         min(schunk, S - kc) * 8, schunk, smem);
                 }
                 if (8 * p + grp < S)   // lanes past the row end add nothing
@@ -393,7 +405,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_persistent(const Tab sg,
             }
         }
     }
-    stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, S * 8, schunk, smem);
+    stage_activation<BATCH, 64 * WAVES, 2>(xq, nb_row, 0, S * 8, schunk, smem);
     int gc = blockIdx.x, pc = 0;
     SegCursor cc = seg_start(sg, gc);
     for (int it0 = 0; it0 < nitems; it0 += DEPTH) {

@@ -52,17 +52,21 @@ struct Raw {            // one lane's raw dwords of one superblock of one row
 //                        pieces (block 4h+g, values 8q..8q+7) of g = 0, 1 in
 //                        bytes [16k, 16k+16) and of g = 2, 3 in
 //                        [128+16k, 128+16k+16), so the 8 lanes of a group read
-//                        8 distinct 16-byte bank quads;
+//                        8 distinct 16-byte bank quads; the two 128-byte
+//                        halves trade places in odd superblocks, so the two
+//                        groups that one LDS cycle serves (superblocks sb and
+//                        sb+1, 256 bytes apart) use different banks too;
 //   d8    [cap]          per block.
 constexpr int kLdsPerSb = 256 + 8 * 4;
+
+__device__ __forceinline__ int swz(int sb) { return 8 * (sb & 1); }   // in 16-byte units
 
 // Stage blocks [j0, j0 + nbc) of every column (nbc a multiple of 8): one
 // thread per q8_1 block, the loads of U blocks in flight before any is used.
 // Ends with a barrier.
-template <int BATCH, int NT>
+template <int BATCH, int NT, int U>
 __device__ __forceinline__ void stage_activation(const uint8_t* __restrict__ xq, int nb_row,
                                                  int j0, int nbc, int schunk, uint8_t* lds) {
-    constexpr int U = 2;
     const int cap = schunk * 8;
     uint8_t* codes = lds;
     float* d8s = (float*)(lds + BATCH * schunk * 256);
@@ -87,10 +91,11 @@ __device__ __forceinline__ void stage_activation(const uint8_t* __restrict__ xq,
                 const int bb = idx / nbc;
                 const int j = idx - bb * nbc;
                 const int sb = j >> 3, jj = j & 7, h = jj >> 2, g = jj & 3;
-                uint8_t* cs = codes + (bb * schunk + sb) * 256 + ((g < 2) ? 0 : 128) + 8 * (g & 1);
+                uint8_t* cs = codes + (bb * schunk + sb) * 256 + 8 * (g & 1);
+                const int u0 = ((g < 2) ? 0 : 8) ^ swz(sb);
 #pragma unroll
                 for (int q = 0; q < 4; ++q)   // 8-value piece q goes to lane 4h + q
-                    *(uint2*)(cs + 16 * (4 * h + q)) = make_uint2(c[i][1 + 2 * q], c[i][2 + 2 * q]);
+                    *(uint2*)(cs + 16 * (u0 + 4 * h + q)) = make_uint2(c[i][1 + 2 * q], c[i][2 + 2 * q]);
                 d8s[bb * cap + j] = half_bits_to_float(c[i][0]);
             }
         }
@@ -141,8 +146,8 @@ __device__ __forceinline__ void compute_pass(const Raw (&r)[RPW], float (&acc)[R
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
         const uint8_t* cs = codes + (b * schunk + sl) * 256;
-        const uint4 lo = *(const uint4*)(cs + 16 * k);
-        const uint4 hi = *(const uint4*)(cs + 128 + 16 * k);
+        const uint4 lo = *(const uint4*)(cs + 16 * (k ^ swz(sl)));
+        const uint4 hi = *(const uint4*)(cs + 16 * ((8 + k) ^ swz(sl)));
         a[b][0] = make_uint2(lo.x, lo.y);
         a[b][1] = make_uint2(lo.z, lo.w);
         a[b][2] = make_uint2(hi.x, hi.y);
@@ -258,7 +263,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __r
                 if (++pl == npass) { pl = 0; gl += gridDim.x; }
             }
         }
-        stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, S * 8, schunk, smem);
+        stage_activation<BATCH, 64 * WAVES, 2>(xq, nb_row, 0, S * 8, schunk, smem);
         int gc = blockIdx.x, pc = 0;
         for (int it0 = 0; it0 < nitems; it0 += DEPTH) {
 #pragma unroll
@@ -285,7 +290,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __r
         for (int d = 0; d < DEPTH; ++d)
             load_pass<RPW>(ring[d], w, row0, m, row_bytes, 8 * d + grp, S, h, q);
 
-        stage_activation<BATCH, 64 * WAVES>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
+        stage_activation<BATCH, 64 * WAVES, (BATCH >= 2 && BATCH <= 4 ? 4 : 2)>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
 
         for (int p0 = 0; p0 < npass; p0 += DEPTH) {
 #pragma unroll
@@ -297,7 +302,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __r
                     if (pl == 0 && p > 0) {
                         __syncthreads();
                         const int kc = chunk * schunk;
-                        stage_activation<BATCH, 64 * WAVES>(xq, nb_row, kc * 8, min(schunk, S - kc) * 8,
+                        stage_activation<BATCH, 64 * WAVES, (BATCH >= 2 && BATCH <= 4 ? 4 : 2)>(xq, nb_row, kc * 8, min(schunk, S - kc) * 8,
                                                             schunk, smem);
                     }
                     if (8 * p + grp < S)
