@@ -42,7 +42,6 @@
 #include "kq_device.h"
 
 #include <algorithm>
-#include <atomic>
 
 namespace kq {
 namespace gemv4 {
@@ -435,19 +434,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_persistent(const Tab sg,
     }
 }
 
-// Occupancy of a persistent kernel, asked once per instantiation.
-template <class K>
-int occupancy(K kern, int threads, size_t lds) {
-    static std::atomic<int> occ{0};
-    int o = occ.load(std::memory_order_relaxed);
-    if (o == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, threads, lds) != hipSuccess || o < 1)
-            o = 1;
-        occ.store(o, std::memory_order_relaxed);
-    }
-    return o;
-}
-
 // Persistent launch over the row groups of table `tab` (one tensor or a
 // segment table).
 template <int BATCH, int RPW, int DEPTH, int WAVES, class Tab>
@@ -455,7 +441,7 @@ hipError_t launch_persistent(const Tab& tab, const void* xq, int64_t k, int schu
                              int cus, int per_cu, hipStream_t stream) {
     if (tab.ngroups == 0) return hipSuccess;
     auto kern = gemv_q4k_persistent<BATCH, RPW, DEPTH, WAVES, Tab>;
-    const int o = occupancy(kern, 64 * WAVES, lds);
+    const int o = occupancy((const void*)kern, 64 * WAVES, lds);
     const int grid = std::min(tab.ngroups, cus * std::min(o, per_cu));
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WAVES), lds, stream, tab,
                        (const uint8_t*)xq, (int)(k / kQK), schunk);
@@ -524,9 +510,10 @@ hipError_t launch_gemv_q4k(const void* w, const void* xq, float* y, const float*
     // workgroups per CU for tall or long rows (gate|up 28672x4096: 12.3 us,
     // down 4096x14336: 9.4 us), else four wavefronts and four workgroups
     // (4096x4096: 4.8 us).  Batches 2-4 use the four-wavefront persistent
-    // form (QKV 6144x4096 at batch 4: 8.8 us) unless the activation only fits
-    // in several LDS pieces or needs more than 64 KB, where three passes in
-    // flight over eight wavefronts per row group work better.
+    // form (QKV 6144x4096 at batch 4: 8.2 us) unless the activation only fits
+    // in several LDS pieces or needs more than 64 KB, where one pass in
+    // flight over eight wavefronts per row group works best (down 4096x14336
+    // at batch 4: 14.6 us against 15.4 with three passes in flight).
     const int S = (int)(k / kQK);
     const int64_t s_round = (S + 7) & ~7;
     const int64_t whole = (int64_t)batch * kLdsPerSb * s_round;
@@ -537,7 +524,7 @@ hipError_t launch_gemv_q4k(const void* w, const void* xq, float* y, const float*
                            : launch_variant<1, 1, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 4, stream);
         case 2: return launch_variant<2, 1, 1, 4>(w, xq, y, residual, m, k, one_piece, cus, 6, stream);
         case 3: return launch_variant<3, 1, 1, 4>(w, xq, y, residual, m, k, one_piece, cus, 6, stream);
-        case 4: return whole > 65536 ? launch_variant<4, 1, 3, 8>(w, xq, y, residual, m, k, one_piece, cus, 0, stream)
+        case 4: return whole > 65536 ? launch_variant<4, 1, 1, 8>(w, xq, y, residual, m, k, one_piece, cus, 0, stream)
                                      : launch_variant<4, 1, 1, 4>(w, xq, y, residual, m, k, one_piece, cus, 6, stream);
         case 5: return wide<5>(w, xq, y, residual, m, k, whole, one_piece, cus, stream);
         case 6: return wide<6>(w, xq, y, residual, m, k, whole, one_piece, cus, stream);

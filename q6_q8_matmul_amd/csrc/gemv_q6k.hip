@@ -34,7 +34,6 @@
 #include "kq_device.h"
 
 #include <algorithm>
-#include <atomic>
 
 namespace kq {
 namespace gemv6 {
@@ -334,13 +333,7 @@ hipError_t launch_variant(const void* w, const void* xq, float* y, const float* 
     const int64_t ngroups = (m + rows_per_block - 1) / rows_per_block;
     if (persist_per_cu > 0 && schunk >= S) {
         auto kern = gemv_q6k_kernel<BATCH, RPW, DEPTH, WAVES, true>;
-        static std::atomic<int> occ{0};
-        int o = occ.load(std::memory_order_relaxed);
-        if (o == 0) {
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, 64 * WAVES, lds) != hipSuccess || o < 1)
-                o = 1;
-            occ.store(o, std::memory_order_relaxed);
-        }
+        const int o = occupancy((const void*)kern, 64 * WAVES, lds);
         const int64_t grid = std::min<int64_t>(ngroups, (int64_t)cus * std::min(o, persist_per_cu));
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WAVES), lds, stream,
                            (const uint8_t*)w, (const uint8_t*)xq, y, residual, (int)m, S, schunk);

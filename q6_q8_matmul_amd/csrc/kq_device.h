@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace kq {
 
 // Byte sizes of the block formats.
@@ -85,6 +87,32 @@ __device__ __forceinline__ void quantize_block8(float4 v, int j, uint32_t* __res
 
     blk[1 + j] = packed;
     if (j == 0) blk[0] = float_to_half_bits(d) | (float_to_half_bits(s) << 16);
+}
+
+// Workgroups of kernel `kern` that fit on one compute unit with `threads`
+// threads and `lds` bytes of dynamic LDS: asked once per (kernel, threads,
+// LDS size) and kept for the process; 1 if the query fails.  Persistent
+// launches size their grid with it (an over-full grid is still correct,
+// its extra workgroups just wait for a slot).
+inline int occupancy(const void* kern, int threads, size_t lds) {
+    struct Entry {
+        const void* kern;
+        int threads;
+        size_t lds;
+        int occ;
+    };
+    static std::mutex mu;
+    static Entry table[64];
+    static int n = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n; ++i)
+        if (table[i].kern == kern && table[i].threads == threads && table[i].lds == lds)
+            return table[i].occ;
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, threads, lds) != hipSuccess || o < 1)
+        o = 1;
+    if (n < 64) table[n++] = Entry{kern, threads, lds, o};
+    return o;
 }
 
 // Launchers (return the launch status).
