@@ -226,6 +226,42 @@ def dequant(kind: str, w: np.ndarray, m: int, k: int) -> np.ndarray:
     return out
 
 
+# Split Q6_K layout (cajeta "One model, start to last token" 2, residency
+# step 3: a Q6_K weight is split into a scale prefix and 208-byte bodies so the
+# kernels read it with aligned 16-byte loads).  Reading: the prefix is the
+# f16 super-scale d of every superblock g = row * S + s, in that order, zero
+# padded to a multiple of 16 bytes; body g is the superblock's bytes 0..207
+# (ql, qh and the 16 int8 scales) unchanged.  A byte permutation: no value
+# changes.
+
+def q6k_split_bytes(m: int, k: int) -> int:
+    """Size of the split layout of an ``m x k`` Q6_K matrix."""
+    g = m * (k // 256)
+    return (2 * g + 15) // 16 * 16 + 208 * g
+
+
+def q6k_split(w: np.ndarray, m: int, k: int) -> np.ndarray:
+    """Raw Q6_K ``uint8[m, (k/256)*210]`` -> the split layout (flat uint8)."""
+    g = m * (k // 256)
+    raw = np.ascontiguousarray(w, dtype=np.uint8).reshape(g, 210)
+    prefix = (2 * g + 15) // 16 * 16
+    out = np.zeros(prefix + 208 * g, dtype=np.uint8)
+    out[: 2 * g] = raw[:, 208:210].reshape(-1)
+    out[prefix:] = raw[:, :208].reshape(-1)
+    return out
+
+
+def q6k_unsplit(wr: np.ndarray, m: int, k: int) -> np.ndarray:
+    """The split layout -> raw Q6_K ``uint8[m, (k/256)*210]``."""
+    g = m * (k // 256)
+    wr = np.ascontiguousarray(wr, dtype=np.uint8).reshape(-1)
+    prefix = (2 * g + 15) // 16 * 16
+    raw = np.empty((g, 210), dtype=np.uint8)
+    raw[:, 208:210] = wr[: 2 * g].reshape(g, 2)
+    raw[:, :208] = wr[prefix: prefix + 208 * g].reshape(g, 208)
+    return raw.reshape(m, (k // 256) * 210)
+
+
 # --------------------------------------------------------------- matmul ----
 
 def matmul(kind: str, w: np.ndarray, xq: np.ndarray, m: int, n: int, k: int,
