@@ -19,8 +19,9 @@ The other workloads are measured the same way and reported under
 Qwen2-7B prefill MMQ at 2048 tokens (Q4_K gate/up 18944x3584, down
 3584x18944, QKV 4608x3584; Q6_K v 512x3584 and down 3584x18944), the fused
 producers RMSNorm -> q8_1 and SwiGLU -> q8_1
-at decode and prefill sizes next to a standalone quantisation, and separately
-stored q, k, v projections as three launches against one segmented launch.
+at decode and prefill sizes next to a standalone quantisation, separately
+stored q, k, v projections as three launches against one segmented launch,
+and the Q6_K launches on the raw layout against the split layout.
 
 ``roofline`` describes the dominant kernel of the step, kq_gemv_q4k: its
 algorithmic bytes per launch (weights + q8_1 activation + f32 output) over
@@ -348,6 +349,48 @@ def measure_segmented(cfg: int):
         out["one_segmented_launch" if seg else "separate_launches"] = {
             "us": round(us, 2), "weight_GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
     return {"workload": wl["name"], "weight_bytes": nbytes, "weight_copies": ncopy, **out}
+
+
+def measure_split(cfg: int):
+    """The Q6_K launches of workload cfg on the raw layout and on the split
+    layout (kq_repack_q6k once at load), each replayed as a HIP graph over
+    rotating weight copies."""
+    import torch
+
+    import q6_q8_matmul_amd as kq
+    from kq_inputs import WORKLOADS, tensor
+
+    wl = WORKLOADS[cfg]
+    out = []
+    for op in wl["ops"]:
+        m, k = op["m"], op["k"]
+        rows = op.get("batch", op.get("n"))
+        h = tensor(cfg, op["w"])
+        ncopy = copies_for(h.nbytes)
+        raw = [torch.from_numpy(h).cuda()]
+        raw += [raw[0].clone() for _ in range(ncopy - 1)]
+        split = [kq.repack_q6k(r, m, k) for r in raw]
+        xq = kq.quantize_q8_1(torch.from_numpy(tensor(cfg, op["x"])).cuda())
+        y = torch.empty((rows, m), dtype=torch.float32, device="cuda")
+        e = {"op": op["label"], "shape": [m, k, rows]}
+        for name, ws in (("raw", raw), ("split", split)):
+            if op["op"] == "gemv_q6k":
+                fn = kq.kq_gemv_q6k if name == "raw" else kq.kq_gemv_q6k_split
+                launch = lambda w, fn=fn: fn(w, xq, y, None, m, k, rows)
+            else:
+                fn = kq.kq_mmq_q6k if name == "raw" else kq.kq_mmq_q6k_split
+                launch = lambda w, fn=fn: fn(w, xq, y, m, rows, k)
+            it = iter(range(1 << 30))
+            us = _graph_time_ms(lambda: launch(ws[next(it) % ncopy]), per_graph=ncopy) * 1e3
+            e[f"{name}_us"] = round(us, 2)
+            if op["op"] == "gemv_q6k":
+                e[f"{name}_weight_GBps"] = round(h.nbytes / (us * 1e-6) / 1e9, 1)
+            else:
+                e[f"{name}_tops"] = round(2.0 * m * rows * k / (us * 1e-6) / 1e12, 1)
+        out.append(e)
+        del raw, split
+        torch.cuda.empty_cache()
+    return {"workload": wl["name"], "layouts": out}
 
 
 def measure(cfg: int, steps: int, warmup: int, use_graph: bool):
@@ -697,6 +740,10 @@ def main(argv=None):
             secondary[f"cfg{cfg}"] = entry
         del wl
         torch.cuda.empty_cache()
+        if cfg in (3, 9):
+            log(f"workload {cfg}: raw vs split Q6_K layout")
+            secondary[f"cfg{cfg}_split_layout"] = measure_split(cfg)
+            torch.cuda.empty_cache()
     if result is None:
         result = {"metric": METRIC, "secondary": secondary}
     elif secondary:

@@ -184,6 +184,47 @@ int kq_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n, in
                void* stream);
 
 /*
+ * The split Q6_K layout, made once at load by kq_repack_q6k (cajeta "One
+ * model, start to last token" 2, residency: a Q6_K weight is split into a
+ * scale prefix and 208-byte bodies so the kernels read it with aligned
+ * 16-byte loads).  For superblock g = row * (k/256) + s of an m x k matrix
+ * (G = m * k/256 superblocks):
+ *   bytes [2g, 2g+2)                f16 d of superblock g
+ *   bytes [2G, P)                   zero, P = 2G rounded up to a multiple of 16
+ *   bytes [P + 208g, P + 208g+208)  the superblock's bytes 0..207 unchanged
+ *                                   (ql, qh, the 16 int8 scales)
+ * Every body starts 16-byte aligned (the raw 210-byte superblocks start at
+ * 2 mod 4 every other time).  The values are unchanged: the split kernels
+ * give bitwise the same outputs as kq_gemv_q6k / kq_mmq_q6k on the raw bytes.
+ *
+ * kq_q6k_split_bytes: size of the split layout, P + 208*G; -1 when m or k is
+ * invalid (m < 0 or > KQ_MAX_ROWS, k not a positive multiple of 256 or
+ * > KQ_MAX_K).  Host only, no device access.
+ */
+int64_t kq_q6k_split_bytes(int64_t m, int64_t k);
+
+/*
+ * Raw Q6_K w [m][k/256] (16-byte aligned) -> the split layout in wr
+ * (kq_q6k_split_bytes(m, k) bytes, 16-byte aligned, caller-allocated, must
+ * not overlap w).  One launch on the stream; asynchronous like every call.
+ */
+int kq_repack_q6k(const void* w, void* wr, int64_t m, int64_t k, void* stream);
+
+/*
+ * kq_gemv_q6k on a weight in the split layout (wr, kq_q6k_split_bytes(m, k)
+ * bytes, 16-byte aligned).  Same arguments, rules and results otherwise.
+ */
+int kq_gemv_q6k_split(const void* wr, const void* xq, float* y, const float* residual,
+                      int64_t m, int64_t k, int32_t batch, void* stream);
+
+/*
+ * kq_mmq_q6k on a weight in the split layout.  Same arguments, rules and
+ * results otherwise (the 4 GiB limit applies to kq_q6k_split_bytes(m, k)).
+ */
+int kq_mmq_q6k_split(const void* wr, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
+                     void* stream);
+
+/*
  * RMSNorm of each row (optionally of x + res), times the gain g, written as
  * q8_1 blocks and optionally as f32 (leone-cuda "CUDA kernel design": RMSNorm
  * with a fixed reduction order and sqrtf, writing its q8_1 blocks; the

@@ -50,11 +50,17 @@ def lib() -> ctypes.CDLL:
         L.kq_gemv_q6k.argtypes = [p, p, p, p, i64, i64, i32, p]
         L.kq_mmq_q4k.argtypes = [p, p, p, i64, i64, i64, p]
         L.kq_mmq_q6k.argtypes = [p, p, p, i64, i64, i64, p]
+        L.kq_mmq_q6k_split.argtypes = [p, p, p, i64, i64, i64, p]
+        L.kq_gemv_q6k_split.argtypes = [p, p, p, p, i64, i64, i32, p]
+        L.kq_repack_q6k.argtypes = [p, p, i64, i64, p]
+        L.kq_q6k_split_bytes.argtypes = [i64, i64]
+        L.kq_q6k_split_bytes.restype = i64
         L.kq_rmsnorm_q8_1.argtypes = [p, p, p, ctypes.c_float, p, p, i64, i64, p]
         L.kq_swiglu_q8_1.argtypes = [p, p, p, p, i64, i64, p]
         L.kq_gemv_q4k_seg.argtypes = [i32, p, p, p, p, p, i64, i32, p]
         for fn in (L.kq_quantize_q8_1, L.kq_gemv_q4k, L.kq_gemv_q6k, L.kq_mmq_q4k,
-                   L.kq_mmq_q6k, L.kq_rmsnorm_q8_1, L.kq_swiglu_q8_1, L.kq_gemv_q4k_seg):
+                   L.kq_mmq_q6k, L.kq_mmq_q6k_split, L.kq_gemv_q6k_split, L.kq_repack_q6k,
+                   L.kq_rmsnorm_q8_1, L.kq_swiglu_q8_1, L.kq_gemv_q4k_seg):
             fn.restype = ctypes.c_int
         L.kq_last_error.argtypes = []
         L.kq_last_error.restype = ctypes.c_char_p
@@ -118,6 +124,23 @@ def kq_mmq_q4k(w, xq, y, m: int, n: int, k: int, stream=None) -> None:
 
 def kq_mmq_q6k(w, xq, y, m: int, n: int, k: int, stream=None) -> None:
     _check(lib().kq_mmq_q6k(_ptr(w), _ptr(xq), _ptr(y), m, n, k, _stream(stream)))
+
+
+def kq_mmq_q6k_split(wr, xq, y, m: int, n: int, k: int, stream=None) -> None:
+    _check(lib().kq_mmq_q6k_split(_ptr(wr), _ptr(xq), _ptr(y), m, n, k, _stream(stream)))
+
+
+def kq_gemv_q6k_split(wr, xq, y, residual, m: int, k: int, batch: int, stream=None) -> None:
+    _check(lib().kq_gemv_q6k_split(_ptr(wr), _ptr(xq), _ptr(y), _ptr(residual), m, k, batch,
+                                   _stream(stream)))
+
+
+def kq_repack_q6k(w, wr, m: int, k: int, stream=None) -> None:
+    _check(lib().kq_repack_q6k(_ptr(w), _ptr(wr), m, k, _stream(stream)))
+
+
+def kq_q6k_split_bytes(m: int, k: int) -> int:
+    return int(lib().kq_q6k_split_bytes(m, k))
 
 
 def kq_gemv_q4k_seg(w, m, y, residual, xq, k: int, batch: int, stream=None) -> None:
@@ -187,6 +210,37 @@ def mmq_q4k(w, xq, m: int, n: int, k: int, out=None, stream=None):
     _require_cuda(w, xq)
     y = out if out is not None else torch.empty((n, m), dtype=torch.float32, device=w.device)
     kq_mmq_q4k(w, xq, y, m, n, k, stream)
+    return y
+
+
+def repack_q6k(w, m: int, k: int, stream=None):
+    """Raw Q6_K weight (uint8 device tensor) -> a new tensor in the split layout."""
+    import torch
+
+    _require_cuda(w)
+    nbytes = kq_q6k_split_bytes(m, k)
+    if nbytes < 0:
+        raise KQError(f"repack_q6k: invalid m={m} or k={k}")
+    wr = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    kq_repack_q6k(w, wr, m, k, stream)
+    return wr
+
+
+def gemv_q6k_split(wr, xq, m: int, k: int, batch: int, residual=None, out=None, stream=None):
+    import torch
+
+    _require_cuda(wr, xq, residual)
+    y = out if out is not None else torch.empty((batch, m), dtype=torch.float32, device=wr.device)
+    kq_gemv_q6k_split(wr, xq, y, residual, m, k, batch, stream)
+    return y
+
+
+def mmq_q6k_split(wr, xq, m: int, n: int, k: int, out=None, stream=None):
+    import torch
+
+    _require_cuda(wr, xq)
+    y = out if out is not None else torch.empty((n, m), dtype=torch.float32, device=wr.device)
+    kq_mmq_q6k_split(wr, xq, y, m, n, k, stream)
     return y
 
 

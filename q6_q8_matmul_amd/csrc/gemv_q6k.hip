@@ -33,6 +33,8 @@
 // Q6_K GEMV with residual epilogue, fixed reduction order, no atomics).
 #include "kq_device.h"
 
+#include <type_traits>
+
 #include <algorithm>
 
 namespace kq {
@@ -44,6 +46,11 @@ struct Raw {            // one lane's raw dwords of one superblock of one row
     uint32_t h[3];      // qh
     uint32_t s[3];      // the half's 8 scale bytes (third dword only if misaligned)
     uint32_t dpar;      // f16 d in the low half, byte parity of the superblock in bit 16
+};
+
+struct RawS {           // the same share read from the split layout (aligned)
+    uint2 l, l2, h, s;  // ql (g = 0 / 2), ql (g = 1 / 3), qh, the half's 8 scale bytes
+    uint32_t d;         // f16 d in the low half
 };
 
 // LDS layout of one staged column (cap = 8 * schunk q8_1 blocks):
@@ -134,8 +141,59 @@ __device__ __forceinline__ void load_pass(Raw (&r)[RPW], const uint8_t* __restri
     }
 }
 
-template <int BATCH, int RPW>
-__device__ __forceinline__ void compute_pass(const Raw (&r)[RPW], float (&acc)[RPW][BATCH],
+// Split layout: superblock g = row * S + s has its 208-byte body at
+// wb + 208 g (16-byte aligned) and its d at wd[g].
+template <int RPW>
+__device__ __forceinline__ void load_pass(RawS (&r)[RPW], const uint8_t* __restrict__ wb,
+                                          const uint16_t* __restrict__ wd, int row0, int m, int S,
+                                          int sb, int h, int q) {
+    const int sbc = min(sb, S - 1);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int64_t g = (int64_t)min(row0 + i, m - 1) * S + sbc;
+        const uint8_t* p = wb + g * 208;
+        r[i].l = *(const uint2*)(p + 64 * h + 8 * q);
+        r[i].l2 = *(const uint2*)(p + 64 * h + 32 + 8 * q);
+        r[i].h = *(const uint2*)(p + 128 + 32 * h + 8 * q);
+        r[i].s = *(const uint2*)(p + 192 + 8 * h);
+        r[i].d = wd[g];
+    }
+}
+
+// One row's share of one superblock: the 8 code dwords, the scale dwords and
+// d, already aligned.
+struct Share {
+    uint32_t L0, L1, M0, M1, H0, H1, S0, S1;
+    float dq;
+};
+
+__device__ __forceinline__ Share share_of(const Raw& r) {
+    const uint32_t sh = (r.dpar >> 16) * 16u;   // 0 or 16 bits
+    Share z;
+    z.L0 = __builtin_amdgcn_alignbit(r.l[1], r.l[0], sh);
+    z.L1 = __builtin_amdgcn_alignbit(r.l[2], r.l[1], sh);
+    z.M0 = __builtin_amdgcn_alignbit(r.l2[1], r.l2[0], sh);
+    z.M1 = __builtin_amdgcn_alignbit(r.l2[2], r.l2[1], sh);
+    z.H0 = __builtin_amdgcn_alignbit(r.h[1], r.h[0], sh);
+    z.H1 = __builtin_amdgcn_alignbit(r.h[2], r.h[1], sh);
+    z.S0 = __builtin_amdgcn_alignbit(r.s[1], r.s[0], sh);
+    z.S1 = __builtin_amdgcn_alignbit(r.s[2], r.s[1], sh);
+    z.dq = half_bits_to_float(r.dpar) * 0.25f;
+    return z;
+}
+
+__device__ __forceinline__ Share share_of(const RawS& r) {
+    Share z;
+    z.L0 = r.l.x; z.L1 = r.l.y;
+    z.M0 = r.l2.x; z.M1 = r.l2.y;
+    z.H0 = r.h.x; z.H1 = r.h.y;
+    z.S0 = r.s.x; z.S1 = r.s.y;
+    z.dq = half_bits_to_float(r.d) * 0.25f;
+    return z;
+}
+
+template <int BATCH, int RPW, class R>
+__device__ __forceinline__ void compute_pass(const R (&r)[RPW], float (&acc)[RPW][BATCH],
                                              const uint8_t* lds, int schunk, int sl, int h, int q) {
     const uint8_t* codes = lds;
     const float* d8s = (const float*)(lds + BATCH * schunk * 256);
@@ -156,16 +214,10 @@ __device__ __forceinline__ void compute_pass(const Raw (&r)[RPW], float (&acc)[R
     }
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-        const uint32_t sh = (r[i].dpar >> 16) * 16u;   // 0 or 16 bits
-        const uint32_t L0 = __builtin_amdgcn_alignbit(r[i].l[1], r[i].l[0], sh);
-        const uint32_t L1 = __builtin_amdgcn_alignbit(r[i].l[2], r[i].l[1], sh);
-        const uint32_t M0 = __builtin_amdgcn_alignbit(r[i].l2[1], r[i].l2[0], sh);
-        const uint32_t M1 = __builtin_amdgcn_alignbit(r[i].l2[2], r[i].l2[1], sh);
-        const uint32_t H0 = __builtin_amdgcn_alignbit(r[i].h[1], r[i].h[0], sh);
-        const uint32_t H1 = __builtin_amdgcn_alignbit(r[i].h[2], r[i].h[1], sh);
-        const uint32_t S0 = __builtin_amdgcn_alignbit(r[i].s[1], r[i].s[0], sh);
-        const uint32_t S1 = __builtin_amdgcn_alignbit(r[i].s[2], r[i].s[1], sh);
-        const float dq = half_bits_to_float(r[i].dpar) * 0.25f;
+        const Share z = share_of(r[i]);
+        const uint32_t L0 = z.L0, L1 = z.L1, M0 = z.M0, M1 = z.M1, H0 = z.H0, H1 = z.H1;
+        const uint32_t S0 = z.S0, S1 = z.S1;
+        const float dq = z.dq;
         // scale of group g: signed byte 2g + (q >> 1) of the half's 8 scale bytes
         const uint32_t so = 8u * (uint32_t)(q >> 1);
         int sc[4];
@@ -225,8 +277,10 @@ __device__ __forceinline__ void finish_rows(float (&acc)[RPW][BATCH], float* y,
 // row groups blockIdx.x, blockIdx.x + gridDim.x, ...; the load ring runs
 // across group boundaries, so a wavefront's next rows are already in flight
 // while it finishes the current ones.
-template <int BATCH, int RPW, int DEPTH, int WAVES, bool PERSIST>
+// SPLIT: the weights are in the split layout, bodies at w and d at wd.
+template <int BATCH, int RPW, int DEPTH, int WAVES, bool PERSIST, bool SPLIT>
 __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __restrict__ w,
+                                                              const uint16_t* __restrict__ wd,
                                                               const uint8_t* __restrict__ xq,
                                                               float* y, const float* residual,
                                                               int m, int S, int schunk) {
@@ -248,7 +302,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __r
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) acc[i][b] = 0.0f;
 
-    Raw ring[DEPTH][RPW];
+    using R = std::conditional_t<SPLIT, RawS, Raw>;
+    R ring[DEPTH][RPW];
+    auto load = [&](R (&slot)[RPW], int row0, int sb) {
+        if constexpr (SPLIT)
+            load_pass<RPW>(slot, w, wd, row0, m, S, sb, h, q);
+        else
+            load_pass<RPW>(slot, w, row0, m, row_bytes, sb, S, h, q);
+    };
     if constexpr (PERSIST) {
         const int rows_per_group = WAVES * RPW;
         const int ngroups = (m + rows_per_group - 1) / rows_per_group;
@@ -258,7 +319,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __r
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             if (d < nitems) {
-                load_pass<RPW>(ring[d], w, (gl * WAVES + wave) * RPW, m, row_bytes, 8 * pl + grp, S, h, q);
+                load(ring[d], (gl * WAVES + wave) * RPW, 8 * pl + grp);
                 if (++pl == npass) { pl = 0; gl += gridDim.x; }
             }
         }
@@ -271,7 +332,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __r
                 if (it < nitems) {
                     if (8 * pc + grp < S) compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pc + grp, h, q);
                     if (it + DEPTH < nitems) {
-                        load_pass<RPW>(ring[d], w, (gl * WAVES + wave) * RPW, m, row_bytes, 8 * pl + grp, S, h, q);
+                        load(ring[d], (gl * WAVES + wave) * RPW, 8 * pl + grp);
                         if (++pl == npass) { pl = 0; gl += gridDim.x; }
                     }
                     if (++pc == npass) {
@@ -287,7 +348,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __r
         const int chunk_passes = schunk >> 3;
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d)
-            load_pass<RPW>(ring[d], w, row0, m, row_bytes, 8 * d + grp, S, h, q);
+            load(ring[d], row0, 8 * d + grp);
 
         stage_activation<BATCH, 64 * WAVES, (BATCH >= 2 && BATCH <= 4 ? 4 : 2)>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
 
@@ -307,7 +368,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __r
                     if (8 * p + grp < S)
                         compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pl + grp, h, q);
                     if (p + DEPTH < npass)
-                        load_pass<RPW>(ring[d], w, row0, m, row_bytes, 8 * (p + DEPTH) + grp, S, h, q);
+                        load(ring[d], row0, 8 * (p + DEPTH) + grp);
                 }
             }
         }
@@ -318,10 +379,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __r
 // Launch one variant.  `persist_per_cu` > 0 asks for the persistent form with
 // that many workgroups per compute unit (capped by occupancy); it is used
 // only when the whole activation fits in one LDS piece.
-template <int BATCH, int RPW, int DEPTH, int WAVES>
+template <int BATCH, int RPW, int DEPTH, int WAVES, bool SPLIT = false>
 hipError_t launch_variant(const void* w, const void* xq, float* y, const float* residual,
                           int64_t m, int64_t k, int lds_budget, int cus, int persist_per_cu,
-                          hipStream_t stream) {
+                          hipStream_t stream, const uint16_t* wd = nullptr) {
     const int S = (int)(k / kQK);
     const int per_sb = BATCH * kLdsPerSb;
     int schunk = (lds_budget / per_sb) & ~7;
@@ -332,42 +393,60 @@ hipError_t launch_variant(const void* w, const void* xq, float* y, const float* 
     const int rows_per_block = WAVES * RPW;
     const int64_t ngroups = (m + rows_per_block - 1) / rows_per_block;
     if (persist_per_cu > 0 && schunk >= S) {
-        auto kern = gemv_q6k_kernel<BATCH, RPW, DEPTH, WAVES, true>;
+        auto kern = gemv_q6k_kernel<BATCH, RPW, DEPTH, WAVES, true, SPLIT>;
         const int o = occupancy((const void*)kern, 64 * WAVES, lds);
         const int64_t grid = std::min<int64_t>(ngroups, (int64_t)cus * std::min(o, persist_per_cu));
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WAVES), lds, stream,
-                           (const uint8_t*)w, (const uint8_t*)xq, y, residual, (int)m, S, schunk);
+                           (const uint8_t*)w, wd, (const uint8_t*)xq, y, residual, (int)m, S, schunk);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((gemv_q6k_kernel<BATCH, RPW, DEPTH, WAVES, false>), dim3((unsigned)ngroups),
-                       dim3(64 * WAVES), lds, stream, (const uint8_t*)w, (const uint8_t*)xq, y,
+    hipLaunchKernelGGL((gemv_q6k_kernel<BATCH, RPW, DEPTH, WAVES, false, SPLIT>), dim3((unsigned)ngroups),
+                       dim3(64 * WAVES), lds, stream, (const uint8_t*)w, wd, (const uint8_t*)xq, y,
                        residual, (int)m, S, schunk);
     return hipGetLastError();
 }
 
 }  // namespace gemv6
 
-hipError_t launch_gemv_q6k(const void* w, const void* xq, float* y, const float* residual,
-                           int64_t m, int64_t k, int batch, int lds_limit, int cus,
-                           hipStream_t stream) {
-    using namespace gemv6;
-    (void)lds_limit;
+namespace gemv6 {
+template <bool SPLIT>
+hipError_t dispatch(const void* w, const uint16_t* wd, const void* xq, float* y,
+                    const float* residual, int64_t m, int64_t k, int batch, int cus,
+                    hipStream_t stream) {
     // Launch shape measured on MI355X over the 128256 x 4096 output head
     // (back-to-back launches on two rotating weight copies): two rows per
     // wavefront, one pass ahead, persistent grid of up to six workgroups per
     // compute unit -- 85 us at batch 1 (94 us for one workgroup per row
     // group), 124 us at batch 4 (160 us).
     switch (batch) {
-        case 1: return launch_variant<1, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
-        case 2: return launch_variant<2, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
-        case 3: return launch_variant<3, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
-        case 4: return launch_variant<4, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
-        case 5: return launch_variant<5, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
-        case 6: return launch_variant<6, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
-        case 7: return launch_variant<7, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
-        case 8: return launch_variant<8, 2, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 6, stream);
+        case 1: return launch_variant<1, 2, 1, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 6, stream, wd);
+        case 2: return launch_variant<2, 2, 1, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 6, stream, wd);
+        case 3: return launch_variant<3, 2, 1, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 6, stream, wd);
+        case 4: return launch_variant<4, 2, 1, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 6, stream, wd);
+        case 5: return launch_variant<5, 2, 1, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 6, stream, wd);
+        case 6: return launch_variant<6, 2, 1, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 6, stream, wd);
+        case 7: return launch_variant<7, 2, 1, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 6, stream, wd);
+        case 8: return launch_variant<8, 2, 1, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 6, stream, wd);
         default: return hipErrorInvalidValue;
     }
+}
+}  // namespace gemv6
+
+hipError_t launch_gemv_q6k(const void* w, const void* xq, float* y, const float* residual,
+                           int64_t m, int64_t k, int batch, int lds_limit, int cus,
+                           hipStream_t stream) {
+    (void)lds_limit;
+    return gemv6::dispatch<false>(w, nullptr, xq, y, residual, m, k, batch, cus, stream);
+}
+
+hipError_t launch_gemv_q6k_split(const void* wr, const void* xq, float* y, const float* residual,
+                                 int64_t m, int64_t k, int batch, int lds_limit, int cus,
+                                 hipStream_t stream) {
+    (void)lds_limit;
+    const int64_t G = m * (k / kQK);
+    const uint8_t* bodies = (const uint8_t*)wr + (2 * G + 15) / 16 * 16;
+    return gemv6::dispatch<true>(bodies, (const uint16_t*)wr, xq, y, residual, m, k, batch, cus,
+                                 stream);
 }
 
 }  // namespace kq

@@ -86,8 +86,17 @@ int check_k(const char* fn, int64_t k, int64_t mult) {
     return KQ_OK;
 }
 
+// Bytes of the split Q6_K layout of an m x k matrix: the f16 d prefix padded
+// to 16 bytes, then one 208-byte body per superblock.
+int64_t split_bytes(int64_t m, int64_t k) {
+    const int64_t g = m * (k / 256);
+    return (2 * g + 15) / 16 * 16 + 208 * g;
+}
+
+// wtotal >= 0: the weight buffer's size when it is not m*(k/256)*wbytes.
 int gemv_common(const char* fn, int wbytes, const void* w, const void* xq, float* y,
-                const float* residual, int64_t m, int64_t k, int32_t batch) {
+                const float* residual, int64_t m, int64_t k, int32_t batch,
+                int64_t wtotal = -1) {
     if (!w || !xq || !y)
         return fail(KQ_ERR_ARG, "%s: null pointer (w=%p xq=%p y=%p)", fn, w, xq, (void*)y);
     if (int rc = check_k(fn, k, 256)) return rc;
@@ -99,7 +108,7 @@ int gemv_common(const char* fn, int wbytes, const void* w, const void* xq, float
         return fail(KQ_ERR_ARG,
                     "%s: misaligned pointer (w=%p xq=%p need 16, y=%p residual=%p need 4)", fn, w,
                     xq, (void*)y, (const void*)residual);
-    const int64_t wn = m * (k / 256) * wbytes;
+    const int64_t wn = wtotal >= 0 ? wtotal : m * (k / 256) * wbytes;
     const int64_t xn = (int64_t)batch * (k / 32) * 36;
     const int64_t yn = (int64_t)batch * m * 4;
     if (overlap(y, yn, w, wn) || overlap(y, yn, xq, xn))
@@ -199,7 +208,7 @@ int kq_gemv_q6k(const void* w, const void* xq, float* y, const float* residual, 
 }
 
 static int mmq_common(const char* fn, int sb_bytes, const void* w, const void* xq, float* y,
-                      int64_t m, int64_t n, int64_t k) {
+                      int64_t m, int64_t n, int64_t k, bool split = false) {
     if (!w || !xq || !y)
         return fail(KQ_ERR_ARG, "%s: null pointer (w=%p xq=%p y=%p)", fn, w, xq, (void*)y);
     if (int rc = check_k(fn, k, 256)) return rc;
@@ -209,7 +218,8 @@ static int mmq_common(const char* fn, int sb_bytes, const void* w, const void* x
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(y, 4))
         return fail(KQ_ERR_ARG, "%s: misaligned pointer (w=%p xq=%p need 16, y=%p needs 4)", fn, w,
                     xq, (void*)y);
-    const int64_t wbytes = m * (k / 256) * sb_bytes, xbytes = n * (k / 32) * 36;
+    const int64_t wbytes = split ? split_bytes(m, k) : m * (k / 256) * sb_bytes;
+    const int64_t xbytes = n * (k / 32) * 36;
     if (wbytes >= (1LL << 32) || xbytes >= (1LL << 32))
         return fail(KQ_ERR_ARG, "%s: w (%lld bytes) or xq (%lld bytes) is 4 GiB or larger", fn,
                     (long long)wbytes, (long long)xbytes);
@@ -235,6 +245,49 @@ int kq_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n, in
     if (m == 0 || n == 0) return ok();
     if (int rc = check_device(fn, nullptr)) return rc;
     return launched(fn, kq::launch_mmq_q6k(w, xq, y, m, n, k, (hipStream_t)stream));
+}
+
+int kq_mmq_q6k_split(const void* wr, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
+                     void* stream) {
+    const char* fn = "kq_mmq_q6k_split";
+    if (int rc = mmq_common(fn, 210, wr, xq, y, m, n, k, true)) return rc;
+    if (m == 0 || n == 0) return ok();
+    if (int rc = check_device(fn, nullptr)) return rc;
+    return launched(fn, kq::launch_mmq_q6k_split(wr, xq, y, m, n, k, (hipStream_t)stream));
+}
+
+int64_t kq_q6k_split_bytes(int64_t m, int64_t k) {
+    if (m < 0 || m > KQ_MAX_ROWS || k <= 0 || k % 256 != 0 || k > KQ_MAX_K) return -1;
+    return split_bytes(m, k);
+}
+
+int kq_repack_q6k(const void* w, void* wr, int64_t m, int64_t k, void* stream) {
+    const char* fn = "kq_repack_q6k";
+    if (!w || !wr) return fail(KQ_ERR_ARG, "%s: null pointer (w=%p wr=%p)", fn, w, wr);
+    if (int rc = check_k(fn, k, 256)) return rc;
+    if (m < 0 || m > KQ_MAX_ROWS)
+        return fail(KQ_ERR_ARG, "%s: m=%lld out of range [0, %d]", fn, (long long)m, KQ_MAX_ROWS);
+    if (!aligned(w, 16) || !aligned(wr, 16))
+        return fail(KQ_ERR_ARG, "%s: misaligned pointer (w=%p wr=%p need 16)", fn, w, wr);
+    if (overlap(wr, split_bytes(m, k), w, m * (k / 256) * 210))
+        return fail(KQ_ERR_ARG, "%s: wr=%p overlaps w=%p", fn, wr, w);
+    if (m == 0) return ok();
+    if (int rc = check_device(fn, nullptr)) return rc;
+    return launched(fn, kq::launch_repack_q6k(w, wr, m, k, (hipStream_t)stream));
+}
+
+int kq_gemv_q6k_split(const void* wr, const void* xq, float* y, const float* residual, int64_t m,
+                      int64_t k, int32_t batch, void* stream) {
+    const char* fn = "kq_gemv_q6k_split";
+    if (int rc = gemv_common(fn, 210, wr, xq, y, residual, m, k, batch,
+                             (m >= 0 && m <= KQ_MAX_ROWS && k > 0 && k <= KQ_MAX_K)
+                                 ? split_bytes(m, k) : 0))
+        return rc;
+    if (m == 0) return ok();
+    int lds = 0, cus = 0;
+    if (int rc = check_device(fn, &lds, &cus)) return rc;
+    return launched(fn, kq::launch_gemv_q6k_split(wr, xq, y, residual, m, k, batch, lds, cus,
+                                                  (hipStream_t)stream));
 }
 
 static int producer_sizes(const char* fn, int64_t rows, int64_t n) {

@@ -131,6 +131,12 @@ hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, in
                           int64_t k, hipStream_t stream);
 hipError_t launch_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                           int64_t k, hipStream_t stream);
+hipError_t launch_mmq_q6k_split(const void* wr, const void* xq, float* y, int64_t m, int64_t n,
+                                int64_t k, hipStream_t stream);
+hipError_t launch_gemv_q6k_split(const void* wr, const void* xq, float* y, const float* residual,
+                                 int64_t m, int64_t k, int batch, int lds_limit, int cus,
+                                 hipStream_t stream);
+hipError_t launch_repack_q6k(const void* w, void* wr, int64_t m, int64_t k, hipStream_t stream);
 hipError_t launch_rmsnorm_q8_1(const float* x, const float* res, const float* g, float eps,
                                float* y, void* xq, int64_t rows, int64_t n, hipStream_t stream);
 hipError_t launch_swiglu_q8_1(const float* gate, const float* up, float* y, void* xq,

@@ -71,9 +71,12 @@ __device__ __forceinline__ void split4(uint32_t q, u16x2 nsc, u16x2 c32, uint32_
     b4 = ((we & 0x00ff00ffu) | ((wo & 0x00ff00ffu) << 8)) & 0x1f1f1f1fu;
 }
 
+// SPLIT: the weights are in the split layout (208-byte bodies at w, 16-byte
+// aligned, and the f16 d of superblock row * S + s at wd[row * S + s]).
+template <bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq,
-                    float* __restrict__ y, int M, int N, int S) {
+void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ wd,
+                    const uint8_t* __restrict__ xq, float* __restrict__ y, int M, int N, int S) {
     __shared__ __align__(16) Smem sm;
 
     const int tid = threadIdx.x;
@@ -106,8 +109,9 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
             asm volatile("" : "+v"(ts));
             const int rr = ts >> 1, e = ts & 1;
             const int gr = min(m0 + rr, M - 1);
-            const uint8_t* p = w + (int64_t)gr * row_bytes + (int64_t)sb * kQ6KBytes;
-            const int phase = (int)((uintptr_t)p & 2);
+            const int64_t g = (int64_t)gr * S + sb;
+            const uint8_t* p = SPLIT ? w + g * 208 : w + (int64_t)gr * row_bytes + (int64_t)sb * kQ6KBytes;
+            const int phase = SPLIT ? 0 : (int)((uintptr_t)p & 2);
             const uint8_t* base = p - phase;   // p - 2 lies in the previous superblock
             uint4 cur[7];
             uint32_t nxt[7];
@@ -116,10 +120,10 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
                 const int ch = e + 2 * c;
                 if (ch < 13) {
                     cur[c] = load16(base + 16 * ch);
-                    nxt[c] = *(const uint32_t*)(base + 16 * ch + (phase ? 16 : 12));
+                    if (!SPLIT) nxt[c] = *(const uint32_t*)(base + 16 * ch + (phase ? 16 : 12));
                 }
             }
-            const uint32_t dbits = e ? (uint32_t) * (const uint16_t*)(p + 208) : 0u;
+            const uint32_t dbits = !e ? 0u : SPLIT ? (uint32_t)wd[g] : (uint32_t) * (const uint16_t*)(p + 208);
             uint4 c0[4], c1[4];
             uint32_t hd[4];
 #pragma unroll
@@ -137,7 +141,7 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
                 const int ch = e + 2 * c;
                 if (ch < 13) {
                     uint4 v = cur[c];
-                    if (phase) {
+                    if (!SPLIT && phase) {
                         v.x = (cur[c].x >> 16) | (cur[c].y << 16);
                         v.y = (cur[c].y >> 16) | (cur[c].z << 16);
                         v.z = (cur[c].z >> 16) | (cur[c].w << 16);
@@ -249,8 +253,19 @@ hipError_t launch_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, in
                           int64_t k, hipStream_t stream) {
     const int S = (int)(k / kQK);
     dim3 grid((unsigned)((m + BM - 1) / BM), (unsigned)((n + BN - 1) / BN));
-    hipLaunchKernelGGL(mmq_q6k_kernel, grid, dim3(256), 0, stream, (const uint8_t*)w,
-                       (const uint8_t*)xq, y, (int)m, (int)n, S);
+    hipLaunchKernelGGL(mmq_q6k_kernel<false>, grid, dim3(256), 0, stream, (const uint8_t*)w,
+                       (const uint16_t*)nullptr, (const uint8_t*)xq, y, (int)m, (int)n, S);
+    return hipGetLastError();
+}
+
+hipError_t launch_mmq_q6k_split(const void* wr, const void* xq, float* y, int64_t m, int64_t n,
+                                int64_t k, hipStream_t stream) {
+    const int S = (int)(k / kQK);
+    const int64_t G = m * S;
+    const uint8_t* bodies = (const uint8_t*)wr + (2 * G + 15) / 16 * 16;
+    dim3 grid((unsigned)((m + BM - 1) / BM), (unsigned)((n + BN - 1) / BN));
+    hipLaunchKernelGGL(mmq_q6k_kernel<true>, grid, dim3(256), 0, stream, bodies,
+                       (const uint16_t*)wr, (const uint8_t*)xq, y, (int)m, (int)n, S);
     return hipGetLastError();
 }
 

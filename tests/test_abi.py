@@ -31,6 +31,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "kq_quantize_q8_1", "kq_gemv_q4k", "kq_gemv_q6k", "kq_mmq_q4k", "kq_mmq_q6k",
+        "kq_q6k_split_bytes", "kq_repack_q6k", "kq_gemv_q6k_split", "kq_mmq_q6k_split",
         "kq_rmsnorm_q8_1", "kq_swiglu_q8_1", "kq_gemv_q4k_seg", "kq_last_error",
         "kq_abi_version"])
 
@@ -75,7 +76,7 @@ def test_quantize_rejects(kq, args, needle):
     assert "kq_quantize_q8_1" in kq.kq_last_error()
 
 
-@pytest.mark.parametrize("fn", ["kq_gemv_q4k", "kq_gemv_q6k"])
+@pytest.mark.parametrize("fn", ["kq_gemv_q4k", "kq_gemv_q6k", "kq_gemv_q6k_split"])
 @pytest.mark.parametrize("args,needle", [
     ((None, X, Y, None, 8, 256, 1, None), "null pointer"),
     ((W, X, None, None, 8, 256, 1, None), "null pointer"),
@@ -100,7 +101,7 @@ def test_gemv_rejects(kq, fn, args, needle):
     assert fn in kq.kq_last_error()
 
 
-@pytest.mark.parametrize("fn", ["kq_mmq_q4k", "kq_mmq_q6k"])
+@pytest.mark.parametrize("fn", ["kq_mmq_q4k", "kq_mmq_q6k", "kq_mmq_q6k_split"])
 @pytest.mark.parametrize("args,needle", [
     ((None, X, Y, 8, 8, 256, None), "null pointer"),
     ((W, X, Y, 8, 8, 100, None), "k=100"),
@@ -120,6 +121,44 @@ def test_mmq_rejects(kq, fn, args, needle):
     assert fn in kq.kq_last_error()
 
 
+@pytest.mark.parametrize("m,k", [(0, 256), (1, 256), (3, 1280), (7, 4096), (128256, 4096), (5, 18944)])
+def test_split_bytes_match_the_oracle(kq, m, k):
+    import oracle
+
+    assert kq.kq_q6k_split_bytes(m, k) == oracle.q6k_split_bytes(m, k)
+
+
+@pytest.mark.parametrize("m,k", [(-1, 256), (1, 0), (1, 100), (1, 65536 + 256), (1 << 31, 256)])
+def test_split_bytes_rejects(kq, m, k):
+    assert kq.kq_q6k_split_bytes(m, k) == -1
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((None, X, 8, 256, None), "null pointer"),
+    ((W, None, 8, 256, None), "null pointer"),
+    ((W, X, 8, 100, None), "k=100"),
+    ((W, X, -2, 256, None), "m=-2"),
+    ((W + 2, X, 8, 256, None), "misaligned"),
+    ((W, X + 8, 8, 256, None), "misaligned"),
+    ((W, W + 1024, 8, 256, None), "overlaps"),
+    ((W + 1024, W, 8, 256, None), "overlaps"),
+])
+def test_repack_rejects(kq, args, needle):
+    rc = kq.lib().kq_repack_q6k(*args)
+    assert rc == kq.KQ_ERR_ARG, kq.kq_last_error()
+    assert needle in kq.kq_last_error() and "kq_repack_q6k" in kq.kq_last_error()
+
+
+def test_split_overlap_uses_the_split_size(kq):
+    # 1 x 512: 420 raw bytes, 432 in the split layout; y at W + 420 lies past
+    # the raw size but inside the split buffer
+    assert kq.kq_q6k_split_bytes(1, 512) == 432
+    rc = kq.lib().kq_gemv_q6k_split(W, X, W + 420, None, 1, 512, 1, None)
+    assert rc == kq.KQ_ERR_ARG and "overlaps" in kq.kq_last_error()
+    rc = kq.lib().kq_mmq_q6k_split(W, X, W + 420, 1, 1, 512, None)
+    assert rc == kq.KQ_ERR_ARG and "overlaps" in kq.kq_last_error()
+
+
 def test_mmq_q6k_size_guard_uses_its_block_size(kq):
     # 100000 rows x 65536: 4.9e9 bytes of Q6_K (rejected), 3.4e9 of Q4_K
     rc = kq.lib().kq_mmq_q6k(W, X, Y, 100000, 8, 65536, None)
@@ -136,6 +175,9 @@ def test_empty_inputs_launch_nothing(kq):
     assert L.kq_mmq_q4k(W, X, Y, 16, 0, 256, None) == kq.KQ_OK
     assert L.kq_mmq_q6k(W, X, Y, 0, 16, 256, None) == kq.KQ_OK
     assert L.kq_mmq_q6k(W, X, Y, 16, 0, 256, None) == kq.KQ_OK
+    assert L.kq_mmq_q6k_split(W, X, Y, 0, 16, 256, None) == kq.KQ_OK
+    assert L.kq_gemv_q6k_split(W, X, Y, None, 0, 256, 2, None) == kq.KQ_OK
+    assert L.kq_repack_q6k(W, X, 0, 256, None) == kq.KQ_OK
 
 
 def test_binding_raises_with_message(kq):
