@@ -641,7 +641,7 @@ def main(argv=None):
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the k-quant "
-              "matmul runs on one MI355X; sharding is described in DESIGN.md).", file=sys.stderr)
+              "matmul library runs on one MI355X).", file=sys.stderr)
         return 2
 
     import torch
