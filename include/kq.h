@@ -48,8 +48,8 @@
  *     kq_last_error() names the call and the offending values;
  *   - KQ_ERR_UNSUPPORTED: the current HIP device is not a gfx950 GPU;
  *   - KQ_ERR_HIP: the launch failed; kq_last_error() holds the HIP error;
- *   - there is no fallback path: a call either launches the gfx950 kernel or
- *     returns an error;
+ *   - there is no fallback path: a call either launches its gfx950 kernel(s)
+ *     or returns an error (kq_q6k_split_bytes only computes a size);
  *   - results are deterministic: the same inputs give the same output bits
  *     on every run (no atomics, fixed reduction order);
  *   - sizes of zero rows / tokens (m == 0, n == 0, rows == 0, batch rows of an

@@ -1,4 +1,5 @@
-// gemv_q4k.hip -- Q4_K x q8_1 matrix-vector product (decode, batch 1..4).
+// gemv_q4k.hip -- Q4_K x q8_1 matrix-vector product (decode, batch 1..8),
+// for one weight tensor or for up to 8 tensors that share one activation.
 //
 // The decode matmul reads every weight byte once, so the kernel is bound by
 // HBM bandwidth (minfer "The CUDA backend" 2.2: decode is weight-streaming
@@ -21,13 +22,15 @@
 //     HBM latency overlaps the activation staging and the arithmetic;
 //   * when the whole activation fits in LDS the grid is persistent: a few
 //     workgroups per compute unit stage it once and walk the row groups
-//     (blockIdx.x, blockIdx.x + gridDim.x, ...), and the load ring runs on
-//     across row groups, so the memory pipe never drains between them;
+//     (blockIdx.x, blockIdx.x + gridDim.x, ...) of one tensor or of a table
+//     of tensors (the segmented form), and the load ring runs on across row
+//     groups, so the memory pipe never drains between them;
 //   * the q8_1 activation is restaged once per workgroup into LDS: per
-//     superblock the 16-byte slices in the order the lanes read them, and per
-//     lane the four d8 values and the four d8 * (sum of the slice's codes);
-//     when the row does not fit the LDS budget it is staged in chunks of whole
-//     passes;
+//     superblock the 16-byte slices in the order the lanes read them
+//     (xor-swizzled by superblock so a 16-lane read hits distinct banks), and
+//     per lane the four d8 values and the four d8 * (sum of the slice's
+//     codes) in two planes; when the row does not fit the LDS budget it is
+//     staged in chunks of whole passes;
 //   * integer dots with v_dot4_i32_i8 (4-bit codes are non-negative bytes),
 //     then per lane sum_j d8_j*(sc_j*A_j) and sum_j m_j*(d8_j*Bq_j) in f32 and
 //     acc += d*first - dmin*second; the minimum term uses the q8 codes

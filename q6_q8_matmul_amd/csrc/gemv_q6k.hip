@@ -1,4 +1,6 @@
-// gemv_q6k.hip -- Q6_K x q8_1 matrix-vector product (output head, batch 1..4).
+// gemv_q6k.hip -- Q6_K x q8_1 matrix-vector product (output head, batch 1..8),
+// on the raw 210-byte layout or on the split layout (f16 d prefix, 208-byte
+// bodies 16-byte aligned) made by kq_repack_q6k.
 //
 // Weight streaming bound like the Q4_K GEMV (minfer "The CUDA backend" 2.2).
 // A Q6_K superblock is 210 bytes, so superblock starts are only 2-byte
@@ -8,7 +10,8 @@
 // 2 (mod 4) address reads the three aligned dwords around them and funnel-
 // shifts (v_alignbit_b32).  Every read stays inside the tensor: at most the
 // two bytes before a superblock that starts at 2 (mod 4), which are the tail
-// of the previous superblock.
+// of the previous superblock.  On the split layout the same lanes read the
+// same bytes with aligned 8-byte loads and no shift, and d from the prefix.
 //
 // Work layout (as the Q4_K GEMV): WAVES wavefronts x RPW rows per row group;
 // 8 groups of 8 lanes take 8 consecutive superblocks of a row per pass; the
@@ -33,9 +36,8 @@
 // Q6_K GEMV with residual epilogue, fixed reduction order, no atomics).
 #include "kq_device.h"
 
-#include <type_traits>
-
 #include <algorithm>
+#include <type_traits>
 
 namespace kq {
 namespace gemv6 {

@@ -1,11 +1,12 @@
 // kq_api.cpp -- the C ABI of libkq (declared in include/kq.h).
 //
 // Every entry point validates its arguments before touching the HIP runtime,
-// checks that the current device is a gfx950 GPU, launches exactly one kernel
-// on the caller's stream and reports the launch status.  Invariant
-// violations return an error that names the offending values; nothing falls
-// back to another path (minfer "The CUDA backend" 3.4: a violated invariant
-// is an error with the values, never a silent detour).
+// checks that the current device is a gfx950 GPU, launches its gfx950 kernel
+// on the caller's stream (one launch; a segmented GEMV whose activation does
+// not fit on chip launches once per segment) and reports the launch status.
+// Invariant violations return an error that names the offending values;
+// nothing falls back to another path (minfer "The CUDA backend" 3.4: a
+// violated invariant is an error with the values, never a silent detour).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
