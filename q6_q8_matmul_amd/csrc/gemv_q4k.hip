@@ -76,56 +76,91 @@ __device__ __forceinline__ int quad_of(int jj) {   // slice r of lane 2c (h = 0)
     return 4 * (2 * hiA + e) + 2 * c;
 }
 
-// Stage blocks [j0, j0 + nbc) of every column (nbc a multiple of 8): one
-// thread per (column, q8_1 block), the loads of U blocks per thread in flight
-// before any is used.  Ends with a barrier.
+// Staging of blocks [j0, j0 + nbc) of every column (nbc a multiple of 8):
+// one thread per (column, q8_1 block), U blocks per thread per round.  A
+// round is split into the issue of its global loads (into StageRegs) and the
+// LDS writes, so a kernel can issue the first round's loads before its weight
+// loads: loads complete in issue order, and activation loads issued after the
+// weight ring would have to wait for the weights' HBM latency before the
+// staging could finish.
+template <int U>
+struct StageRegs {
+    uint32_t c[U][9];
+};
+
 template <int BATCH, int NT, int U>
-__device__ __forceinline__ void stage_activation(const uint8_t* __restrict__ xq, int nb_row,
-                                                 int j0, int nbc, int schunk, uint8_t* lds) {
+__device__ __forceinline__ void stage_issue(StageRegs<U>& r, const uint8_t* __restrict__ xq,
+                                            int nb_row, int j0, int nbc, int base) {
+    const int total = BATCH * nbc;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        const int idx = base + i * NT + (int)threadIdx.x;
+        if (idx < total) {
+            const int bb = BATCH == 1 ? 0 : idx / nbc;
+            const int j = idx - bb * nbc;
+            const uint32_t* blk = (const uint32_t*)(xq + ((int64_t)bb * nb_row + j0 + j) * kQ81Bytes);
+#pragma unroll
+            for (int e = 0; e < 9; ++e) r.c[i][e] = blk[e];
+        }
+    }
+}
+
+template <int BATCH, int NT, int U>
+__device__ __forceinline__ void stage_write(const StageRegs<U>& r, int nbc, int base, int schunk,
+                                            uint8_t* lds) {
     uint8_t* codes = lds;
     float* d8p = (float*)(lds + BATCH * schunk * 256);
     float* zp = d8p + BATCH * schunk * 16;
     const int total = BATCH * nbc;
-    for (int base = 0; base < total; base += NT * U) {
-        uint32_t c[U][9];
 #pragma unroll
-        for (int i = 0; i < U; ++i) {
-            const int idx = base + i * NT + (int)threadIdx.x;
-            if (idx < total) {
-                const int bb = BATCH == 1 ? 0 : idx / nbc;
-                const int j = idx - bb * nbc;
-                const uint32_t* blk = (const uint32_t*)(xq + ((int64_t)bb * nb_row + j0 + j) * kQ81Bytes);
-#pragma unroll
-                for (int e = 0; e < 9; ++e) c[i][e] = blk[e];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < U; ++i) {
-            const int idx = base + i * NT + (int)threadIdx.x;
-            if (idx < total) {
-                const int bb = BATCH == 1 ? 0 : idx / nbc;
-                const int j = idx - bb * nbc;
-                const int sb = j >> 3, jj = j & 7;
-                const float d8 = half_bits_to_float(c[i][0]);
-                const int s0 = dot4(c[i][1], 0x01010101u, dot4(c[i][2], 0x01010101u,
-                               dot4(c[i][3], 0x01010101u, dot4(c[i][4], 0x01010101u, 0))));
-                const int s1 = dot4(c[i][5], 0x01010101u, dot4(c[i][6], 0x01010101u,
-                               dot4(c[i][7], 0x01010101u, dot4(c[i][8], 0x01010101u, 0))));
-                const int q0 = quad_of(jj);
-                uint8_t* cs = codes + (bb * schunk + sb) * 256 + 16 * (q0 ^ swz(sb));
-                *(uint4*)cs = make_uint4(c[i][1], c[i][2], c[i][3], c[i][4]);
-                *(uint4*)(cs + 16) = make_uint4(c[i][5], c[i][6], c[i][7], c[i][8]);
-                const int r = q0 >> 2, t0 = q0 & 3;   // slice index and lane (h = 0)
-                float* dp = d8p + ((bb * schunk + sb) * 4 + t0) * 4;
-                float* zq = zp + ((bb * schunk + sb) * 4 + t0) * 4;
-                dp[r] = d8;
-                zq[r] = d8 * (float)s0;
-                dp[4 + r] = d8;                       // lane t0 + 1 (h = 1)
-                zq[4 + r] = d8 * (float)s1;
-            }
+    for (int i = 0; i < U; ++i) {
+        const int idx = base + i * NT + (int)threadIdx.x;
+        if (idx < total) {
+            const int bb = BATCH == 1 ? 0 : idx / nbc;
+            const int j = idx - bb * nbc;
+            const int sb = j >> 3, jj = j & 7;
+            const uint32_t* c = r.c[i];
+            const float d8 = half_bits_to_float(c[0]);
+            const int s0 = dot4(c[1], 0x01010101u, dot4(c[2], 0x01010101u,
+                           dot4(c[3], 0x01010101u, dot4(c[4], 0x01010101u, 0))));
+            const int s1 = dot4(c[5], 0x01010101u, dot4(c[6], 0x01010101u,
+                           dot4(c[7], 0x01010101u, dot4(c[8], 0x01010101u, 0))));
+            const int q0 = quad_of(jj);
+            uint8_t* cs = codes + (bb * schunk + sb) * 256 + 16 * (q0 ^ swz(sb));
+            *(uint4*)cs = make_uint4(c[1], c[2], c[3], c[4]);
+            *(uint4*)(cs + 16) = make_uint4(c[5], c[6], c[7], c[8]);
+            const int rr = q0 >> 2, t0 = q0 & 3;   // slice index and lane (h = 0)
+            float* dp = d8p + ((bb * schunk + sb) * 4 + t0) * 4;
+            float* zq = zp + ((bb * schunk + sb) * 4 + t0) * 4;
+            dp[rr] = d8;
+            zq[rr] = d8 * (float)s0;
+            dp[4 + rr] = d8;                       // lane t0 + 1 (h = 1)
+            zq[4 + rr] = d8 * (float)s1;
         }
     }
+}
+
+// The rest of a staging whose first round was issued into r: its LDS writes,
+// every later round, and the closing barrier.
+template <int BATCH, int NT, int U>
+__device__ __forceinline__ void stage_finish(StageRegs<U>& r, const uint8_t* __restrict__ xq,
+                                             int nb_row, int j0, int nbc, int schunk,
+                                             uint8_t* lds) {
+    stage_write<BATCH, NT, U>(r, nbc, 0, schunk, lds);
+    for (int base = NT * U; base < BATCH * nbc; base += NT * U) {
+        stage_issue<BATCH, NT, U>(r, xq, nb_row, j0, nbc, base);
+        stage_write<BATCH, NT, U>(r, nbc, base, schunk, lds);
+    }
     __syncthreads();
+}
+
+// A whole staging (all loads of a round in flight before any is used).
+template <int BATCH, int NT, int U>
+__device__ __forceinline__ void stage_activation(const uint8_t* __restrict__ xq, int nb_row,
+                                                 int j0, int nbc, int schunk, uint8_t* lds) {
+    StageRegs<U> r;
+    stage_issue<BATCH, NT, U>(r, xq, nb_row, j0, nbc, 0);
+    stage_finish<BATCH, NT, U>(r, xq, nb_row, j0, nbc, schunk, lds);
 }
 
 template <int RPW>
@@ -329,11 +364,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __r
     const uint8_t* rowp[RPW];
     const int pair0 = (blockIdx.x * WAVES + wave) * RPW;   // first row pair of this wave
     const int chunk_passes = schunk >> 3;   // schunk is a multiple of 8 superblocks
+    constexpr int U = BATCH == 1 ? 2 : 4;
+    StageRegs<U> sr;   // the activation loads go first (see stage_issue)
+    stage_issue<BATCH, 64 * WAVES, U>(sr, xq, nb_row, 0, min(schunk, S) * 8, 0);
     group_rows<RPW>(rowp, w, blockIdx.x, WAVES, wave, half, m, row_bytes);
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) load_pass<RPW>(ring[d], rowp, 8 * d + grp, S, t);
 
-    stage_activation<BATCH, 64 * WAVES, (BATCH == 1 ? 2 : 4)>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
+    stage_finish<BATCH, 64 * WAVES, U>(sr, xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
 
     for (int p0 = 0; p0 < npass; p0 += DEPTH) {
 #pragma unroll
@@ -390,6 +428,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_persistent(const Tab sg,
     const uint8_t* rowp[RPW];
     // (group, pass) of the next item to load and of the next to compute
     int gl = blockIdx.x, pl = 0;
+    StageRegs<2> sr;   // the activation loads go first (see stage_issue)
+    stage_issue<BATCH, 64 * WAVES, 2>(sr, xq, nb_row, 0, S * 8, 0);
     SegCursor cl = seg_start(sg, gl);
     auto rows_of = [&](int g) {
         seg_seek(cl, sg, g);
@@ -398,7 +438,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_persistent(const Tab sg,
     rows_of(gl);
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
-        if (d < nitems) {
+        if (d == 0 || d < nitems) {   // nitems >= 1: the grid has at most one workgroup per group
             load_pass<RPW>(ring[d], rowp, 8 * pl + grp, S, t);
             if (++pl == npass) {
                 pl = 0;
@@ -407,7 +447,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_persistent(const Tab sg,
             }
         }
     }
-    stage_activation<BATCH, 64 * WAVES, 2>(xq, nb_row, 0, S * 8, schunk, smem);
+    stage_finish<BATCH, 64 * WAVES, 2>(sr, xq, nb_row, 0, S * 8, schunk, smem);
     int gc = blockIdx.x, pc = 0;
     SegCursor cc = seg_start(sg, gc);
     for (int it0 = 0; it0 < nitems; it0 += DEPTH) {

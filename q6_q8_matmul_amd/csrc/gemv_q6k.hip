@@ -69,46 +69,79 @@ constexpr int kLdsPerSb = 256 + 8 * 4;
 
 __device__ __forceinline__ int swz(int sb) { return 8 * (sb & 1); }   // in 16-byte units
 
-// Stage blocks [j0, j0 + nbc) of every column (nbc a multiple of 8): one
-// thread per q8_1 block, the loads of U blocks in flight before any is used.
-// Ends with a barrier.
+// Staging of blocks [j0, j0 + nbc) of every column (nbc a multiple of 8):
+// one thread per (column, q8_1 block), U blocks per thread per round.  A
+// round is split into the issue of its global loads and the LDS writes, so a
+// kernel can issue the first round's loads before its weight loads (loads
+// complete in issue order: activation loads issued after the weight ring
+// would wait for the weights' HBM latency before the staging could finish).
+template <int U>
+struct StageRegs {
+    uint32_t c[U][9];
+};
+
 template <int BATCH, int NT, int U>
-__device__ __forceinline__ void stage_activation(const uint8_t* __restrict__ xq, int nb_row,
-                                                 int j0, int nbc, int schunk, uint8_t* lds) {
+__device__ __forceinline__ void stage_issue(StageRegs<U>& r, const uint8_t* __restrict__ xq,
+                                            int nb_row, int j0, int nbc, int base) {
+    const int total = BATCH * nbc;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        const int idx = base + i * NT + (int)threadIdx.x;
+        if (idx < total) {
+            const int bb = idx / nbc;
+            const int j = idx - bb * nbc;
+            const uint32_t* blk = (const uint32_t*)(xq + ((int64_t)bb * nb_row + j0 + j) * kQ81Bytes);
+#pragma unroll
+            for (int e = 0; e < 9; ++e) r.c[i][e] = blk[e];
+        }
+    }
+}
+
+template <int BATCH, int NT, int U>
+__device__ __forceinline__ void stage_write(const StageRegs<U>& r, int nbc, int base, int schunk,
+                                            uint8_t* lds) {
     const int cap = schunk * 8;
     uint8_t* codes = lds;
     float* d8s = (float*)(lds + BATCH * schunk * 256);
     const int total = BATCH * nbc;
-    for (int base = 0; base < total; base += NT * U) {
-        uint32_t c[U][9];
 #pragma unroll
-        for (int i = 0; i < U; ++i) {
-            const int idx = base + i * NT + (int)threadIdx.x;
-            if (idx < total) {
-                const int bb = idx / nbc;
-                const int j = idx - bb * nbc;
-                const uint32_t* blk = (const uint32_t*)(xq + ((int64_t)bb * nb_row + j0 + j) * kQ81Bytes);
+    for (int i = 0; i < U; ++i) {
+        const int idx = base + i * NT + (int)threadIdx.x;
+        if (idx < total) {
+            const int bb = idx / nbc;
+            const int j = idx - bb * nbc;
+            const int sb = j >> 3, jj = j & 7, h = jj >> 2, g = jj & 3;
+            uint8_t* cs = codes + (bb * schunk + sb) * 256 + 8 * (g & 1);
+            const int u0 = ((g < 2) ? 0 : 8) ^ swz(sb);
 #pragma unroll
-                for (int e = 0; e < 9; ++e) c[i][e] = blk[e];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < U; ++i) {
-            const int idx = base + i * NT + (int)threadIdx.x;
-            if (idx < total) {
-                const int bb = idx / nbc;
-                const int j = idx - bb * nbc;
-                const int sb = j >> 3, jj = j & 7, h = jj >> 2, g = jj & 3;
-                uint8_t* cs = codes + (bb * schunk + sb) * 256 + 8 * (g & 1);
-                const int u0 = ((g < 2) ? 0 : 8) ^ swz(sb);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)   // 8-value piece q goes to lane 4h + q
-                    *(uint2*)(cs + 16 * (u0 + 4 * h + q)) = make_uint2(c[i][1 + 2 * q], c[i][2 + 2 * q]);
-                d8s[bb * cap + j] = half_bits_to_float(c[i][0]);
-            }
+            for (int q = 0; q < 4; ++q)   // 8-value piece q goes to lane 4h + q
+                *(uint2*)(cs + 16 * (u0 + 4 * h + q)) = make_uint2(r.c[i][1 + 2 * q], r.c[i][2 + 2 * q]);
+            d8s[bb * cap + j] = half_bits_to_float(r.c[i][0]);
         }
     }
+}
+
+// The rest of a staging whose first round was issued into r: its LDS writes,
+// every later round, and the closing barrier.
+template <int BATCH, int NT, int U>
+__device__ __forceinline__ void stage_finish(StageRegs<U>& r, const uint8_t* __restrict__ xq,
+                                             int nb_row, int j0, int nbc, int schunk,
+                                             uint8_t* lds) {
+    stage_write<BATCH, NT, U>(r, nbc, 0, schunk, lds);
+    for (int base = NT * U; base < BATCH * nbc; base += NT * U) {
+        stage_issue<BATCH, NT, U>(r, xq, nb_row, j0, nbc, base);
+        stage_write<BATCH, NT, U>(r, nbc, base, schunk, lds);
+    }
     __syncthreads();
+}
+
+// A whole staging (all loads of a round in flight before any is used).
+template <int BATCH, int NT, int U>
+__device__ __forceinline__ void stage_activation(const uint8_t* __restrict__ xq, int nb_row,
+                                                 int j0, int nbc, int schunk, uint8_t* lds) {
+    StageRegs<U> r;
+    stage_issue<BATCH, NT, U>(r, xq, nb_row, j0, nbc, 0);
+    stage_finish<BATCH, NT, U>(r, xq, nb_row, j0, nbc, schunk, lds);
 }
 
 // Three aligned dwords covering the 8 bytes at offset `off` of a superblock
@@ -318,14 +351,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __r
         const int nitems = ((ngroups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x) * npass;
         // (group, pass) of the next item to load and of the next to compute
         int gl = blockIdx.x, pl = 0;
+        StageRegs<2> sr;   // the activation loads go first (see stage_issue)
+        stage_issue<BATCH, 64 * WAVES, 2>(sr, xq, nb_row, 0, S * 8, 0);
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
-            if (d < nitems) {
+            if (d == 0 || d < nitems) {   // nitems >= 1: at most one workgroup per group
                 load(ring[d], (gl * WAVES + wave) * RPW, 8 * pl + grp);
                 if (++pl == npass) { pl = 0; gl += gridDim.x; }
             }
         }
-        stage_activation<BATCH, 64 * WAVES, 2>(xq, nb_row, 0, S * 8, schunk, smem);
+        stage_finish<BATCH, 64 * WAVES, 2>(sr, xq, nb_row, 0, S * 8, schunk, smem);
         int gc = blockIdx.x, pc = 0;
         for (int it0 = 0; it0 < nitems; it0 += DEPTH) {
 #pragma unroll
@@ -348,11 +383,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q6k_kernel(const uint8_t* __r
     } else {
         const int row0 = (blockIdx.x * WAVES + wave) * RPW;
         const int chunk_passes = schunk >> 3;
+        constexpr int U = BATCH >= 2 && BATCH <= 4 ? 4 : 2;
+        StageRegs<U> sr;   // the activation loads go first (see stage_issue)
+        stage_issue<BATCH, 64 * WAVES, U>(sr, xq, nb_row, 0, min(schunk, S) * 8, 0);
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d)
             load(ring[d], row0, 8 * d + grp);
 
-        stage_activation<BATCH, 64 * WAVES, (BATCH >= 2 && BATCH <= 4 ? 4 : 2)>(xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
+        stage_finish<BATCH, 64 * WAVES, U>(sr, xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
 
         for (int p0 = 0; p0 < npass; p0 += DEPTH) {
 #pragma unroll
