@@ -12,11 +12,14 @@
 //   * a wavefront streams row pairs: lanes 0..31 one row, lanes 32..63 the
 //     next; RPW pairs per wavefront, WAVES wavefronts per workgroup;
 //   * in a half-wave, 8 groups of 4 lanes take 8 consecutive superblocks per
-//     pass; lane t of a group loads the 16-byte code slices [16t, 16t+16) and
-//     [64+16t, 64+16t+16) plus the 16-byte header, i.e. 16 values of each of
-//     sub-blocks 2c, 2c+1, 2c+4, 2c+5 (c = t/2, values 16h..16h+15, h = t%2),
-//     so every lane decodes the same mix of low (j < 4) and high (j >= 4)
-//     six-bit fields and the code has no lane-dependent branches;
+//     pass; lane t of a group loads the 16-byte header and the code bytes
+//     [32t, 32t+32), whose low nibbles are sub-block 2t and high nibbles
+//     sub-block 2t+1, so each lane owns two whole 32-value sub-blocks and
+//     their two (scale, min) pairs; lanes 0, 1 take their six-bit fields
+//     from the low bits of scale bytes 0..7 and lanes 2, 3 from the nibbles
+//     of bytes 8..11 plus the top bits of bytes 0..7, both through the same
+//     v_bfe_u32 sequence with lane-constant offsets and widths (a zero width
+//     gives zero), so the code has no lane-dependent branches;
 //   * the loads of the first DEPTH passes are issued before anything else and
 //     every later pass is requested DEPTH passes ahead (a register ring), so
 //     HBM latency overlaps the activation staging and the arithmetic;
@@ -26,16 +29,17 @@
 //     of tensors (the segmented form), and the load ring runs on across row
 //     groups, so the memory pipe never drains between them;
 //   * the q8_1 activation is restaged once per workgroup into LDS: per
-//     superblock the 16-byte slices in the order the lanes read them
-//     (xor-swizzled by superblock so a 16-lane read hits distinct banks), and
-//     per lane the four d8 values and the four d8 * (sum of the slice's
-//     codes) in two planes; when the row does not fit the LDS budget it is
-//     staged in chunks of whole passes;
+//     superblock its 256 codes in natural order, 16-byte units xor-swizzled
+//     by superblock so a 16-lane read hits distinct banks, and per lane one
+//     float4 (d8 of its two blocks, d8 * (sum of each block's codes)); when
+//     the row does not fit the LDS budget it is staged in chunks of whole
+//     passes;
 //   * integer dots with v_dot4_i32_i8 (4-bit codes are non-negative bytes),
-//     then per lane sum_j d8_j*(sc_j*A_j) and sum_j m_j*(d8_j*Bq_j) in f32 and
-//     acc += d*first - dmin*second; the minimum term uses the q8 codes
-//     (leone-cuda "CUDA kernel design": minimum correction formed from the
-//     same lane-local codes);
+//     one 32-value dot A_j per sub-block and column, then per lane
+//     acc += (d*sc_j) * (A_j*d8_j) - (dmin*m_j) * (d8_j*Bq_j) in f32, with
+//     d*sc_j and dmin*m_j formed once per row (exact: f16 times a six-bit
+//     integer); the minimum term uses the q8 codes (leone-cuda "CUDA kernel
+//     design": minimum correction formed from the same lane-local codes);
 //   * one fixed xor-butterfly over the 32 lanes of a row per batch column,
 //     then the optional residual is added when the row is written
 //     (leone-cuda "CUDA kernel design": residual epilogue, same f32 addition
@@ -51,30 +55,24 @@ namespace gemv4 {
 
 struct Slice {      // one lane's share of one superblock of one row
     uint4 hdr;      // d, dmin, 12 scale bytes
-    uint4 qa;       // code bytes [16t, 16t+16)
-    uint4 qb;       // code bytes [64+16t, 64+16t+16)
+    uint4 qa;       // code bytes [32t, 32t+16)
+    uint4 qb;       // code bytes [32t+16, 32t+32)
 };
 
 // LDS layout of one staged column (schunk superblocks):
-//   codes [schunk][256]   quad 4r + t (16 bytes) = the slice lane t reads as
-//                         its r-th block: r = 0, 1, 2, 3 <-> blocks 2c, 2c+1,
-//                         2c+4, 2c+5, values 16h..16h+15; stored at quad
-//                         4(r ^ (sb & 3)) + t of superblock sb;
-//   d8p   [schunk][4]     float4 per lane t: d8 of its four blocks;
-//   zp    [schunk][4]     float4 per lane t: d8 * (sum of the slice's 16
-//                         codes) for each.
-// The sixteen lanes that one LDS cycle serves read superblocks sb .. sb+3 at
-// the same quad; the xor gives them four different quads, so each 16-byte
-// read touches 16 distinct bank groups (a 256-byte stride alone puts all
-// four superblocks on the same banks).
-constexpr int kLdsPerSb = 256 + 4 * 8 * 4;
+//   codes [schunk][256]   the superblock's 256 q8 codes; 16-byte unit u
+//                         (values 16u..16u+15) stored at unit u ^ (sb & 3);
+//                         lane t reads units 4t .. 4t+3 (blocks 2t, 2t+1);
+//   dz    [schunk][4]     float4 per lane t: d8 of blocks 2t and 2t+1, then
+//                         d8 * (sum of the block's 32 codes) for each.
+// The sixteen lanes that one LDS cycle serves are four lanes of each of
+// superblocks sb .. sb+3 (sb a multiple of 4); their reads of unit 4t + r
+// land on units 4t + (r ^ (sb & 3)): sixteen distinct 16-byte bank groups
+// (the 256-byte superblock stride alone would put all four superblocks on
+// the same banks).  The dz reads of those lanes are 256 contiguous bytes.
+constexpr int kLdsPerSb = 256 + 4 * 16;
 
-__device__ __forceinline__ int swz(int sb) { return 4 * (sb & 3); }
-
-__device__ __forceinline__ int quad_of(int jj) {   // slice r of lane 2c (h = 0) of block jj
-    const int hiA = jj >> 2, c = (jj >> 1) & 1, e = jj & 1;
-    return 4 * (2 * hiA + e) + 2 * c;
-}
+__device__ __forceinline__ int swz(int sb) { return sb & 3; }
 
 // Staging of blocks [j0, j0 + nbc) of every column (nbc a multiple of 8):
 // one thread per (column, q8_1 block), U blocks per thread per round.  A
@@ -109,8 +107,7 @@ template <int BATCH, int NT, int U>
 __device__ __forceinline__ void stage_write(const StageRegs<U>& r, int nbc, int base, int schunk,
                                             uint8_t* lds) {
     uint8_t* codes = lds;
-    float* d8p = (float*)(lds + BATCH * schunk * 256);
-    float* zp = d8p + BATCH * schunk * 16;
+    float* dz = (float*)(lds + BATCH * schunk * 256);
     const int total = BATCH * nbc;
 #pragma unroll
     for (int i = 0; i < U; ++i) {
@@ -121,21 +118,16 @@ __device__ __forceinline__ void stage_write(const StageRegs<U>& r, int nbc, int 
             const int sb = j >> 3, jj = j & 7;
             const uint32_t* c = r.c[i];
             const float d8 = half_bits_to_float(c[0]);
-            const int s0 = dot4(c[1], 0x01010101u, dot4(c[2], 0x01010101u,
-                           dot4(c[3], 0x01010101u, dot4(c[4], 0x01010101u, 0))));
-            const int s1 = dot4(c[5], 0x01010101u, dot4(c[6], 0x01010101u,
-                           dot4(c[7], 0x01010101u, dot4(c[8], 0x01010101u, 0))));
-            const int q0 = quad_of(jj);
-            uint8_t* cs = codes + (bb * schunk + sb) * 256 + 16 * (q0 ^ swz(sb));
-            *(uint4*)cs = make_uint4(c[1], c[2], c[3], c[4]);
-            *(uint4*)(cs + 16) = make_uint4(c[5], c[6], c[7], c[8]);
-            const int rr = q0 >> 2, t0 = q0 & 3;   // slice index and lane (h = 0)
-            float* dp = d8p + ((bb * schunk + sb) * 4 + t0) * 4;
-            float* zq = zp + ((bb * schunk + sb) * 4 + t0) * 4;
-            dp[rr] = d8;
-            zq[rr] = d8 * (float)s0;
-            dp[4 + rr] = d8;                       // lane t0 + 1 (h = 1)
-            zq[4 + rr] = d8 * (float)s1;
+            int sq = 0;
+#pragma unroll
+            for (int e = 1; e <= 8; ++e) sq = dot4(c[e], 0x01010101u, sq);
+            uint8_t* cs = codes + (bb * schunk + sb) * 256;
+            const int x = swz(sb);
+            *(uint4*)(cs + 16 * ((2 * jj) ^ x)) = make_uint4(c[1], c[2], c[3], c[4]);
+            *(uint4*)(cs + 16 * ((2 * jj + 1) ^ x)) = make_uint4(c[5], c[6], c[7], c[8]);
+            float* dp = dz + ((bb * schunk + sb) * 4 + (jj >> 1)) * 4;
+            dp[jj & 1] = d8;
+            dp[2 + (jj & 1)] = d8 * (float)sq;
         }
     }
 }
@@ -171,70 +163,72 @@ __device__ __forceinline__ void load_pass(Slice (&s)[RPW], const uint8_t* const 
     for (int i = 0; i < RPW; ++i) {
         const uint8_t* p = rowp[i] + sbc * kQ4KBytes;
         s[i].hdr = load16(p);
-        s[i].qa = load16(p + 16 + 16 * t);
-        s[i].qb = load16(p + 80 + 16 * t);
+        s[i].qa = load16(p + 16 + 32 * t);
+        s[i].qb = load16(p + 32 + 32 * t);
     }
 }
 
-__device__ __forceinline__ int dot16(uint4 w, uint4 a) {
-    return dot4(w.w, a.w, dot4(w.z, a.z, dot4(w.y, a.y, dot4(w.x, a.x, 0))));
+__device__ __forceinline__ int dot16(uint4 w, uint4 a, int c) {
+    return dot4(w.w, a.w, dot4(w.z, a.z, dot4(w.y, a.y, dot4(w.x, a.x, c))));
+}
+
+__device__ __forceinline__ uint4 lo_nibbles(uint4 q) {
+    return make_uint4(q.x & 0x0f0f0f0fu, q.y & 0x0f0f0f0fu, q.z & 0x0f0f0f0fu, q.w & 0x0f0f0f0fu);
+}
+
+__device__ __forceinline__ uint4 hi_nibbles(uint4 q) {
+    return make_uint4((q.x >> 4) & 0x0f0f0f0fu, (q.y >> 4) & 0x0f0f0f0fu, (q.z >> 4) & 0x0f0f0f0fu,
+                      (q.w >> 4) & 0x0f0f0f0fu);
 }
 
 template <int BATCH, int RPW>
 __device__ __forceinline__ void compute_pass(const Slice (&s)[RPW], float (&acc)[RPW][BATCH],
                                              const uint8_t* lds, int schunk, int sl, int t) {
-    // activation slices of this lane for every column: read once, used by all rows
+    // activation of this lane for every column: read once, used by all rows
     const uint8_t* codes = lds;
-    const float4* d8p = (const float4*)(lds + BATCH * schunk * 256);
-    const float4* zp = d8p + BATCH * schunk * 4;
+    const float4* dz = (const float4*)(lds + BATCH * schunk * 256);
     uint4 a[BATCH][4];
-    float4 d8v[BATCH], dbq[BATCH];
+    float4 dzv[BATCH];
     const int x = swz(sl);
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
-        const uint8_t* cs = codes + (b * schunk + sl) * 256;
+        const uint8_t* cs = codes + (b * schunk + sl) * 256 + 64 * t;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) a[b][r] = *(const uint4*)(cs + 16 * ((4 * r + t) ^ x));
-        d8v[b] = d8p[(b * schunk + sl) * 4 + t];
-        dbq[b] = zp[(b * schunk + sl) * 4 + t];
+        for (int r = 0; r < 4; ++r) a[b][r] = *(const uint4*)(cs + 16 * (r ^ x));
+        dzv[b] = dz[(b * schunk + sl) * 4 + t];
     }
-    const uint32_t sh = 16u * (uint32_t)(t >> 1);   // byte 2c of the scale words
+    // six-bit fields of sub-blocks j = 2t, 2t+1 (byte e = 2(t%2) + {0,1} of
+    // a scale word): j < 4 -> scale = bits 0..5 of byte e of bytes 0..3, min
+    // = the same of bytes 4..7; j >= 4 -> scale = low nibble of byte 8+e
+    // with bits 6..7 of byte e above it, min = high nibble of byte 8+e with
+    // bits 6..7 of byte 4+e
+    const bool hi = t >= 2;
+    const uint32_t p0 = 16u * (uint32_t)(t & 1);
+    const uint32_t wl = hi ? 4u : 6u, wh = hi ? 2u : 0u, mo = hi ? 4u : 0u;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const uint4 hdr = s[i].hdr;
         const float d = half_bits_to_float(hdr.x);
         const float dmin = half_bits_to_float(hdr.x >> 16);
-        // six-bit scales/mins: j = 2c, 2c+1 in the low six bits of bytes 0..3,
-        // j = 2c+4, 2c+5 in the nibbles of bytes 8..11 plus the top two bits
-        // of bytes 0..7
-        const int sc0 = (int)__builtin_amdgcn_ubfe(hdr.y, sh, 6);
-        const int sc1 = (int)__builtin_amdgcn_ubfe(hdr.y, sh + 8, 6);
-        const int sc2 = (int)(__builtin_amdgcn_ubfe(hdr.w, sh, 4) | (__builtin_amdgcn_ubfe(hdr.y, sh + 6, 2) << 4));
-        const int sc3 = (int)(__builtin_amdgcn_ubfe(hdr.w, sh + 8, 4) | (__builtin_amdgcn_ubfe(hdr.y, sh + 14, 2) << 4));
-        const float m0 = (float)__builtin_amdgcn_ubfe(hdr.z, sh, 6);
-        const float m1 = (float)__builtin_amdgcn_ubfe(hdr.z, sh + 8, 6);
-        const float m2 = (float)(__builtin_amdgcn_ubfe(hdr.w, sh + 4, 4) | (__builtin_amdgcn_ubfe(hdr.z, sh + 6, 2) << 4));
-        const float m3 = (float)(__builtin_amdgcn_ubfe(hdr.w, sh + 12, 4) | (__builtin_amdgcn_ubfe(hdr.z, sh + 14, 2) << 4));
-        const uint4 qa = s[i].qa, qb = s[i].qb;
-        const uint4 w0 = make_uint4(qa.x & 0x0f0f0f0fu, qa.y & 0x0f0f0f0fu, qa.z & 0x0f0f0f0fu, qa.w & 0x0f0f0f0fu);
-        const uint4 w1 = make_uint4((qa.x >> 4) & 0x0f0f0f0fu, (qa.y >> 4) & 0x0f0f0f0fu,
-                                    (qa.z >> 4) & 0x0f0f0f0fu, (qa.w >> 4) & 0x0f0f0f0fu);
-        const uint4 w2 = make_uint4(qb.x & 0x0f0f0f0fu, qb.y & 0x0f0f0f0fu, qb.z & 0x0f0f0f0fu, qb.w & 0x0f0f0f0fu);
-        const uint4 w3 = make_uint4((qb.x >> 4) & 0x0f0f0f0fu, (qb.y >> 4) & 0x0f0f0f0fu,
-                                    (qb.z >> 4) & 0x0f0f0f0fu, (qb.w >> 4) & 0x0f0f0f0fu);
+        const uint32_t ws = hi ? hdr.w : hdr.y, wm = hi ? hdr.w : hdr.z;
+        const uint32_t sc0 = __builtin_amdgcn_ubfe(ws, p0, wl) | (__builtin_amdgcn_ubfe(hdr.y, p0 + 6, wh) << 4);
+        const uint32_t sc1 = __builtin_amdgcn_ubfe(ws, p0 + 8, wl) | (__builtin_amdgcn_ubfe(hdr.y, p0 + 14, wh) << 4);
+        const uint32_t m0 = __builtin_amdgcn_ubfe(wm, p0 + mo, wl) | (__builtin_amdgcn_ubfe(hdr.z, p0 + 6, wh) << 4);
+        const uint32_t m1 = __builtin_amdgcn_ubfe(wm, p0 + 8 + mo, wl) | (__builtin_amdgcn_ubfe(hdr.z, p0 + 14, wh) << 4);
+        const float ds0 = d * (float)sc0, ds1 = d * (float)sc1;
+        const float dm0 = dmin * (float)m0, dm1 = dmin * (float)m1;
+        const uint4 la = lo_nibbles(s[i].qa), lb = lo_nibbles(s[i].qb);
+        const uint4 ha = hi_nibbles(s[i].qa), hb = hi_nibbles(s[i].qb);
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
-            const int A0 = dot16(w0, a[b][0]), A1 = dot16(w1, a[b][1]);
-            const int A2 = dot16(w2, a[b][2]), A3 = dot16(w3, a[b][3]);
-            float f = (float)__mul24(A0, sc0) * d8v[b].x;
-            f += (float)__mul24(A1, sc1) * d8v[b].y;
-            f += (float)__mul24(A2, sc2) * d8v[b].z;
-            f += (float)__mul24(A3, sc3) * d8v[b].w;
-            float g = m0 * dbq[b].x;
-            g += m1 * dbq[b].y;
-            g += m2 * dbq[b].z;
-            g += m3 * dbq[b].w;
-            acc[i][b] += d * f - dmin * g;
+            const int A0 = dot16(lb, a[b][1], dot16(la, a[b][0], 0));
+            const int A1 = dot16(hb, a[b][3], dot16(ha, a[b][2], 0));
+            float v = acc[i][b];
+            v = fmaf(ds0, (float)A0 * dzv[b].x, v);
+            v = fmaf(ds1, (float)A1 * dzv[b].y, v);
+            v = fmaf(-dm0, dzv[b].z, v);
+            v = fmaf(-dm1, dzv[b].w, v);
+            acc[i][b] = v;
         }
     }
 }
@@ -396,6 +390,81 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __r
     finish_rows<BATCH, RPW>(acc, y, residual, pair0, half, lane, m);
 }
 
+// K split over two wavefronts per row pair (the whole activation staged in
+// one piece): wavefront w of the first WH takes passes [0, np2) of its row
+// pair, wavefront WH + w the passes [np2, npass) of the same pair.  The second
+// half's row sums go through LDS and are added to the first half's in that
+// order, so results are deterministic; with one activation piece per
+// workgroup limited by LDS, this doubles the wavefronts streaming weights.
+template <int BATCH, int RPW, int WH>
+__global__ __launch_bounds__(128 * WH) void gemv_q4k_ksplit(const uint8_t* __restrict__ w,
+                                                            const uint8_t* __restrict__ xq,
+                                                            float* y, const float* residual,
+                                                            int m, int S, int schunk) {
+    extern __shared__ __align__(16) uint8_t smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int kh = wave / WH, wv = wave - kh * WH;   // K half, wavefront within the half
+    const int half = lane >> 5;
+    const int grp = (lane >> 2) & 7;
+    const int t = lane & 3;
+    const int64_t row_bytes = (int64_t)S * kQ4KBytes;
+    const int nb_row = S * 8;
+    const int npass = (S + 7) >> 3;
+    const int np2 = (npass + 1) >> 1;
+    const int pbeg = kh * np2, pend = min(npass, pbeg + np2);
+
+    float acc[RPW][BATCH];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) acc[i][b] = 0.0f;
+
+    const int pair0 = (blockIdx.x * WH + wv) * RPW;
+    Slice ring[RPW];
+    const uint8_t* rowp[RPW];
+    StageRegs<2> sr;   // the activation loads go first (see stage_issue)
+    stage_issue<BATCH, 128 * WH, 2>(sr, xq, nb_row, 0, S * 8, 0);
+    group_rows<RPW>(rowp, w, blockIdx.x, WH, wv, half, m, row_bytes);
+    if (pbeg < pend) load_pass<RPW>(ring, rowp, 8 * pbeg + grp, S, t);
+    stage_finish<BATCH, 128 * WH, 2>(sr, xq, nb_row, 0, S * 8, schunk, smem);
+
+    for (int p = pbeg; p < pend; ++p) {
+        if (8 * p + grp < S)   // lanes past the row end add nothing
+            compute_pass<BATCH, RPW>(ring, acc, smem, schunk, 8 * p + grp, t);
+        if (p + 1 < pend) load_pass<RPW>(ring, rowp, 8 * (p + 1) + grp, S, t);
+    }
+
+    float* red = (float*)(smem + (size_t)schunk * BATCH * kLdsPerSb);   // [WH*RPW*2][BATCH]
+    float v[RPW][BATCH];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) v[i][b] = half_wave_sum(acc[i][b]);
+    if (kh == 1 && (lane & 31) == 0) {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i)
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) red[((wv * RPW + i) * 2 + half) * BATCH + b] = v[i][b];
+    }
+    __syncthreads();
+    if (kh == 0 && (lane & 31) == 0) {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int r = 2 * (pair0 + i) + half;
+            if (r < m) {
+#pragma unroll
+                for (int b = 0; b < BATCH; ++b) {
+                    const float sum = v[i][b] + red[((wv * RPW + i) * 2 + half) * BATCH + b];
+                    const int64_t o = (int64_t)b * m + r;
+                    y[o] = residual ? residual[o] + sum : sum;
+                }
+            }
+        }
+    }
+}
+
 // Persistent form (the whole activation fits in LDS): a grid of a few
 // workgroups per compute unit stages the activation once and walks the row
 // groups blockIdx.x, blockIdx.x + gridDim.x, ... of all segments; the load
@@ -491,6 +560,21 @@ hipError_t launch_persistent(const Tab& tab, const void* xq, int64_t k, int schu
     return hipGetLastError();
 }
 
+// K-split launch (the whole activation in one piece of at most lds_limit).
+template <int BATCH, int RPW, int WH>
+hipError_t launch_ksplit(const void* w, const void* xq, float* y, const float* residual,
+                         int64_t m, int64_t k, int lds_limit, hipStream_t stream) {
+    const int S = (int)(k / kQK);
+    const int schunk = (S + 7) & ~7;
+    const size_t lds = (size_t)schunk * BATCH * kLdsPerSb + (size_t)WH * RPW * 2 * BATCH * 4;
+    if (lds > (size_t)lds_limit) return hipErrorInvalidConfiguration;
+    const int64_t ngroups = (m + WH * RPW * 2 - 1) / (WH * RPW * 2);
+    hipLaunchKernelGGL((gemv_q4k_ksplit<BATCH, RPW, WH>), dim3((unsigned)ngroups), dim3(128 * WH),
+                       lds, stream, (const uint8_t*)w, (const uint8_t*)xq, y, residual, (int)m, S,
+                       schunk);
+    return hipGetLastError();
+}
+
 // LDS chunk (superblocks per staged piece) of a batch under a budget; 0 if
 // not even one pass fits.
 template <int BATCH>
@@ -567,7 +651,9 @@ hipError_t launch_gemv_q4k(const void* w, const void* xq, float* y, const float*
                            : launch_variant<1, 1, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 4, stream);
         case 2: return launch_variant<2, 1, 1, 4>(w, xq, y, residual, m, k, one_piece, cus, 6, stream);
         case 3: return launch_variant<3, 1, 1, 4>(w, xq, y, residual, m, k, one_piece, cus, 6, stream);
-        case 4: return whole > 65536 ? launch_variant<4, 1, 1, 8>(w, xq, y, residual, m, k, one_piece, cus, 0, stream)
+        case 4: return whole > 65536 ? (whole + 4096 <= lds_limit
+                                            ? launch_ksplit<4, 1, 8>(w, xq, y, residual, m, k, lds_limit, stream)
+                                            : launch_variant<4, 1, 1, 8>(w, xq, y, residual, m, k, one_piece, cus, 0, stream))
                                      : launch_variant<4, 1, 1, 4>(w, xq, y, residual, m, k, one_piece, cus, 6, stream);
         case 5: return wide<5>(w, xq, y, residual, m, k, whole, one_piece, cus, stream);
         case 6: return wide<6>(w, xq, y, residual, m, k, whole, one_piece, cus, stream);
