@@ -59,18 +59,23 @@ struct Slice {      // one lane's share of one superblock of one row
     uint4 qb;       // code bytes [32t+16, 32t+32)
 };
 
-// LDS layout of one staged column (schunk superblocks):
-//   codes [schunk][256]   the superblock's 256 q8 codes; 16-byte unit u
-//                         (values 16u..16u+15) stored at unit u ^ (sb & 3);
-//                         lane t reads units 4t .. 4t+3 (blocks 2t, 2t+1);
-//   dz    [schunk][4]     float4 per lane t: d8 of blocks 2t and 2t+1, then
-//                         d8 * (sum of the block's 32 codes) for each.
-// The sixteen lanes that one LDS cycle serves are four lanes of each of
-// superblocks sb .. sb+3 (sb a multiple of 4); their reads of unit 4t + r
-// land on units 4t + (r ^ (sb & 3)): sixteen distinct 16-byte bank groups
-// (the 256-byte superblock stride alone would put all four superblocks on
-// the same banks).  The dz reads of those lanes are 256 contiguous bytes.
-constexpr int kLdsPerSb = 256 + 4 * 16;
+// LDS layout of a staged activation (schunk superblocks, BATCH columns): one
+// block of lds_per_sb(BATCH) bytes per superblock sb, holding
+//   codes [BATCH][256]    column b's 256 q8 codes; 16-byte unit u (values
+//                         16u..16u+15) stored at unit u ^ (sb & 3); lane t
+//                         reads units 4t .. 4t+3 (blocks 2t, 2t+1);
+//   dz    [DZ][4]         float4 per (column, lane t): d8 of blocks 2t and
+//                         2t+1, then d8 * (sum of the block's 32 codes) for
+//                         each; DZ = BATCH rounded up to an odd count.
+// Every column and dz offset is then a compile-time immediate from one base
+// per lane and pass.  The sixteen lanes that one LDS cycle serves are four
+// lanes t of each of superblocks sb .. sb+3 (sb a multiple of 4).  The block
+// stride is an odd multiple of 64 bytes modulo 256, so for the codes the
+// xor puts the four superblocks on different low unit bits and t on the
+// high ones, and for dz the superblocks land on different 64-byte quarters:
+// either way sixteen distinct 16-byte bank groups.
+constexpr int lds_dz_cols(int batch) { return batch + ((batch & 1) ? 0 : 1); }
+constexpr int lds_per_sb(int batch) { return batch * 256 + lds_dz_cols(batch) * 64; }
 
 __device__ __forceinline__ int swz(int sb) { return sb & 3; }
 
@@ -104,10 +109,7 @@ __device__ __forceinline__ void stage_issue(StageRegs<U>& r, const uint8_t* __re
 }
 
 template <int BATCH, int NT, int U>
-__device__ __forceinline__ void stage_write(const StageRegs<U>& r, int nbc, int base, int schunk,
-                                            uint8_t* lds) {
-    uint8_t* codes = lds;
-    float* dz = (float*)(lds + BATCH * schunk * 256);
+__device__ __forceinline__ void stage_write(const StageRegs<U>& r, int nbc, int base, uint8_t* lds) {
     const int total = BATCH * nbc;
 #pragma unroll
     for (int i = 0; i < U; ++i) {
@@ -121,11 +123,12 @@ __device__ __forceinline__ void stage_write(const StageRegs<U>& r, int nbc, int 
             int sq = 0;
 #pragma unroll
             for (int e = 1; e <= 8; ++e) sq = dot4(c[e], 0x01010101u, sq);
-            uint8_t* cs = codes + (bb * schunk + sb) * 256;
+            uint8_t* blk = lds + sb * lds_per_sb(BATCH);
+            uint8_t* cs = blk + bb * 256;
             const int x = swz(sb);
             *(uint4*)(cs + 16 * ((2 * jj) ^ x)) = make_uint4(c[1], c[2], c[3], c[4]);
             *(uint4*)(cs + 16 * ((2 * jj + 1) ^ x)) = make_uint4(c[5], c[6], c[7], c[8]);
-            float* dp = dz + ((bb * schunk + sb) * 4 + (jj >> 1)) * 4;
+            float* dp = (float*)(blk + BATCH * 256) + (bb * 4 + (jj >> 1)) * 4;
             dp[jj & 1] = d8;
             dp[2 + (jj & 1)] = d8 * (float)sq;
         }
@@ -136,12 +139,11 @@ __device__ __forceinline__ void stage_write(const StageRegs<U>& r, int nbc, int 
 // every later round, and the closing barrier.
 template <int BATCH, int NT, int U>
 __device__ __forceinline__ void stage_finish(StageRegs<U>& r, const uint8_t* __restrict__ xq,
-                                             int nb_row, int j0, int nbc, int schunk,
-                                             uint8_t* lds) {
-    stage_write<BATCH, NT, U>(r, nbc, 0, schunk, lds);
+                                             int nb_row, int j0, int nbc, uint8_t* lds) {
+    stage_write<BATCH, NT, U>(r, nbc, 0, lds);
     for (int base = NT * U; base < BATCH * nbc; base += NT * U) {
         stage_issue<BATCH, NT, U>(r, xq, nb_row, j0, nbc, base);
-        stage_write<BATCH, NT, U>(r, nbc, base, schunk, lds);
+        stage_write<BATCH, NT, U>(r, nbc, base, lds);
     }
     __syncthreads();
 }
@@ -149,10 +151,10 @@ __device__ __forceinline__ void stage_finish(StageRegs<U>& r, const uint8_t* __r
 // A whole staging (all loads of a round in flight before any is used).
 template <int BATCH, int NT, int U>
 __device__ __forceinline__ void stage_activation(const uint8_t* __restrict__ xq, int nb_row,
-                                                 int j0, int nbc, int schunk, uint8_t* lds) {
+                                                 int j0, int nbc, uint8_t* lds) {
     StageRegs<U> r;
     stage_issue<BATCH, NT, U>(r, xq, nb_row, j0, nbc, 0);
-    stage_finish<BATCH, NT, U>(r, xq, nb_row, j0, nbc, schunk, lds);
+    stage_finish<BATCH, NT, U>(r, xq, nb_row, j0, nbc, lds);
 }
 
 template <int RPW>
@@ -172,6 +174,19 @@ __device__ __forceinline__ int dot16(uint4 w, uint4 a, int c) {
     return dot4(w.w, a.w, dot4(w.z, a.z, dot4(w.y, a.y, dot4(w.x, a.x, c))));
 }
 
+// Byte-wise signed dot of four int8 pairs, from zero: the VOP3P form takes
+// the zero as an inline constant (the accumulating VOP2 form that the
+// compiler picks for the builtin needs a v_mov to clear its destination).
+__device__ __forceinline__ int dot4_z(uint32_t a, uint32_t b) {
+    int r;
+    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+__device__ __forceinline__ int dot16_z(uint4 w, uint4 a) {
+    return dot4(w.w, a.w, dot4(w.z, a.z, dot4(w.y, a.y, dot4_z(w.x, a.x))));
+}
+
 __device__ __forceinline__ uint4 lo_nibbles(uint4 q) {
     return make_uint4(q.x & 0x0f0f0f0fu, q.y & 0x0f0f0f0fu, q.z & 0x0f0f0f0fu, q.w & 0x0f0f0f0fu);
 }
@@ -183,20 +198,22 @@ __device__ __forceinline__ uint4 hi_nibbles(uint4 q) {
 
 template <int BATCH, int RPW>
 __device__ __forceinline__ void compute_pass(const Slice (&s)[RPW], float (&acc)[RPW][BATCH],
-                                             const uint8_t* lds, int schunk, int sl, int t) {
+                                             const uint8_t* lds, int sl, int t) {
     // activation of this lane for every column: read once, used by all rows
-    const uint8_t* codes = lds;
-    const float4* dz = (const float4*)(lds + BATCH * schunk * 256);
+    const uint8_t* blk = lds + sl * lds_per_sb(BATCH);
+    const uint8_t* cs = blk + 64 * t;
+    const float4* dz = (const float4*)(blk + BATCH * 256) + t;
     uint4 a[BATCH][4];
     float4 dzv[BATCH];
     const int x = swz(sl);
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-        const uint8_t* cs = codes + (b * schunk + sl) * 256 + 64 * t;
+    for (int r = 0; r < 4; ++r) {
+        const uint8_t* cr = cs + 16 * (r ^ x);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) a[b][r] = *(const uint4*)(cs + 16 * (r ^ x));
-        dzv[b] = dz[(b * schunk + sl) * 4 + t];
+        for (int b = 0; b < BATCH; ++b) a[b][r] = *(const uint4*)(cr + b * 256);
     }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) dzv[b] = dz[4 * b];
     // six-bit fields of sub-blocks j = 2t, 2t+1 (byte e = 2(t%2) + {0,1} of
     // a scale word): j < 4 -> scale = bits 0..5 of byte e of bytes 0..3, min
     // = the same of bytes 4..7; j >= 4 -> scale = low nibble of byte 8+e
@@ -221,8 +238,8 @@ __device__ __forceinline__ void compute_pass(const Slice (&s)[RPW], float (&acc)
         const uint4 ha = hi_nibbles(s[i].qa), hb = hi_nibbles(s[i].qb);
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
-            const int A0 = dot16(lb, a[b][1], dot16(la, a[b][0], 0));
-            const int A1 = dot16(hb, a[b][3], dot16(ha, a[b][2], 0));
+            const int A0 = dot16(lb, a[b][1], dot16_z(la, a[b][0]));
+            const int A1 = dot16(hb, a[b][3], dot16_z(ha, a[b][2]));
             float v = acc[i][b];
             v = fmaf(ds0, (float)A0 * dzv[b].x, v);
             v = fmaf(ds1, (float)A1 * dzv[b].y, v);
@@ -365,7 +382,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __r
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) load_pass<RPW>(ring[d], rowp, 8 * d + grp, S, t);
 
-    stage_finish<BATCH, 64 * WAVES, U>(sr, xq, nb_row, 0, min(schunk, S) * 8, schunk, smem);
+    stage_finish<BATCH, 64 * WAVES, U>(sr, xq, nb_row, 0, min(schunk, S) * 8, smem);
 
     for (int p0 = 0; p0 < npass; p0 += DEPTH) {
 #pragma unroll
@@ -378,10 +395,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __r
                     __syncthreads();
                     const int kc = chunk * schunk;
                     stage_activation<BATCH, 64 * WAVES, (BATCH == 1 ? 2 : 4)>(xq, nb_row, kc * 8,
-                                                        min(schunk, S - kc) * 8, schunk, smem);
+                                                        min(schunk, S - kc) * 8, smem);
                 }
                 if (8 * p + grp < S)   // lanes past the row end add nothing
-                    compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pl + grp, t);
+                    compute_pass<BATCH, RPW>(ring[d], acc, smem, 8 * pl + grp, t);
                 if (p + DEPTH < npass)
                     load_pass<RPW>(ring[d], rowp, 8 * (p + DEPTH) + grp, S, t);
             }
@@ -428,15 +445,15 @@ __global__ __launch_bounds__(128 * WH) void gemv_q4k_ksplit(const uint8_t* __res
     stage_issue<BATCH, 128 * WH, 2>(sr, xq, nb_row, 0, S * 8, 0);
     group_rows<RPW>(rowp, w, blockIdx.x, WH, wv, half, m, row_bytes);
     if (pbeg < pend) load_pass<RPW>(ring, rowp, 8 * pbeg + grp, S, t);
-    stage_finish<BATCH, 128 * WH, 2>(sr, xq, nb_row, 0, S * 8, schunk, smem);
+    stage_finish<BATCH, 128 * WH, 2>(sr, xq, nb_row, 0, S * 8, smem);
 
     for (int p = pbeg; p < pend; ++p) {
         if (8 * p + grp < S)   // lanes past the row end add nothing
-            compute_pass<BATCH, RPW>(ring, acc, smem, schunk, 8 * p + grp, t);
+            compute_pass<BATCH, RPW>(ring, acc, smem, 8 * p + grp, t);
         if (p + 1 < pend) load_pass<RPW>(ring, rowp, 8 * (p + 1) + grp, S, t);
     }
 
-    float* red = (float*)(smem + (size_t)schunk * BATCH * kLdsPerSb);   // [WH*RPW*2][BATCH]
+    float* red = (float*)(smem + (size_t)schunk * lds_per_sb(BATCH));   // [WH*RPW*2][BATCH]
     float v[RPW][BATCH];
 #pragma unroll
     for (int i = 0; i < RPW; ++i)
@@ -516,7 +533,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_persistent(const Tab sg,
             }
         }
     }
-    stage_finish<BATCH, 64 * WAVES, 2>(sr, xq, nb_row, 0, S * 8, schunk, smem);
+    stage_finish<BATCH, 64 * WAVES, 2>(sr, xq, nb_row, 0, S * 8, smem);
     int gc = blockIdx.x, pc = 0;
     SegCursor cc = seg_start(sg, gc);
     for (int it0 = 0; it0 < nitems; it0 += DEPTH) {
@@ -525,7 +542,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_persistent(const Tab sg,
             const int it = it0 + d;
             if (it < nitems) {
                 if (8 * pc + grp < S)   // lanes past the row end add nothing
-                    compute_pass<BATCH, RPW>(ring[d], acc, smem, schunk, 8 * pc + grp, t);
+                    compute_pass<BATCH, RPW>(ring[d], acc, smem, 8 * pc + grp, t);
                 if (it + DEPTH < nitems) {
                     load_pass<RPW>(ring[d], rowp, 8 * pl + grp, S, t);
                     if (++pl == npass) {
@@ -566,7 +583,7 @@ hipError_t launch_ksplit(const void* w, const void* xq, float* y, const float* r
                          int64_t m, int64_t k, int lds_limit, hipStream_t stream) {
     const int S = (int)(k / kQK);
     const int schunk = (S + 7) & ~7;
-    const size_t lds = (size_t)schunk * BATCH * kLdsPerSb + (size_t)WH * RPW * 2 * BATCH * 4;
+    const size_t lds = (size_t)schunk * lds_per_sb(BATCH) + (size_t)WH * RPW * 2 * BATCH * 4;
     if (lds > (size_t)lds_limit) return hipErrorInvalidConfiguration;
     const int64_t ngroups = (m + WH * RPW * 2 - 1) / (WH * RPW * 2);
     hipLaunchKernelGGL((gemv_q4k_ksplit<BATCH, RPW, WH>), dim3((unsigned)ngroups), dim3(128 * WH),
@@ -580,7 +597,7 @@ hipError_t launch_ksplit(const void* w, const void* xq, float* y, const float* r
 template <int BATCH>
 int chunk_for(int64_t k, int lds_budget) {
     const int S = (int)(k / kQK);
-    int schunk = (lds_budget / (BATCH * kLdsPerSb)) & ~7;      // whole passes of 8 superblocks
+    int schunk = (lds_budget / lds_per_sb(BATCH)) & ~7;      // whole passes of 8 superblocks
     const int s_round = (S + 7) & ~7;
     if (schunk > s_round) schunk = s_round;
     return schunk < 8 ? 0 : schunk;
@@ -597,7 +614,7 @@ hipError_t launch_variant(const void* w, const void* xq, float* y, const float* 
     const int S = (int)(k / kQK);
     const int schunk = chunk_for<BATCH>(k, lds_budget);
     if (schunk == 0) return hipErrorInvalidConfiguration;
-    const size_t lds = (size_t)schunk * BATCH * kLdsPerSb;
+    const size_t lds = (size_t)schunk * lds_per_sb(BATCH);
     if (persist_per_cu > 0 && schunk >= S) {
         const int rows_per_group = WAVES * RPW * 2;
         const Seg1 tab{(const uint8_t*)w, y, residual, (int)m,
@@ -643,7 +660,7 @@ hipError_t launch_gemv_q4k(const void* w, const void* xq, float* y, const float*
     // at batch 4: 14.6 us against 15.4 with three passes in flight).
     const int S = (int)(k / kQK);
     const int64_t s_round = (S + 7) & ~7;
-    const int64_t whole = (int64_t)batch * kLdsPerSb * s_round;
+    const int64_t whole = (int64_t)lds_per_sb(batch) * s_round;
     const int one_piece = whole <= lds_limit ? lds_limit : 65536;
     const bool big = m >= 16384 || S > 16;
     switch (batch) {
@@ -679,7 +696,7 @@ hipError_t launch_segs(const Segs& sg, const void* xq, int64_t k, int lds_budget
             tab.g0[s + 1] = tab.g0[s] + (tab.m[s] + rows_per_group - 1) / rows_per_group;
         tab.ngroups = tab.g0[tab.n];
         return launch_persistent<BATCH, RPW, DEPTH, WAVES>(
-            tab, xq, k, schunk, (size_t)schunk * BATCH * kLdsPerSb, cus, per_cu, stream);
+            tab, xq, k, schunk, (size_t)schunk * lds_per_sb(BATCH), cus, per_cu, stream);
     }
     for (int s = 0; s < sg.n; ++s) {
         if (sg.m[s] == 0) continue;
@@ -707,7 +724,7 @@ hipError_t launch_gemv_q4k_seg(int nseg, const void* const* w, const int64_t* m,
     }
     // the single-tensor launch shapes, chosen on the launch's total rows
     const int S = (int)(k / kQK);
-    const int64_t whole = (int64_t)batch * kLdsPerSb * ((S + 7) & ~7);
+    const int64_t whole = (int64_t)lds_per_sb(batch) * ((S + 7) & ~7);
     const bool big = total >= 16384 || S > 16;
     const int fit = whole > 65536 ? 0 : 65536;   // 0: one ordinary launch per segment
     switch (batch) {
