@@ -79,58 +79,123 @@ constexpr int lds_per_sb(int batch) { return batch * 256 + lds_dz_cols(batch) * 
 
 __device__ __forceinline__ int swz(int sb) { return sb & 3; }
 
-// Staging of blocks [j0, j0 + nbc) of every column (nbc a multiple of 8):
-// one thread per (column, q8_1 block), U blocks per thread per round.  A
-// round is split into the issue of its global loads (into StageRegs) and the
-// LDS writes, so a kernel can issue the first round's loads before its weight
-// loads: loads complete in issue order, and activation loads issued after the
-// weight ring would have to wait for the weights' HBM latency before the
-// staging could finish.
-template <int U>
+// Staging of blocks [j0, j0 + nbc) of every column (j0, nbc multiples of 8),
+// U items per thread per round, in one of two forms:
+//   * BATCH >= 4: an item is a (column, run of 4 q8_1 blocks).  A run is 144
+//     bytes and starts 16-byte aligned (xq is 16-byte aligned, a column is
+//     288 * S bytes, j0 a multiple of 8), so it comes in nine 16-byte loads
+//     whose dwords are its four blocks, and the lane's d8 values leave in
+//     two float4 writes;
+//   * fewer columns: an item is one (column, block), nine dword loads.  The
+//     code words of a run's blocks sit at odd dword offsets of its load
+//     registers and must be copied into aligned quads for the 16-byte LDS
+//     writes; the small-batch kernels cannot spare those registers (batch 1:
+//     59 -> 102 VGPRs), and a small batch has little to stage.
+// A round is split into the issue of its global loads (into StageRegs) and
+// the LDS writes, so a kernel can issue the first round's loads before its
+// weight loads: loads complete in issue order, and activation loads issued
+// after the weight ring would have to wait for the weights' HBM latency
+// before the staging could finish.
+template <int BATCH>
+constexpr bool stage_runs() { return BATCH >= 4; }
+
+template <int BATCH>
+__device__ __forceinline__ int stage_items(int nbc) { return stage_runs<BATCH>() ? BATCH * (nbc >> 2) : BATCH * nbc; }
+
+template <int BATCH, int U>
 struct StageRegs {
-    uint32_t c[U][9];
+    uint4 q[stage_runs<BATCH>() ? U : 1][9];    // runs
+    uint32_t c[stage_runs<BATCH>() ? 1 : U][9];  // single blocks
 };
 
+// Column of item `idx` (n items per column), without a division.
+template <int BATCH>
+__device__ __forceinline__ int column_of(int idx, int n) {
+    int bb = 0;
+#pragma unroll
+    for (int c = 1; c < BATCH; ++c) bb += idx >= c * n ? 1 : 0;
+    return bb;
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4 (&c)[9], int w) {   // w a constant
+    const uint4 v = c[w >> 2];
+    return (w & 3) == 0 ? v.x : (w & 3) == 1 ? v.y : (w & 3) == 2 ? v.z : v.w;
+}
+
 template <int BATCH, int NT, int U>
-__device__ __forceinline__ void stage_issue(StageRegs<U>& r, const uint8_t* __restrict__ xq,
+__device__ __forceinline__ void stage_issue(StageRegs<BATCH, U>& r, const uint8_t* __restrict__ xq,
                                             int nb_row, int j0, int nbc, int base) {
-    const int total = BATCH * nbc;
+    constexpr bool runs = stage_runs<BATCH>();
+    const int per_col = runs ? nbc >> 2 : nbc;
+    const int total = BATCH * per_col;
 #pragma unroll
     for (int i = 0; i < U; ++i) {
         const int idx = base + i * NT + (int)threadIdx.x;
         if (idx < total) {
-            const int bb = BATCH == 1 ? 0 : idx / nbc;
-            const int j = idx - bb * nbc;
-            const uint32_t* blk = (const uint32_t*)(xq + ((int64_t)bb * nb_row + j0 + j) * kQ81Bytes);
+            const int bb = column_of<BATCH>(idx, per_col);
+            const int j = idx - bb * per_col;
+            if constexpr (runs) {
+                const uint8_t* run = xq + ((int64_t)bb * nb_row + j0 + 4 * j) * kQ81Bytes;
 #pragma unroll
-            for (int e = 0; e < 9; ++e) r.c[i][e] = blk[e];
+                for (int e = 0; e < 9; ++e) r.q[i][e] = load16(run + 16 * e);
+            } else {
+                const uint32_t* blk = (const uint32_t*)(xq + ((int64_t)bb * nb_row + j0 + j) * kQ81Bytes);
+#pragma unroll
+                for (int e = 0; e < 9; ++e) r.c[i][e] = blk[e];
+            }
         }
     }
 }
 
+// Codes and d8 values of block jj (0..7) of superblock sb, column bb; the
+// block's nine words come from `word(0..8)` (d|s word, then the 8 code words).
+template <int BATCH, class Word>
+__device__ __forceinline__ void stage_block(uint8_t* lds, int bb, int sb, int jj, Word word,
+                                            float& d8, float& z) {
+    uint8_t* cs = lds + sb * lds_per_sb(BATCH) + bb * 256;
+    const int x = swz(sb);
+    d8 = half_bits_to_float(word(0));
+    int sq = 0;
+#pragma unroll
+    for (int u = 1; u <= 8; ++u) sq = dot4(word(u), 0x01010101u, sq);
+    z = d8 * (float)sq;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        *(uint4*)(cs + 16 * ((2 * jj + h) ^ x)) =
+            make_uint4(word(1 + 4 * h), word(2 + 4 * h), word(3 + 4 * h), word(4 + 4 * h));
+}
+
 template <int BATCH, int NT, int U>
-__device__ __forceinline__ void stage_write(const StageRegs<U>& r, int nbc, int base, uint8_t* lds) {
-    const int total = BATCH * nbc;
+__device__ __forceinline__ void stage_write(const StageRegs<BATCH, U>& r, int nbc, int base,
+                                            uint8_t* lds) {
+    constexpr bool runs = stage_runs<BATCH>();
+    const int per_col = runs ? nbc >> 2 : nbc;
+    const int total = BATCH * per_col;
 #pragma unroll
     for (int i = 0; i < U; ++i) {
         const int idx = base + i * NT + (int)threadIdx.x;
         if (idx < total) {
-            const int bb = BATCH == 1 ? 0 : idx / nbc;
-            const int j = idx - bb * nbc;
-            const int sb = j >> 3, jj = j & 7;
-            const uint32_t* c = r.c[i];
-            const float d8 = half_bits_to_float(c[0]);
-            int sq = 0;
+            const int bb = column_of<BATCH>(idx, per_col);
+            const int j = idx - bb * per_col;
+            if constexpr (runs) {
+                const int sb = j >> 1, hq = j & 1;   // blocks 4hq .. 4hq+3 of superblock sb
+                float v[2][4];                       // lanes 2hq, 2hq+1
 #pragma unroll
-            for (int e = 1; e <= 8; ++e) sq = dot4(c[e], 0x01010101u, sq);
-            uint8_t* blk = lds + sb * lds_per_sb(BATCH);
-            uint8_t* cs = blk + bb * 256;
-            const int x = swz(sb);
-            *(uint4*)(cs + 16 * ((2 * jj) ^ x)) = make_uint4(c[1], c[2], c[3], c[4]);
-            *(uint4*)(cs + 16 * ((2 * jj + 1) ^ x)) = make_uint4(c[5], c[6], c[7], c[8]);
-            float* dp = (float*)(blk + BATCH * 256) + (bb * 4 + (jj >> 1)) * 4;
-            dp[jj & 1] = d8;
-            dp[2 + (jj & 1)] = d8 * (float)sq;
+                for (int e = 0; e < 4; ++e)
+                    stage_block<BATCH>(lds, bb, sb, 4 * hq + e,
+                                       [&](int u) { return word_of(r.q[i], 9 * e + u); },
+                                       v[e >> 1][e & 1], v[e >> 1][2 + (e & 1)]);
+                float4* dp = (float4*)(lds + sb * lds_per_sb(BATCH) + BATCH * 256) + bb * 4 + 2 * hq;
+                dp[0] = make_float4(v[0][0], v[0][1], v[0][2], v[0][3]);
+                dp[1] = make_float4(v[1][0], v[1][1], v[1][2], v[1][3]);
+            } else {
+                const int sb = j >> 3, jj = j & 7;
+                float d8, z;
+                stage_block<BATCH>(lds, bb, sb, jj, [&](int u) { return r.c[i][u]; }, d8, z);
+                float* dp = (float*)(lds + sb * lds_per_sb(BATCH) + BATCH * 256) + (bb * 4 + (jj >> 1)) * 4;
+                dp[jj & 1] = d8;
+                dp[2 + (jj & 1)] = z;
+            }
         }
     }
 }
@@ -138,10 +203,10 @@ __device__ __forceinline__ void stage_write(const StageRegs<U>& r, int nbc, int 
 // The rest of a staging whose first round was issued into r: its LDS writes,
 // every later round, and the closing barrier.
 template <int BATCH, int NT, int U>
-__device__ __forceinline__ void stage_finish(StageRegs<U>& r, const uint8_t* __restrict__ xq,
+__device__ __forceinline__ void stage_finish(StageRegs<BATCH, U>& r, const uint8_t* __restrict__ xq,
                                              int nb_row, int j0, int nbc, uint8_t* lds) {
     stage_write<BATCH, NT, U>(r, nbc, 0, lds);
-    for (int base = NT * U; base < BATCH * nbc; base += NT * U) {
+    for (int base = NT * U; base < stage_items<BATCH>(nbc); base += NT * U) {
         stage_issue<BATCH, NT, U>(r, xq, nb_row, j0, nbc, base);
         stage_write<BATCH, NT, U>(r, nbc, base, lds);
     }
@@ -152,7 +217,7 @@ __device__ __forceinline__ void stage_finish(StageRegs<U>& r, const uint8_t* __r
 template <int BATCH, int NT, int U>
 __device__ __forceinline__ void stage_activation(const uint8_t* __restrict__ xq, int nb_row,
                                                  int j0, int nbc, uint8_t* lds) {
-    StageRegs<U> r;
+    StageRegs<BATCH, U> r;
     stage_issue<BATCH, NT, U>(r, xq, nb_row, j0, nbc, 0);
     stage_finish<BATCH, NT, U>(r, xq, nb_row, j0, nbc, lds);
 }
@@ -375,13 +440,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __r
     const uint8_t* rowp[RPW];
     const int pair0 = (blockIdx.x * WAVES + wave) * RPW;   // first row pair of this wave
     const int chunk_passes = schunk >> 3;   // schunk is a multiple of 8 superblocks
-    constexpr int U = BATCH == 1 ? 2 : 4;
-    StageRegs<U> sr;   // the activation loads go first (see stage_issue)
+    constexpr int U = stage_runs<BATCH>() ? 1 : (BATCH == 1 ? 2 : 4);
+    StageRegs<BATCH, U> sr;   // the activation loads go first (see stage_issue)
     stage_issue<BATCH, 64 * WAVES, U>(sr, xq, nb_row, 0, min(schunk, S) * 8, 0);
     group_rows<RPW>(rowp, w, blockIdx.x, WAVES, wave, half, m, row_bytes);
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) load_pass<RPW>(ring[d], rowp, 8 * d + grp, S, t);
-
+    __builtin_amdgcn_sched_barrier(0);   // keep the staging arithmetic after the weight loads
     stage_finish<BATCH, 64 * WAVES, U>(sr, xq, nb_row, 0, min(schunk, S) * 8, smem);
 
     for (int p0 = 0; p0 < npass; p0 += DEPTH) {
@@ -394,7 +459,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __r
                 if (pl == 0 && p > 0) {                    // uniform over the workgroup
                     __syncthreads();
                     const int kc = chunk * schunk;
-                    stage_activation<BATCH, 64 * WAVES, (BATCH == 1 ? 2 : 4)>(xq, nb_row, kc * 8,
+                    stage_activation<BATCH, 64 * WAVES, U>(xq, nb_row, kc * 8,
                                                         min(schunk, S - kc) * 8, smem);
                 }
                 if (8 * p + grp < S)   // lanes past the row end add nothing
@@ -441,11 +506,13 @@ __global__ __launch_bounds__(128 * WH) void gemv_q4k_ksplit(const uint8_t* __res
     const int pair0 = (blockIdx.x * WH + wv) * RPW;
     Slice ring[RPW];
     const uint8_t* rowp[RPW];
-    StageRegs<2> sr;   // the activation loads go first (see stage_issue)
-    stage_issue<BATCH, 128 * WH, 2>(sr, xq, nb_row, 0, S * 8, 0);
+    constexpr int U = stage_runs<BATCH>() ? 1 : 2;
+    StageRegs<BATCH, U> sr;   // the activation loads go first (see stage_issue)
+    stage_issue<BATCH, 128 * WH, U>(sr, xq, nb_row, 0, S * 8, 0);
     group_rows<RPW>(rowp, w, blockIdx.x, WH, wv, half, m, row_bytes);
-    if (pbeg < pend) load_pass<RPW>(ring, rowp, 8 * pbeg + grp, S, t);
-    stage_finish<BATCH, 128 * WH, 2>(sr, xq, nb_row, 0, S * 8, smem);
+    load_pass<RPW>(ring, rowp, 8 * pbeg + grp, S, t);   // unconditional (clamped): no merge
+    __builtin_amdgcn_sched_barrier(0);   // keep the staging arithmetic after the weight loads
+    stage_finish<BATCH, 128 * WH, U>(sr, xq, nb_row, 0, S * 8, smem);
 
     for (int p = pbeg; p < pend; ++p) {
         if (8 * p + grp < S)   // lanes past the row end add nothing
@@ -514,8 +581,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_persistent(const Tab sg,
     const uint8_t* rowp[RPW];
     // (group, pass) of the next item to load and of the next to compute
     int gl = blockIdx.x, pl = 0;
-    StageRegs<2> sr;   // the activation loads go first (see stage_issue)
-    stage_issue<BATCH, 64 * WAVES, 2>(sr, xq, nb_row, 0, S * 8, 0);
+    constexpr int U = stage_runs<BATCH>() ? 1 : 2;
+    StageRegs<BATCH, U> sr;   // the activation loads go first (see stage_issue)
+    stage_issue<BATCH, 64 * WAVES, U>(sr, xq, nb_row, 0, S * 8, 0);
     SegCursor cl = seg_start(sg, gl);
     auto rows_of = [&](int g) {
         seg_seek(cl, sg, g);
@@ -533,7 +601,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_persistent(const Tab sg,
             }
         }
     }
-    stage_finish<BATCH, 64 * WAVES, 2>(sr, xq, nb_row, 0, S * 8, smem);
+    __builtin_amdgcn_sched_barrier(0);   // keep the staging arithmetic after the weight loads
+    stage_finish<BATCH, 64 * WAVES, U>(sr, xq, nb_row, 0, S * 8, smem);
     int gc = blockIdx.x, pc = 0;
     SegCursor cc = seg_start(sg, gc);
     for (int it0 = 0; it0 < nitems; it0 += DEPTH) {
