@@ -264,21 +264,6 @@ __device__ __forceinline__ uint4 hi_nibbles(uint4 q) {
 template <int BATCH, int RPW>
 __device__ __forceinline__ void compute_pass(const Slice (&s)[RPW], float (&acc)[RPW][BATCH],
                                              const uint8_t* lds, int sl, int t) {
-    // activation of this lane for every column: read once, used by all rows
-    const uint8_t* blk = lds + sl * lds_per_sb(BATCH);
-    const uint8_t* cs = blk + 64 * t;
-    const float4* dz = (const float4*)(blk + BATCH * 256) + t;
-    uint4 a[BATCH][4];
-    float4 dzv[BATCH];
-    const int x = swz(sl);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint8_t* cr = cs + 16 * (r ^ x);
-#pragma unroll
-        for (int b = 0; b < BATCH; ++b) a[b][r] = *(const uint4*)(cr + b * 256);
-    }
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b) dzv[b] = dz[4 * b];
     // six-bit fields of sub-blocks j = 2t, 2t+1 (byte e = 2(t%2) + {0,1} of
     // a scale word): j < 4 -> scale = bits 0..5 of byte e of bytes 0..3, min
     // = the same of bytes 4..7; j >= 4 -> scale = low nibble of byte 8+e
@@ -287,6 +272,8 @@ __device__ __forceinline__ void compute_pass(const Slice (&s)[RPW], float (&acc)
     const bool hi = t >= 2;
     const uint32_t p0 = 16u * (uint32_t)(t & 1);
     const uint32_t wl = hi ? 4u : 6u, wh = hi ? 2u : 0u, mo = hi ? 4u : 0u;
+    float ds0[RPW], ds1[RPW], dm0[RPW], dm1[RPW];
+    uint4 la[RPW], lb[RPW], ha[RPW], hb[RPW];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const uint4 hdr = s[i].hdr;
@@ -297,19 +284,35 @@ __device__ __forceinline__ void compute_pass(const Slice (&s)[RPW], float (&acc)
         const uint32_t sc1 = __builtin_amdgcn_ubfe(ws, p0 + 8, wl) | (__builtin_amdgcn_ubfe(hdr.y, p0 + 14, wh) << 4);
         const uint32_t m0 = __builtin_amdgcn_ubfe(wm, p0 + mo, wl) | (__builtin_amdgcn_ubfe(hdr.z, p0 + 6, wh) << 4);
         const uint32_t m1 = __builtin_amdgcn_ubfe(wm, p0 + 8 + mo, wl) | (__builtin_amdgcn_ubfe(hdr.z, p0 + 14, wh) << 4);
-        const float ds0 = d * (float)sc0, ds1 = d * (float)sc1;
-        const float dm0 = dmin * (float)m0, dm1 = dmin * (float)m1;
-        const uint4 la = lo_nibbles(s[i].qa), lb = lo_nibbles(s[i].qb);
-        const uint4 ha = hi_nibbles(s[i].qa), hb = hi_nibbles(s[i].qb);
+        ds0[i] = d * (float)sc0;
+        ds1[i] = d * (float)sc1;
+        dm0[i] = dmin * (float)m0;
+        dm1[i] = dmin * (float)m1;
+        la[i] = lo_nibbles(s[i].qa);
+        lb[i] = lo_nibbles(s[i].qb);
+        ha[i] = hi_nibbles(s[i].qa);
+        hb[i] = hi_nibbles(s[i].qb);
+    }
+    // then one column at a time: its activation slice of this lane (units
+    // 4t .. 4t+3 and the d8 float4), used by every row
+    const uint8_t* cs = lds + sl * lds_per_sb(BATCH) + 64 * t;
+    const float4* dz = (const float4*)(lds + sl * lds_per_sb(BATCH) + BATCH * 256) + t;
+    const int x = swz(sl);
 #pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
-            const int A0 = dot16(lb, a[b][1], dot16_z(la, a[b][0]));
-            const int A1 = dot16(hb, a[b][3], dot16_z(ha, a[b][2]));
+    for (int b = 0; b < BATCH; ++b) {
+        uint4 a[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[r] = *(const uint4*)(cs + 16 * (r ^ x) + b * 256);
+        const float4 z = dz[4 * b];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int A0 = dot16(lb[i], a[1], dot16_z(la[i], a[0]));
+            const int A1 = dot16(hb[i], a[3], dot16_z(ha[i], a[2]));
             float v = acc[i][b];
-            v = fmaf(ds0, (float)A0 * dzv[b].x, v);
-            v = fmaf(ds1, (float)A1 * dzv[b].y, v);
-            v = fmaf(-dm0, dzv[b].z, v);
-            v = fmaf(-dm1, dzv[b].w, v);
+            v = fmaf(ds0[i], (float)A0 * z.x, v);
+            v = fmaf(ds1[i], (float)A1 * z.y, v);
+            v = fmaf(-dm0[i], z.z, v);
+            v = fmaf(-dm1[i], z.w, v);
             acc[i][b] = v;
         }
     }
@@ -476,8 +479,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4k_kernel(const uint8_t* __r
 // one piece): wavefront w of the first WH takes passes [0, np2) of its row
 // pair, wavefront WH + w the passes [np2, npass) of the same pair.  The second
 // half's row sums go through LDS and are added to the first half's in that
-// order, so results are deterministic; with one activation piece per
+// order, so results are deterministic.  With one activation piece per
 // workgroup limited by LDS, this doubles the wavefronts streaming weights.
+// One pass is in flight per wavefront: requesting all of a wavefront's
+// passes together with the staging was slower (the staging and the barrier
+// then finish behind the weight loads, and the passes run back to back).
 template <int BATCH, int RPW, int WH>
 __global__ __launch_bounds__(128 * WH) void gemv_q4k_ksplit(const uint8_t* __restrict__ w,
                                                             const uint8_t* __restrict__ xq,
