@@ -239,19 +239,6 @@ __device__ __forceinline__ int dot16(uint4 w, uint4 a, int c) {
     return dot4(w.w, a.w, dot4(w.z, a.z, dot4(w.y, a.y, dot4(w.x, a.x, c))));
 }
 
-// Byte-wise signed dot of four int8 pairs, from zero: the VOP3P form takes
-// the zero as an inline constant (the accumulating VOP2 form that the
-// compiler picks for the builtin needs a v_mov to clear its destination).
-__device__ __forceinline__ int dot4_z(uint32_t a, uint32_t b) {
-    int r;
-    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
-
-__device__ __forceinline__ int dot16_z(uint4 w, uint4 a) {
-    return dot4(w.w, a.w, dot4(w.z, a.z, dot4(w.y, a.y, dot4_z(w.x, a.x))));
-}
-
 __device__ __forceinline__ uint4 lo_nibbles(uint4 q) {
     return make_uint4(q.x & 0x0f0f0f0fu, q.y & 0x0f0f0f0fu, q.z & 0x0f0f0f0fu, q.w & 0x0f0f0f0fu);
 }

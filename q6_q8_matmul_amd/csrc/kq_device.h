@@ -37,6 +37,20 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
+// Byte-wise signed dot of four int8 pairs, from zero: the VOP3P form takes
+// the zero as an inline constant (the accumulating VOP2 form that the
+// compiler picks for the builtin needs a v_mov to clear its destination).
+__device__ __forceinline__ int dot4_z(uint32_t a, uint32_t b) {
+    int r;
+    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// Dot of 16 int8 pairs (one 16-byte slice each), from zero.
+__device__ __forceinline__ int dot16_z(uint4 w, uint4 a) {
+    return dot4(w.w, a.w, dot4(w.z, a.z, dot4(w.y, a.y, dot4_z(w.x, a.x))));
+}
+
 // Sum over the 64 lanes of a wavefront with a fixed xor-butterfly order;
 // every lane receives the same total.
 __device__ __forceinline__ float wave_sum(float v) {
