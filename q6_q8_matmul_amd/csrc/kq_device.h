@@ -144,9 +144,9 @@ hipError_t launch_gemv_q6k(const void* w, const void* xq, float* y, const float*
 hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                           int64_t k, hipStream_t stream);
 hipError_t launch_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
-                          int64_t k, hipStream_t stream);
+                          int64_t k, int cus, hipStream_t stream);
 hipError_t launch_mmq_q6k_split(const void* wr, const void* xq, float* y, int64_t m, int64_t n,
-                                int64_t k, hipStream_t stream);
+                                int64_t k, int cus, hipStream_t stream);
 hipError_t launch_gemv_q6k_split(const void* wr, const void* xq, float* y, const float* residual,
                                  int64_t m, int64_t k, int batch, int lds_limit, int cus,
                                  hipStream_t stream);

@@ -19,16 +19,19 @@
 // one shift-add, one conversion and one fused multiply-add by d8 per output
 // and block; d (and the sign) is applied once per superblock.
 //
-// Tiling: a workgroup (4 wavefronts) computes 128 weight rows x 128 tokens;
-// wavefront w owns rows 32w .. 32w+31 and all 128 tokens (four 32 x 32 MFMA
-// tiles), so every weight value is decoded by exactly one lane.  Per
+// Tiling: a workgroup (4 wavefronts) computes 128 weight rows x BN = 32 NT
+// tokens; wavefront w owns rows 32w .. 32w+31 and all BN tokens (NT 32 x 32
+// MFMA tiles), so every weight value is decoded by exactly one lane.  NT = 4
+// (BN = 128) amortises the decode over the most tiles; a product whose
+// 128 x 128 grid would leave compute units idle (the 512-row value
+// projection: 64 workgroups for 256 CUs) takes NT = 2 or 1.  Per
 // superblock (256 values = 8 q8_1 blocks), every global load of a stage
 // issued before the first LDS write:
 //   * the 210-byte superblocks of the 128 rows -> LDS, realigned to 4 bytes
 //     (every other superblock starts at 2 mod 4; 4-byte-aligned 16-byte
 //     loads plus a 16-bit funnel shift, never reading outside the weight
 //     tensor); -d per row as f32;
-//   * the q8_1 blocks of the 128 tokens -> LDS as int8 codes (token rows
+//   * the q8_1 blocks of the BN tokens -> LDS as int8 codes (token rows
 //     padded to 272 bytes) and f32 d8 per (token, block).
 // Outputs beyond m or n are computed from clamped (valid) rows/tokens and not
 // stored.  No atomics; results are bitwise reproducible.
@@ -43,16 +46,17 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 128;            // weight rows per workgroup
-constexpr int BN = 128;            // tokens per workgroup
 constexpr int kRawDw = 56;         // LDS dwords per row: 53 used (212 B), 16-byte aligned rows
 constexpr int kCodeStride = 272;   // LDS bytes per token row of codes (256 + 16 pad)
 constexpr int kTokStride = 9;      // floats per token in the d8 plane (8 + 1 pad)
 
+template <int NT>
 struct Smem {
-    uint32_t wraw[BM * kRawDw];        // realigned Q6_K superblock per row
-    float negd[BM];                    // -d per row
-    int8_t codes[BN * kCodeStride];    // q8 codes per token
-    float d8[BN * kTokStride];         // per (token, block)
+    static constexpr int BN = 32 * NT;   // tokens per workgroup
+    uint32_t wraw[BM * kRawDw];          // realigned Q6_K superblock per row
+    float negd[BM];                      // -d per row
+    int8_t codes[BN * kCodeStride];      // q8 codes per token
+    float d8[BN * kTokStride];           // per (token, block)
 };
 
 // Four 6-bit codes (one per byte, 0..63) -> the int8 operand bytes a and b
@@ -73,11 +77,12 @@ __device__ __forceinline__ void split4(uint32_t q, u16x2 nsc, u16x2 c32, uint32_
 
 // SPLIT: the weights are in the split layout (208-byte bodies at w, 16-byte
 // aligned, and the f16 d of superblock row * S + s at wd[row * S + s]).
-template <bool SPLIT>
+template <int NT, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ wd,
                     const uint8_t* __restrict__ xq, float* __restrict__ y, int M, int N, int S) {
-    __shared__ __align__(16) Smem sm;
+    constexpr int BN = Smem<NT>::BN;
+    __shared__ __align__(16) Smem<NT> sm;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -89,9 +94,9 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ 
     const int nb_row = S * 8;
     const int r = wave * 32 + l32;   // this lane's weight row within the tile
 
-    float acc[4][16];
+    float acc[NT][16];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < NT; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
 
@@ -100,8 +105,8 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ 
         // Weights: two threads per row; thread (row, e) takes the 16-byte
         // chunks e, e+2, ... of the superblock's bytes 0..207 (13 chunks),
         // realigned to the superblock start; the odd thread also takes the
-        // f16 d at bytes 208..209.  Activations: 128 tokens x 8 q8_1 blocks,
-        // four (token, block) pairs per thread.
+        // f16 d at bytes 208..209.  Activations: BN tokens x 8 q8_1 blocks,
+        // NT (token, block) pairs per thread.
         {
             // recompute the staging addresses every superblock: kept live
             // across the MFMA loop they would cost registers it needs
@@ -124,10 +129,10 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ 
                 }
             }
             const uint32_t dbits = !e ? 0u : SPLIT ? (uint32_t)wd[g] : (uint32_t) * (const uint16_t*)(p + 208);
-            uint4 c0[4], c1[4];
-            uint32_t hd[4];
+            uint4 c0[NT], c1[NT];
+            uint32_t hd[NT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < NT; ++i) {
                 const int idx = ts + 256 * i;
                 const int t = idx >> 3, j = idx & 7;
                 const int gt = min(n0 + t, N - 1);
@@ -155,7 +160,7 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ 
                 sm.negd[rr] = -half_bits_to_float(dbits);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < NT; ++i) {
                 const int idx = tid + 256 * i;
                 const int t = idx >> 3, j = idx & 7;
                 uint4* dst = (uint4*)(sm.codes + t * kCodeStride + 32 * j);
@@ -166,9 +171,9 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ 
         }
         __syncthreads();
 
-        float pt[4][16];
+        float pt[NT][16];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NT; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) pt[b][i] = 0.0f;
 
@@ -206,7 +211,7 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ 
                 const v4i A = v4i{(int)av[0], (int)av[1], (int)av[2], (int)av[3]};
                 const v4i B = v4i{(int)bv[0], (int)bv[1], (int)bv[2], (int)bv[3]};
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
+                for (int nt = 0; nt < NT; ++nt) {
                     const int t = nt * 32 + l32;
                     const uint4 x = *(const uint4*)(sm.codes + t * kCodeStride + 32 * j + 16 * h2);
                     const v4i X = v4i{(int)x.x, (int)x.y, (int)x.z, (int)x.w};
@@ -228,7 +233,7 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ 
             nd[4 * g + 0] = v.x; nd[4 * g + 1] = v.y; nd[4 * g + 2] = v.z; nd[4 * g + 3] = v.w;
         }
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NT; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[b][i] = __builtin_fmaf(pt[b][i], nd[i], acc[b][i]);
         __syncthreads();
@@ -236,7 +241,7 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ 
 
     // ---- store: lane holds token (l32 of each tile) and 16 rows
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
         const int n = n0 + nt * 32 + l32;
         if (n >= N) continue;
 #pragma unroll
@@ -249,24 +254,43 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
-                          int64_t k, hipStream_t stream) {
-    const int S = (int)(k / kQK);
-    dim3 grid((unsigned)((m + BM - 1) / BM), (unsigned)((n + BN - 1) / BN));
-    hipLaunchKernelGGL(mmq_q6k_kernel<false>, grid, dim3(256), 0, stream, (const uint8_t*)w,
-                       (const uint16_t*)nullptr, (const uint8_t*)xq, y, (int)m, (int)n, S);
+// Tokens per workgroup: the largest of 128, 64, 32 whose grid still gives
+// every compute unit a workgroup (a smaller tile repeats the weight decode
+// for fewer tokens, but idle compute units cost more).
+static int mmq_q6k_nt(int64_t m, int64_t n, int cus) {
+    const int64_t mt = (m + BM - 1) / BM;
+    for (int nt = 4; nt > 1; nt >>= 1)
+        if (mt * ((n + 32 * nt - 1) / (32 * nt)) >= cus) return nt;
+    return 1;
+}
+
+template <bool SPLIT>
+static hipError_t launch_mmq_q6k_any(const uint8_t* w, const uint16_t* wd, const void* xq, float* y,
+                                     int64_t m, int64_t n, int S, int cus, hipStream_t stream) {
+    const int nt = mmq_q6k_nt(m, n, cus);
+    dim3 grid((unsigned)((m + BM - 1) / BM), (unsigned)((n + 32 * nt - 1) / (32 * nt)));
+    auto launch = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, w, wd, (const uint8_t*)xq, y, (int)m,
+                           (int)n, S);
+    };
+    if (nt == 4) launch(mmq_q6k_kernel<4, SPLIT>);
+    else if (nt == 2) launch(mmq_q6k_kernel<2, SPLIT>);
+    else launch(mmq_q6k_kernel<1, SPLIT>);
     return hipGetLastError();
 }
 
+hipError_t launch_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
+                          int64_t k, int cus, hipStream_t stream) {
+    return launch_mmq_q6k_any<false>((const uint8_t*)w, nullptr, xq, y, m, n, (int)(k / kQK), cus,
+                                     stream);
+}
+
 hipError_t launch_mmq_q6k_split(const void* wr, const void* xq, float* y, int64_t m, int64_t n,
-                                int64_t k, hipStream_t stream) {
+                                int64_t k, int cus, hipStream_t stream) {
     const int S = (int)(k / kQK);
     const int64_t G = m * S;
     const uint8_t* bodies = (const uint8_t*)wr + (2 * G + 15) / 16 * 16;
-    dim3 grid((unsigned)((m + BM - 1) / BM), (unsigned)((n + BN - 1) / BN));
-    hipLaunchKernelGGL(mmq_q6k_kernel<true>, grid, dim3(256), 0, stream, bodies,
-                       (const uint16_t*)wr, (const uint8_t*)xq, y, (int)m, (int)n, S);
-    return hipGetLastError();
+    return launch_mmq_q6k_any<true>(bodies, (const uint16_t*)wr, xq, y, m, n, S, cus, stream);
 }
 
 }  // namespace kq

@@ -119,7 +119,8 @@ def test_gemv_split_output_head(kq):
         torch.cuda.empty_cache()
 
 
-MMQ_CASES = [(1, 1, 256), (5, 3, 512), (150, 70, 768), (300, 130, 3584), (131, 70, 18944)]
+MMQ_CASES = [(1, 1, 256), (5, 3, 512), (150, 70, 768), (300, 130, 3584), (131, 70, 18944),
+             (3584, 640, 256), (4096, 1024, 256)]
 
 
 @pytest.mark.parametrize("m,n,k", MMQ_CASES, ids=[f"m{m}-n{n}-k{k}" for m, n, k in MMQ_CASES])
