@@ -594,6 +594,56 @@ def summarize(cfg: int, trace_csv=None, fetch_csv=None, write_csv=None):
     return "\n".join(out), traffic
 
 
+# MI355X layout used to normalise the SQ counters of one kernel: the busy
+# cycles are summed over every SIMD (4 per CU) and GRBM_GUI_ACTIVE over the
+# XCDs, so a kernel's cycles are GRBM_GUI_ACTIVE / XCDS.
+MI355X_CUS, MI355X_XCDS, SIMDS_PER_CU = 256, 8, 4
+MMQ_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
+                "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE")
+
+
+def summarize_counters(cfg: int, counters_csv: str):
+    """Per launch of workload cfg, the median of each counter over the
+    run's steps, and for the MMQ launches the matrix-core and VALU busy
+    fractions and the int8 MFMA work the counters saw against 2*M*N*K."""
+    import csv
+    from kq_inputs import WORKLOADS
+
+    rows = list(csv.DictReader(open(counters_csv)))
+    labels, kinds, steps = _steps_in(rows, cfg)
+    ops = {op["label"]: op for op in WORKLOADS[cfg].get("bench_ops", WORKLOADS[cfg]["ops"])}
+    out = [f"counters: {len(steps)} steps matched in {counters_csv}",
+           f"normalisation: kernel cycles = GRBM_GUI_ACTIVE / {MI355X_XCDS} XCDs; "
+           f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ({SIMDS_PER_CU} SIMDs x {MI355X_CUS} CUs x kernel cycles); "
+           f"VALU busy = SQ_ACTIVE_INST_VALU (4-cycle issue slots) x 4 / the same"]
+    for t, lab in enumerate(labels):
+        if not kinds[t].startswith("mmq"):
+            continue
+        med = {}
+        for name in MMQ_COUNTERS:
+            v = sorted(sum(float(r["Counter_Value"]) for r in s[t] if r["Counter_Name"] == name)
+                       for s in steps)
+            if v:
+                med[name] = v[len(v) // 2]
+        op = ops[lab]
+        work = 2.0 * op["m"] * op["n"] * op["k"]
+        out.append(f"{lab} ({kinds[t]}, {op['m']}x{op['k']} x {op['n']} tokens, 2MNK = {work:.4e}):")
+        for name in MMQ_COUNTERS:
+            if name in med:
+                out.append(f"  {name:28s} median {med[name]:16,.0f}")
+        cyc = med.get("GRBM_GUI_ACTIVE", 0) / MI355X_XCDS
+        if cyc > 0:
+            simd_cycles = SIMDS_PER_CU * MI355X_CUS * cyc
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+                out.append(f"  MFMA busy {100 * med['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:6.1f} %")
+            if "SQ_ACTIVE_INST_VALU" in med:
+                out.append(f"  VALU busy {100 * 4 * med['SQ_ACTIVE_INST_VALU'] / simd_cycles:6.1f} %")
+        if med.get("SQ_INSTS_VALU_MFMA_MOPS_I8"):   # one count = 512 int8 ops
+            mops = 512 * med["SQ_INSTS_VALU_MFMA_MOPS_I8"]
+            out.append(f"  int8 MFMA ops 512 x SQ_INSTS_VALU_MFMA_MOPS_I8 = {mops:.4e} = {mops / work:.3f} x 2MNK")
+    return "\n".join(out)
+
+
 def _workload_name(cfg: int) -> str:
     from kq_inputs import WORKLOADS
 
@@ -629,10 +679,15 @@ def main(argv=None):
     ap.add_argument("--trace-csv", default=None)
     ap.add_argument("--fetch-csv", default=None)
     ap.add_argument("--write-csv", default=None)
+    ap.add_argument("--counters-csv", default=None,
+                    help="one --pmc pass with the MMQ counters (matrix-core and VALU busy)")
     args = ap.parse_args(argv)
 
     if args.summarize:
         cfg = 1 if args.only is None else args.only
+        if args.counters_csv:
+            print(summarize_counters(cfg, args.counters_csv))
+            return 0
         text, traffic = summarize(cfg, args.trace_csv, args.fetch_csv, args.write_csv)
         print(text)
         if traffic:
