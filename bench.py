@@ -406,6 +406,68 @@ def measure(cfg: int, steps: int, warmup: int, use_graph: bool):
     return wl, ms, durs
 
 
+def stream_read_ceiling(nbytes: int = 2 << 30, reps: int = 10):
+    """Measured streaming-read ceiling of the device: kq_read_probe (16-byte
+    loads, one workgroup per 32 KiB, an xor per wavefront stored) over a
+    2 GiB buffer, larger than the Infinity Cache, event-timed, median of
+    `reps` launches.  The 8 TB/s spec peak stays the roofline; this is the
+    practical read rate beside it."""
+    import torch
+
+    import q6_q8_matmul_amd as kq
+
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(kq.kq_read_probe_words(nbytes), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        kq.kq_read_probe(buf, nbytes, out, stream.cuda_stream)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        kq.kq_read_probe(buf, nbytes, out, stream.cuda_stream)
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    del buf, out
+    torch.cuda.empty_cache()
+    t = sorted(ts)[len(ts) // 2]
+    return {"GBps": round(nbytes / t / 1e9, 1), "bytes": nbytes,
+            "how": "kq_read_probe (16-byte loads) over 2 GiB, median of 10 event-timed launches"}
+
+
+def read_floors_us(wl: Workload):
+    """Per GEMV launch of the step, the time kq_read_probe takes to read the
+    same weight tensor, rotated over the same copies and timed the same way
+    as the launch itself (graph replay of one launch per copy)."""
+    import torch
+
+    import q6_q8_matmul_amd as kq
+
+    out = {}
+    for op in wl.ops:
+        if not op["op"].startswith("gemv"):
+            continue
+        bufs = [wl.w[c][op["w"]] for c in range(wl.ncopies)]
+        nbytes = bufs[0].numel() // 16 * 16
+        res = torch.empty(kq.kq_read_probe_words(nbytes), dtype=torch.int32, device="cuda")
+        launches = [lambda b=b: kq.kq_read_probe(b, nbytes, res) for b in bufs]
+        ms = _graph_time_ms(lambda: [f() for f in launches], per_graph=1) / len(launches)
+        out[op["label"]] = round(ms * 1e3, 2)
+        del res
+    return out
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl: Workload, seconds: float):
     """The oracle on the host: the same step (quantise + every matmul of the
     workload) repeated until `seconds` have passed; also the GPU step
@@ -446,6 +508,7 @@ def cpu_baseline(wl: Workload, seconds: float):
         "value": round(gbps, 3),
         "unit": "GB/s",
         "cores": threads,
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
         "sample": f"the whole step ({wl.wl['name']}: q8_1 quantisation of every input plus every "
                   f"matmul, f64 dequantise-then-dot) repeated {reps}x in {dt:.1f} s",
@@ -783,6 +846,14 @@ def main(argv=None):
                            "hip_graphs": use_graph},
                 "roofline": roofline,
             }
+            ceiling = stream_read_ceiling()
+            ceiling["gemv_frac_of_ceiling"] = round(achieved / ceiling["GBps"], 4)
+            result["stream_read_ceiling"] = ceiling
+            floors = read_floors_us(wl)
+            for e in per_op:
+                if e["op"] in floors:
+                    e["read_floor_us"] = floors[e["op"]]
+                    e["frac_of_read_floor"] = round(floors[e["op"]] / e["avg_us"], 4)
             if not args.no_cpu:
                 log(f"cpu baseline (~{args.cpu_seconds} s)")
                 cb, parity = cpu_baseline(wl, args.cpu_seconds)

@@ -266,6 +266,24 @@ int kq_rmsnorm_q8_1(const float* x, const float* res, const float* g, float eps,
 int kq_swiglu_q8_1(const float* gate, const float* up, float* y, void* xq, int64_t rows,
                    int64_t n, void* stream);
 
+/*
+ * Measurement helper, not part of the k-quant path: the decode GEMVs stream
+ * their weights once (minfer "The CUDA backend" 2.2), and the benchmark
+ * reports their rate beside what a plain read of the same bytes reaches on
+ * the same device.  kq_read_probe reads nbytes at p once with 16-byte loads
+ * (one workgroup per 32 KiB) and stores, per 8 KiB wavefront share, the xor
+ * of its 32-bit words into out: out[4 * c + w] = xor over u = 0..7, l =
+ * 0..63 of the 16-byte word 2048 c + 256 u + 64 w + l (words past the end
+ * read as zero).
+ *   p      device, 16-byte aligned, nbytes > 0 a multiple of 16, < 2^40.
+ *   out    device uint32 [kq_read_probe_words(nbytes)], 4-byte aligned,
+ *          not overlapping p.
+ * kq_read_probe_words: that count, 4 * ceil(nbytes / 32768); -1 for an
+ * invalid nbytes.  Errors as the other calls (KQ_ERR_ARG, nothing launched).
+ */
+int64_t kq_read_probe_words(int64_t nbytes);
+int kq_read_probe(const void* p, int64_t nbytes, uint32_t* out, void* stream);
+
 /* Text of the last error on this host thread ("" if none). */
 const char* kq_last_error(void);
 

@@ -259,6 +259,27 @@ int kq_mmq_q6k_split(const void* wr, const void* xq, float* y, int64_t m, int64_
     return launched(fn, kq::launch_mmq_q6k_split(wr, xq, y, m, n, k, cus, (hipStream_t)stream));
 }
 
+int64_t kq_read_probe_words(int64_t nbytes) {
+    if (nbytes <= 0 || nbytes % 16 != 0 || nbytes >= (1LL << 40)) return -1;
+    return kq::read_probe_words(nbytes);
+}
+
+int kq_read_probe(const void* p, int64_t nbytes, uint32_t* out, void* stream) {
+    const char* fn = "kq_read_probe";
+    if (!p || !out) return fail(KQ_ERR_ARG, "%s: null pointer (p=%p out=%p)", fn, p, (void*)out);
+    if (nbytes <= 0 || nbytes % 16 != 0 || nbytes >= (1LL << 40))
+        return fail(KQ_ERR_ARG, "%s: nbytes=%lld must be a positive multiple of 16 below 2^40", fn,
+                    (long long)nbytes);
+    if (!aligned(p, 16) || !aligned(out, 4))
+        return fail(KQ_ERR_ARG, "%s: misaligned pointer (p=%p needs 16, out=%p needs 4)", fn, p,
+                    (void*)out);
+    const int64_t words = kq::read_probe_words(nbytes);
+    if (overlap(out, words * 4, p, nbytes))
+        return fail(KQ_ERR_ARG, "%s: out=%p overlaps p=%p", fn, (void*)out, p);
+    if (int rc = check_device(fn, nullptr)) return rc;
+    return launched(fn, kq::launch_read_probe(p, nbytes, out, (hipStream_t)stream));
+}
+
 int64_t kq_q6k_split_bytes(int64_t m, int64_t k) {
     if (m < 0 || m > KQ_MAX_ROWS || k <= 0 || k % 256 != 0 || k > KQ_MAX_K) return -1;
     return split_bytes(m, k);

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
         "kq_quantize_q8_1", "kq_gemv_q4k", "kq_gemv_q6k", "kq_mmq_q4k", "kq_mmq_q6k",
         "kq_q6k_split_bytes", "kq_repack_q6k", "kq_gemv_q6k_split", "kq_mmq_q6k_split",
         "kq_rmsnorm_q8_1", "kq_swiglu_q8_1", "kq_gemv_q4k_seg", "kq_last_error",
-        "kq_abi_version"])
+        "kq_abi_version", "kq_read_probe", "kq_read_probe_words"])
 
 
 def test_library_exports_every_declared_symbol(kq):
@@ -282,3 +282,28 @@ def test_gemv_seg_empty_and_null_arrays(kq):
     assert rc == kq.KQ_ERR_ARG and "k=100" in kq.kq_last_error()
     rc = kq.lib().kq_gemv_q4k_seg(1, None, None, None, None, X, 256, 1, None)
     assert rc == kq.KQ_ERR_ARG and "null array" in kq.kq_last_error()
+
+
+@pytest.mark.parametrize("nbytes,words", [(16, 4), (32768, 4), (32784, 8), (2 << 30, 4 * 65536)])
+def test_read_probe_words(kq, nbytes, words):
+    assert kq.kq_read_probe_words(nbytes) == words
+
+
+@pytest.mark.parametrize("nbytes", [0, -16, 8, 1 << 40])
+def test_read_probe_words_rejects(kq, nbytes):
+    assert kq.kq_read_probe_words(nbytes) == -1
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((None, 4096, Y, None), "null pointer"),
+    ((W, 4096, None, None), "null pointer"),
+    ((W, 0, Y, None), "nbytes=0"),
+    ((W, 4100, Y, None), "nbytes=4100"),
+    ((W + 8, 4096, Y, None), "misaligned"),
+    ((W, 4096, Y + 2, None), "misaligned"),
+    ((W, 4096, W + 64, None), "overlaps"),
+])
+def test_read_probe_rejects(kq, args, needle):
+    rc = kq.lib().kq_read_probe(*args)
+    assert rc == kq.KQ_ERR_ARG, kq.kq_last_error()
+    assert needle in kq.kq_last_error() and "kq_read_probe" in kq.kq_last_error()
