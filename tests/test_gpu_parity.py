@@ -163,8 +163,9 @@ def test_gemv_shapes(kq, kind, m, k, batch, with_res):
 
 
 @pytest.mark.parametrize("kind", ["q4k", "q6k"])
-def test_gemv_in_place_residual(kq, kind):
-    m, k, b = 333, 4096, 4
+@pytest.mark.parametrize("k", [4096, 14336])   # 14336 at batch 4: the Q4_K K split
+def test_gemv_in_place_residual(kq, kind, k):
+    m, b = 333, 4
     say(f"gemv {kind} in place m={m} k={k} batch={b}")
     w, x, res = random_case(77, kind, m, k, b, with_residual=True)
     xq = oracle.quantize_q8_1(x)
