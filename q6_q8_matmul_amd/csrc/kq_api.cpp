@@ -235,8 +235,9 @@ int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, in
     const char* fn = "kq_mmq_q4k";
     if (int rc = mmq_common(fn, 144, w, xq, y, m, n, k)) return rc;
     if (m == 0 || n == 0) return ok();
-    if (int rc = check_device(fn, nullptr)) return rc;
-    return launched(fn, kq::launch_mmq_q4k(w, xq, y, m, n, k, (hipStream_t)stream));
+    int cus = 0;
+    if (int rc = check_device(fn, nullptr, &cus)) return rc;
+    return launched(fn, kq::launch_mmq_q4k(w, xq, y, m, n, k, cus, (hipStream_t)stream));
 }
 
 int kq_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,

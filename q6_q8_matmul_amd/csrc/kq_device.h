@@ -144,7 +144,7 @@ hipError_t launch_gemv_q6k(const void* w, const void* xq, float* y, const float*
 int64_t read_probe_words(int64_t nbytes);
 hipError_t launch_read_probe(const void* p, int64_t nbytes, uint32_t* out, hipStream_t stream);
 hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
-                          int64_t k, hipStream_t stream);
+                          int64_t k, int cus, hipStream_t stream);
 hipError_t launch_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                           int64_t k, int cus, hipStream_t stream);
 hipError_t launch_mmq_q6k_split(const void* wr, const void* xq, float* y, int64_t m, int64_t n,

@@ -10,13 +10,15 @@
 // (weight row, token, 32-block) and receives its own scale:
 //     T = d8 * (D * A - Mn * Bq),  D = d*sc, Mn = dmin*m, Bq = sum of q8 codes.
 //
-// Tiling: a workgroup (4 wavefronts, 2 x 2) computes 128 weight rows x 128
-// tokens; each wavefront a 64 x 64 block of four 32 x 32 MFMA tiles.  The K
+// Tiling: a workgroup (4 wavefronts, 2 x 2) computes 128 weight rows x BN =
+// 64 NTW tokens; each wavefront a 64 x 32 NTW block of 2 x NTW 32 x 32 MFMA
+// tiles (NTW = 2, or 1 where three smaller workgroups per CU take fewer
+// rounds of the grid, see launch_mmq_q4k).  The K
 // loop walks one superblock (256 values, 8 q8_1 blocks) at a time, every
 // global load of a stage issued before the first LDS write:
 //   * raw Q4_K superblocks of the 128 rows -> LDS (16-byte loads);
 //     per row and sub-block the f32 pair (D, -Mn) -> LDS;
-//   * q8_1 blocks of the 128 tokens -> LDS as int8 codes (rows padded to
+//   * q8_1 blocks of the BN tokens -> LDS as int8 codes (rows padded to
 //     272 bytes against bank conflicts) plus per (token, block) d8 and
 //     d8*Bq;
 //   * per pair of blocks (the low and high nibbles of the same 32 code
@@ -31,6 +33,8 @@
 // stored.  No atomics; results are bitwise reproducible.
 #include "kq_device.h"
 
+#include <algorithm>
+
 namespace kq {
 namespace {
 
@@ -40,11 +44,12 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
 
 constexpr int BM = 128;            // weight rows per workgroup
-constexpr int BN = 128;            // tokens per workgroup
 constexpr int kCodeStride = 272;   // LDS bytes per token row of codes (256 + 16 pad)
 constexpr int kTokStride = 9;      // floats per token in the d8 / z planes (8 + 1 pad)
 
+template <int NTW>
 struct Smem {
+    static constexpr int BN = 64 * NTW;  // tokens per workgroup
     uint8_t wraw[BM * kQ4KBytes];        // raw superblocks, 144 bytes per row
     float dsc[8][BM];                    // D = d*sc    per (block, row)
     float nmn[8][BM];                    // -Mn = -dmin*m per (block, row)
@@ -53,10 +58,12 @@ struct Smem {
     float z[BN * kTokStride];            // d8 * (sum of the block's codes)
 };
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int NTW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NTW == 1 ? 3 : 2, NTW == 1 ? 3 : 2)))
 void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq,
                     float* __restrict__ y, int M, int N, int S) {
-    __shared__ __align__(16) Smem sm;
+    constexpr int BN = Smem<NTW>::BN;
+    __shared__ __align__(16) Smem<NTW> sm;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -68,11 +75,11 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
     const int64_t row_bytes = (int64_t)S * kQ4KBytes;
     const int nb_row = S * 8;
 
-    float acc[2][2][16];
+    float acc[2][NTW][16];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NTW; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
@@ -81,7 +88,7 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
         // Weights: two threads per row; thread (row, e) takes the 16-byte
         // chunks e, e+2, ... of the row's 144-byte superblock (9 chunks); the
         // even thread also decodes the header chunk into (D, -Mn) per
-        // sub-block.  Activations: 128 tokens x 8 q8_1 blocks, four (token,
+        // sub-block.  Activations: BN tokens x 8 q8_1 blocks, 2 NTW (token,
         // block) pairs per thread.
         {
             // recompute the staging addresses every superblock: kept live
@@ -97,10 +104,10 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
                 const int ch = e + 2 * c;
                 if (ch < 9) cw[c] = load16(p + 16 * ch);
             }
-            uint4 c0[4], c1[4];
-            uint32_t hd[4];
+            uint4 c0[2 * NTW], c1[2 * NTW];
+            uint32_t hd[2 * NTW];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 2 * NTW; ++i) {
                 const int idx = ts + 256 * i;
                 const int t = idx >> 3, j = idx & 7;
                 const int gt = min(n0 + t, N - 1);
@@ -129,7 +136,7 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 2 * NTW; ++i) {
                 const int idx = tid + 256 * i;
                 const int t = idx >> 3, j = idx & 7;
                 const uint32_t cc[8] = {c0[i].x, c0[i].y, c0[i].z, c0[i].w,
@@ -154,11 +161,11 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
         //   S     = D (x) d8           f32 MFMA, two outer products
         //   part += float(A_2p) * S_2p + float(A_2p+1) * S_2p+1   (VALU)
         // with A the exact int32 block dots from the int8 MFMA.
-        v16f part[2][2];
+        v16f part[2][NTW];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NTW; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) part[a][b][i] = 0.0f;
 
@@ -178,11 +185,11 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
                 Dp[mt] = sm.dsc[jl][r];
                 Mp[mt] = sm.nmn[jl][r];
             }
-            v4i B[2][2];
-            float dp[2], zp[2];
+            v4i B[NTW][2];
+            float dp[NTW], zp[NTW];
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int t = wn * 64 + nt * 32 + l32;
+            for (int nt = 0; nt < NTW; ++nt) {
+                const int t = wn * 32 * NTW + nt * 32 + l32;
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const uint4 a = *(const uint4*)(sm.codes + t * kCodeStride + 32 * (2 * pp + e) + 16 * h2);
@@ -194,7 +201,7 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
+                for (int nt = 0; nt < NTW; ++nt) {
                     const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
                     const v32f zf = {};
                     const v16i R0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mt][0], B[nt][0], zero, 0, 0, 0);
@@ -212,7 +219,7 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NTW; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[a][b][i] += part[a][b][i];
         __syncthreads();
@@ -222,8 +229,8 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int n = n0 + wn * 64 + nt * 32 + l32;
+        for (int nt = 0; nt < NTW; ++nt) {
+            const int n = n0 + wn * 32 * NTW + nt * 32 + l32;
             if (n >= N) continue;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -235,12 +242,30 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
 
 }  // namespace
 
+// Tokens per workgroup, 128 (NTW = 2: two workgroups per CU) or 64 (NTW =
+// 1: 168 VGPRs and 48 KB of LDS, three per CU, whose staging then hides
+// better behind the others' arithmetic).  Measured on one box at 2048
+// tokens, a full round of the 64-token form takes ~0.7 of a round of the
+// 128-token one, so the form with the fewer weighted rounds is launched:
+// QKV 4608 rows 207 -> 162 us, gate/up 627 -> 603-620 us with 64 tokens;
+// down 3584 rows stays at 128 (448 tiles fit one round of 512 slots; 896
+// small tiles would take two rounds: 623 against 664 us).
 hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
-                          int64_t k, hipStream_t stream) {
+                          int64_t k, int cus, hipStream_t stream) {
     const int S = (int)(k / kQK);
-    dim3 grid((unsigned)((m + BM - 1) / BM), (unsigned)((n + BN - 1) / BN));
-    hipLaunchKernelGGL(mmq_q4k_kernel, grid, dim3(256), 0, stream, (const uint8_t*)w,
-                       (const uint8_t*)xq, y, (int)m, (int)n, S);
+    const int64_t mt = (m + BM - 1) / BM;
+    const int64_t t2 = mt * ((n + 127) / 128), t1 = mt * ((n + 63) / 64);
+    const int64_t s2 = (int64_t)cus * std::max(1, occupancy((const void*)mmq_q4k_kernel<2>, 256, 0));
+    const int64_t s1 = (int64_t)cus * std::max(1, occupancy((const void*)mmq_q4k_kernel<1>, 256, 0));
+    const bool small = 7 * ((t1 + s1 - 1) / s1) < 10 * ((t2 + s2 - 1) / s2);
+    const int bn = small ? 64 : 128;
+    dim3 grid((unsigned)mt, (unsigned)((n + bn - 1) / bn));
+    if (small)
+        hipLaunchKernelGGL(mmq_q4k_kernel<1>, grid, dim3(256), 0, stream, (const uint8_t*)w,
+                           (const uint8_t*)xq, y, (int)m, (int)n, S);
+    else
+        hipLaunchKernelGGL(mmq_q4k_kernel<2>, grid, dim3(256), 0, stream, (const uint8_t*)w,
+                           (const uint8_t*)xq, y, (int)m, (int)n, S);
     return hipGetLastError();
 }
 

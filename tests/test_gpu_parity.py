@@ -206,13 +206,14 @@ def test_gemv_deterministic(kq, kind):
 
 # ----------------------------------------------------------------- MMQ -----
 
-# The small shapes take the 32-token tile; on a 256-CU MI355X the 128-row x
-# 64-token grid of 3584 x 640 and the 128 x 128 grid of 4096 x 1024 are the
-# first to reach one workgroup per CU, so those two cover the 64- and
-# 128-token tiles with full outputs.
+# Workgroup token tiles on a 256-CU MI355X.  Q6_K: the small shapes take
+# 32 tokens; 3584 x 640 and 4096 x 1024 are the first grids of 64 and 128
+# tokens to give every CU a workgroup.  Q4_K: every shape but 3584 x 2048
+# takes 64 tokens; that one (448 tiles of 128 tokens, one round of 512
+# slots) keeps 128.
 MMQ_SHAPES = [(1, 1, 256), (5, 3, 512), (128, 128, 256), (200, 150, 1024), (129, 257, 768),
               (300, 64, 3584), (64, 300, 2048), (131, 70, 18944), (3584, 640, 256),
-              (4096, 1024, 256)]
+              (4096, 1024, 256), (3584, 2048, 256)]
 MMQ_CASES = [(kind, *shape) for kind in ("q4k", "q6k") for shape in MMQ_SHAPES]
 
 
