@@ -90,7 +90,8 @@ def _fails_some_pin(path):
 
 @pytest.mark.parametrize("label,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(label, old, new, tmp_path):
-    src = open(SRC).read()
+    with open(SRC) as f:
+        src = f.read()
     assert src.count(old) == 1, f"mutation site for {label!r} not unique"
     mutant = os.path.join(tmp_path, "mutant.c")
     with open(mutant, "w") as f:
