@@ -57,8 +57,12 @@ __device__ __forceinline__ float4 load4(const float* p) { return *(const float4*
 // wavefront 0.  PER_SEGMENT: workgroup row*segs + seg writes segment seg of
 // the row (wavefront 0; every workgroup of the row repeats the same
 // reduction, whose row reads hit L2).  Otherwise workgroup `row` writes all
-// segments of its row, wavefront w taking segments w, w+4, ...
-template <bool PER_SEGMENT>
+// segments of its row, wavefront w taking segments w, w+4, ...  STASH (one
+// workgroup per row, the row in dynamic LDS): the reduction pass keeps each
+// h = x (+ res) it forms, and the second pass reads them from LDS instead of
+// reading the row from memory again; the values and their order are the
+// same, so the outputs are too.
+template <bool PER_SEGMENT, bool STASH>
 __global__ __launch_bounds__(256) void rmsnorm_q8_1_kernel(const float* __restrict__ x,
                                                            const float* __restrict__ res,
                                                            const float* __restrict__ g, float eps,
@@ -66,6 +70,7 @@ __global__ __launch_bounds__(256) void rmsnorm_q8_1_kernel(const float* __restri
                                                            uint32_t* __restrict__ xq, int n,
                                                            int segs) {
     __shared__ float part[256];
+    extern __shared__ float hbuf[];   // STASH: the row's n values of h
     const int l = threadIdx.x;
     const int lane = l & 63, wave = l >> 6;
     const int64_t row = PER_SEGMENT ? blockIdx.x / segs : blockIdx.x;
@@ -86,6 +91,7 @@ __global__ __launch_bounds__(256) void rmsnorm_q8_1_kernel(const float* __restri
 #pragma unroll 16
     for (int i = l; i < n; i += 256) {
         const float h = rr ? xr[i] + rr[i] : xr[i];
+        if (STASH) hbuf[i] = h;
         acc = __builtin_fmaf(h, h, acc);
     }
     part[l] = acc;
@@ -105,8 +111,8 @@ __global__ __launch_bounds__(256) void rmsnorm_q8_1_kernel(const float* __restri
     if (PER_SEGMENT && wave != 0) return;
     for (; seg < segs; seg += PER_SEGMENT ? segs : 4) {
         const int i = seg * 256 + 4 * lane;
-        float4 h = PER_SEGMENT ? h0 : load4(xr + i);
-        if (rr) {
+        float4 h = PER_SEGMENT ? h0 : STASH ? *(const float4*)(hbuf + i) : load4(xr + i);
+        if (rr && !STASH) {
             const float4 q = PER_SEGMENT ? q0 : load4(rr + i);
             h.x = h.x + q.x; h.y = h.y + q.y; h.z = h.z + q.z; h.w = h.w + q.w;
         }
@@ -143,13 +149,18 @@ hipError_t launch_rmsnorm_q8_1(const float* x, const float* res, const float* g,
     const int segs = (int)(n / 256);
     // Few rows: one workgroup per segment keeps every q8_1 block of a decode
     // row in flight at once (the repeated row reads hit L2).  Many rows: one
-    // workgroup per row reads the row once for the reduction.
+    // workgroup per row reduces once; it keeps the row in LDS between its two
+    // passes when the row fits 64 KB beside the 1 KB reduction buffer, and
+    // reads it again otherwise.
     if (rows * segs <= 4096 || rows < 64)
-        hipLaunchKernelGGL(rmsnorm_q8_1_kernel<true>, dim3((unsigned)(rows * segs)), dim3(256), 0,
-                           stream, x, res, g, eps, y, (uint32_t*)xq, (int)n, segs);
+        hipLaunchKernelGGL((rmsnorm_q8_1_kernel<true, false>), dim3((unsigned)(rows * segs)), dim3(256),
+                           0, stream, x, res, g, eps, y, (uint32_t*)xq, (int)n, segs);
+    else if (n * 4 + 1024 <= 65536)
+        hipLaunchKernelGGL((rmsnorm_q8_1_kernel<false, true>), dim3((unsigned)rows), dim3(256),
+                           (size_t)n * 4, stream, x, res, g, eps, y, (uint32_t*)xq, (int)n, segs);
     else
-        hipLaunchKernelGGL(rmsnorm_q8_1_kernel<false>, dim3((unsigned)rows), dim3(256), 0, stream,
-                           x, res, g, eps, y, (uint32_t*)xq, (int)n, segs);
+        hipLaunchKernelGGL((rmsnorm_q8_1_kernel<false, false>), dim3((unsigned)rows), dim3(256), 0,
+                           stream, x, res, g, eps, y, (uint32_t*)xq, (int)n, segs);
     return hipGetLastError();
 }
 

@@ -61,7 +61,8 @@ def check_swiglu(kq, gate, up, want_y=True, label=""):
         assert same.all(), f"{label}: {np.count_nonzero(~same)} y values differ"
 
 
-RMS_SHAPES = [(1, 256), (1, 4096), (3, 14336), (2, 65536), (17, 1280), (64, 512), (70, 16384)]
+RMS_SHAPES = [(1, 256), (1, 4096), (3, 14336), (2, 65536), (17, 1280), (64, 512), (70, 16384),
+              (300, 3584), (80, 16128)]
 
 
 @pytest.mark.parametrize("rows,n", RMS_SHAPES, ids=[f"r{r}-n{n}" for r, n in RMS_SHAPES])
