@@ -42,20 +42,25 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 128;            // weight rows per workgroup
 constexpr int kCodeStride = 272;   // LDS bytes per token row of codes (256 + 16 pad)
-constexpr int kTokStride = 9;      // floats per token in the d8 / z planes (8 + 1 pad)
+constexpr int kTokStride = 9;      // floats per token in the d8 plane (8 + 1 pad)
+constexpr int kZStride = 40;       // bf16 per token in the z plane (4 x 8 + 8 pad)
 
 template <int NTW>
 struct Smem {
     static constexpr int BN = 64 * NTW;  // tokens per workgroup
     uint8_t wraw[BM * kQ4KBytes];        // raw superblocks, 144 bytes per row
     float dsc[8][BM];                    // D = d*sc    per (block, row)
-    float nmn[8][BM];                    // -Mn = -dmin*m per (block, row)
+    uint32_t mins[BM][4];                // m of blocks 0..7 per row, as bf16 (exact)
+    float ndmin[BM];                     // -dmin per row
     int8_t codes[BN * kCodeStride];      // q8 codes per token
     float d8[BN * kTokStride];           // per (token, block)
-    float z[BN * kTokStride];            // d8 * (sum of the block's codes)
+    uint16_t zs[BN * kZStride];          // z = d8 * (sum of the block's codes) per
+                                         // (token, block) as three bf16 parts
+                                         // [hi x 8][mid x 8][lo x 8][0 x 8]
 };
 
 template <int NTW>
@@ -127,13 +132,19 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
                 const uint32_t lowS = hdr.y & 0x3f3f3f3fu, lowM = hdr.z & 0x3f3f3f3fu;
                 const uint32_t hiS = (hdr.w & 0x0f0f0f0fu) | ((hdr.y >> 2) & 0x30303030u);
                 const uint32_t hiM = ((hdr.w >> 4) & 0x0f0f0f0fu) | ((hdr.z >> 2) & 0x30303030u);
+                uint32_t mb[4];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const uint32_t s4 = j < 4 ? lowS : hiS, m4 = j < 4 ? lowM : hiM;
                     const int sh = 8 * (j & 3);
                     sm.dsc[j][rr] = d * (float)((s4 >> sh) & 0xff);
-                    sm.nmn[j][rr] = -(dmin * (float)((m4 >> sh) & 0xff));
+                    // m < 64 has at most six significant bits: its bf16 is exact
+                    const uint32_t mbits = __float_as_uint((float)((m4 >> sh) & 0xff)) >> 16;
+                    if (j & 1) mb[j >> 1] |= mbits << 16;
+                    else mb[j >> 1] = mbits;
                 }
+                *(uint4*)sm.mins[rr] = make_uint4(mb[0], mb[1], mb[2], mb[3]);
+                sm.ndmin[rr] = -dmin;
             }
 #pragma unroll
             for (int i = 0; i < 2 * NTW; ++i) {
@@ -149,31 +160,69 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
                 dst[0] = c0[i];
                 dst[1] = c1[i];
                 sm.d8[t * kTokStride + j] = d8;
-                sm.z[t * kTokStride + j] = d8 * (float)sum;
+                // z in three bf16 parts, each the next eight significant bits
+                // (truncation leaves an exact remainder; a finite z has 24)
+                const float z = d8 * (float)sum;
+                const uint32_t zh = __float_as_uint(z) & 0xffff0000u;
+                const float r1 = z - __uint_as_float(zh);
+                const uint32_t zm = __float_as_uint(r1) & 0xffff0000u;
+                const float r2 = r1 - __uint_as_float(zm);
+                const bool fin = __builtin_isfinite(z);
+                uint16_t* zt = sm.zs + t * kZStride + j;
+                zt[0] = (uint16_t)(zh >> 16);
+                zt[8] = fin ? (uint16_t)(zm >> 16) : (uint16_t)0;
+                zt[16] = fin ? (uint16_t)(__float_as_uint(r2) >> 16) : (uint16_t)0;
+                zt[24] = 0;
             }
         }
         __syncthreads();
 
-        // Per-superblock partial of every output.  Each pair of blocks
-        // (2p, 2p+1) -- the low and high nibbles of the same code bytes --
-        // contributes, per 32 x 32 tile:
-        //   part += (-Mn) (x) z        f32 MFMA, K = 2 (the two blocks)
+        // Per-superblock partial of every output, per 32 x 32 tile:
+        //   part  = -dmin * sum_j m_j z_j      two bf16 MFMAs over the 8
+        //           blocks x 3 parts of z (products exact, f32 sums), one
+        //           f32 multiply per output;
+        // then each pair of blocks (2p, 2p+1) -- the low and high nibbles of
+        // the same code bytes -- adds
         //   S     = D (x) d8           f32 MFMA, two outer products
         //   part += float(A_2p) * S_2p + float(A_2p+1) * S_2p+1   (VALU)
         // with A the exact int32 block dots from the int8 MFMA.
         v16f part[2][NTW];
+        {
+            v8bf am[2], bz[NTW][2];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+            for (int mt = 0; mt < 2; ++mt)
+                am[mt] = __builtin_bit_cast(v8bf, *(const uint4*)sm.mins[wm * 64 + mt * 32 + l32]);
 #pragma unroll
-            for (int b = 0; b < NTW; ++b)
+            for (int nt = 0; nt < NTW; ++nt) {
+                const uint16_t* zt = sm.zs + (wn * 32 * NTW + nt * 32 + l32) * kZStride + 8 * h2;
+                bz[nt][0] = __builtin_bit_cast(v8bf, *(const uint4*)zt);
+                bz[nt][1] = __builtin_bit_cast(v8bf, *(const uint4*)(zt + 16));
+            }
 #pragma unroll
-                for (int i = 0; i < 16; ++i) part[a][b][i] = 0.0f;
+            for (int mt = 0; mt < 2; ++mt) {
+                // -dmin of this lane's 16 output rows: 4 runs of 4
+                float nd[16];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 v = *(const float4*)(sm.ndmin + wm * 64 + mt * 32 + 8 * g + 4 * h2);
+                    nd[4 * g] = v.x; nd[4 * g + 1] = v.y; nd[4 * g + 2] = v.z; nd[4 * g + 3] = v.w;
+                }
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) {
+                    const v16f zero = {};
+                    v16f pm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[mt], bz[nt][0], zero, 0, 0, 0);
+                    pm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[mt], bz[nt][1], pm, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) part[mt][nt][i] = nd[i] * pm[i];
+                }
+            }
+        }
 
 #pragma unroll 1
         for (int pp = 0; pp < 4; ++pp) {
             const int jl = 2 * pp + h2;   // this lane's block within the pair for the f32 MFMAs
             v4i A[2][2];
-            float Dp[2], Mp[2];
+            float Dp[2];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 const int r = wm * 64 + mt * 32 + l32;
@@ -183,10 +232,9 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
                 A[mt][1] = v4i{(int)((q.x >> 4) & 0x0f0f0f0fu), (int)((q.y >> 4) & 0x0f0f0f0fu),
                                (int)((q.z >> 4) & 0x0f0f0f0fu), (int)((q.w >> 4) & 0x0f0f0f0fu)};
                 Dp[mt] = sm.dsc[jl][r];
-                Mp[mt] = sm.nmn[jl][r];
             }
             v4i B[NTW][2];
-            float dp[NTW], zp[NTW];
+            float dp[NTW];
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) {
                 const int t = wn * 32 * NTW + nt * 32 + l32;
@@ -196,7 +244,6 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
                     B[nt][e] = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
                 }
                 dp[nt] = sm.d8[t * kTokStride + jl];
-                zp[nt] = sm.z[t * kTokStride + jl];
             }
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
@@ -207,7 +254,7 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
                     const v16i R0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mt][0], B[nt][0], zero, 0, 0, 0);
                     const v16i R1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mt][1], B[nt][1], zero, 0, 0, 0);
                     const v32f S = __builtin_amdgcn_mfma_f32_32x32x1f32(Dp[mt], dp[nt], zf, 0, 0, 0);
-                    v16f pt = __builtin_amdgcn_mfma_f32_32x32x2f32(Mp[mt], zp[nt], part[mt][nt], 0, 0, 0);
+                    v16f pt = part[mt][nt];
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         pt[i] += (float)R0[i] * S[i];
