@@ -17,18 +17,20 @@
 // loop walks one superblock (256 values, 8 q8_1 blocks) at a time, every
 // global load of a stage issued before the first LDS write:
 //   * raw Q4_K superblocks of the 128 rows -> LDS (16-byte loads);
-//     per row and sub-block the f32 pair (D, -Mn) -> LDS;
+//     per row and sub-block D (f32), per row the eight m (bf16) and -dmin;
 //   * q8_1 blocks of the BN tokens -> LDS as int8 codes (rows padded to
 //     272 bytes against bank conflicts) plus per (token, block) d8 and
-//     d8*Bq;
+//     z = d8*Bq, the latter as three bf16 parts whose sum is exactly z;
+//   * the minimum terms of the whole superblock: two bf16 MFMAs over the
+//     8 blocks x 3 parts give sum_j m_j z_j (exact products, f32 sums),
+//     times -dmin per row: the start of the superblock's partial;
 //   * per pair of blocks (the low and high nibbles of the same 32 code
 //     bytes): nibbles -> two int8 operands in registers, two int8 MFMAs
 //     give the exact block dots; one f32 MFMA forms both blocks' scale outer
-//     products D (x) d8, another accumulates the minimum terms; the VALU only
-//     converts the dots and applies the scales (2 instructions per output
-//     and block).  Per-superblock partials are added to the output
-//     accumulator once per superblock, so each output sees about
-//     12 + k/256 f32 roundings in sequence.
+//     products D (x) d8; the VALU only converts the dots and applies the
+//     scales (2 instructions per output and block).  Per-superblock partials
+//     are added to the output accumulator once per superblock, so each
+//     output sees about 11 + k/256 f32 roundings in sequence.
 // Outputs beyond m or n are computed from clamped (valid) rows/tokens and not
 // stored.  No atomics; results are bitwise reproducible.
 #include "kq_device.h"
@@ -290,7 +292,7 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
 }  // namespace
 
 // Tokens per workgroup, 128 (NTW = 2: two workgroups per CU) or 64 (NTW =
-// 1: 168 VGPRs and 48 KB of LDS, three per CU, whose staging then hides
+// 1: 168 VGPRs and 49 KB of LDS, three per CU, whose staging then hides
 // better behind the others' arithmetic).  Measured on one box at 2048
 // tokens, a full round of the 64-token form takes ~0.7 of a round of the
 // 128-token one, so the form with the fewer weighted rounds is launched:
