@@ -306,7 +306,9 @@ hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, in
     const int64_t t2 = mt * ((n + 127) / 128), t1 = mt * ((n + 63) / 64);
     const int64_t s2 = (int64_t)cus * std::max(1, occupancy((const void*)mmq_q4k_kernel<2>, 256, 0));
     const int64_t s1 = (int64_t)cus * std::max(1, occupancy((const void*)mmq_q4k_kernel<1>, 256, 0));
-    const bool small = 7 * ((t1 + s1 - 1) / s1) < 10 * ((t2 + s2 - 1) / s2);
+    // the 64-token grid must also fit 65535 workgroups in y (n up to 65535*128
+    // is accepted, which only the 128-token form covers)
+    const bool small = (n + 63) / 64 <= 65535 && 7 * ((t1 + s1 - 1) / s1) < 10 * ((t2 + s2 - 1) / s2);
     const int bn = small ? 64 : 128;
     dim3 grid((unsigned)mt, (unsigned)((n + bn - 1) / bn));
     if (small)

@@ -231,6 +231,31 @@ def test_mmq_full(kq, kind, m, n, k):
     check_close(y, y_ref, den, f"mmq {kind} m{m} n{n} k{k}")
 
 
+@pytest.mark.parametrize("kind", ["q4k", "q6k"])
+def test_mmq_token_grid_limit(kq, kind):
+    """More tokens than 65535 workgroups of 64 cover (n = 2^22 + 64, a ragged
+    last tile): the launch must take 128-token tiles.  The q8_1 rows repeat
+    with period 4096, so every token's outputs must equal those of its base
+    token bit for bit, and the base tokens are checked against the oracle."""
+    m, k, period, n = 3, 256, 4096, (1 << 22) + 64
+    say(f"mmq {kind} token-grid limit m={m} n={n} k={k}")
+    w, x, _ = random_case(9001, kind, m, k, period)
+    xq_base = oracle.quantize_q8_1(x)
+    reps = -(-n // period)
+    xq = np.tile(xq_base, (reps, 1))[:n]
+    y = mmq(kq, kind)(dev(w), dev(xq), m, n, k)
+    del xq
+    torch.cuda.synchronize()
+    yb = y[:period].clone()
+    full = y[: (n // period) * period].view(n // period, period, m)
+    assert torch.equal(full, yb.expand_as(full)), "a repeated token's outputs differ"
+    assert torch.equal(y[(n // period) * period:], yb[: n % period]), "ragged tail differs"
+    y_ref, den = oracle.matmul(kind, w, xq_base, m, period, k)
+    check_close(host(yb), y_ref, den, f"mmq {kind} token-grid limit (base tokens)")
+    del y, full, yb
+    torch.cuda.empty_cache()
+
+
 def _q6k_extreme(m, k, rng, scale_choice, code_choice):
     """Q6_K bytes with chosen int8 scales and 6-bit codes (placed at the
     format's byte offsets: ql nibbles and qh bit pairs of every code equal)."""
