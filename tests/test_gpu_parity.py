@@ -82,7 +82,7 @@ def test_quantize_bitexact_adversarial(kq):
     assert bad.size == 0, f"rows {bad[:5]} differ"
 
 
-@pytest.mark.parametrize("rows,k", [(1, 32), (3, 96), (5, 256), (7, 4128), (1000, 64)])
+@pytest.mark.parametrize("rows,k", [(1, 32), (3, 96), (5, 256), (7, 4128), (1000, 64), (3, 65536)])
 def test_quantize_ragged(kq, rows, k):
     x = np.random.default_rng(rows * 7 + k).standard_normal((rows, k)).astype(np.float32)
     say(f"quantize ragged rows={rows} k={k}")
@@ -149,6 +149,9 @@ SHAPES = [
     ("q4k", 1000, 4096, 8, True), ("q4k", 513, 2048, 5, False), ("q4k", 37, 14336, 6, True),
     ("q4k", 130, 28672, 7, False), ("q6k", 1001, 4096, 8, True), ("q6k", 77, 768, 5, False),
     ("q6k", 9, 32768, 8, False), ("q6k", 2000, 1024, 6, True),
+    # the largest k the calls accept (KQ_MAX_K): the activation in many LDS chunks
+    ("q4k", 37, 65536, 1, True), ("q4k", 37, 65536, 4, False), ("q4k", 19, 65536, 8, True),
+    ("q6k", 37, 65536, 1, False), ("q6k", 37, 65536, 4, True), ("q6k", 19, 65536, 8, False),
 ]
 
 
@@ -213,7 +216,7 @@ def test_gemv_deterministic(kq, kind):
 # slots) keeps 128.
 MMQ_SHAPES = [(1, 1, 256), (5, 3, 512), (128, 128, 256), (200, 150, 1024), (129, 257, 768),
               (300, 64, 3584), (64, 300, 2048), (131, 70, 18944), (3584, 640, 256),
-              (4096, 1024, 256), (3584, 2048, 256)]
+              (4096, 1024, 256), (3584, 2048, 256), (130, 70, 65536)]
 MMQ_CASES = [(kind, *shape) for kind in ("q4k", "q6k") for shape in MMQ_SHAPES]
 
 

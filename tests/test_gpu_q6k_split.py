@@ -66,7 +66,7 @@ def test_repack_output_head(kq):
     assert np.array_equal(host(wr), oracle.q6k_split(w, m, k))
 
 
-GEMV_CASES = [(m, k, b, r) for (m, k) in [(1, 256), (37, 768), (300, 4096), (130, 14336)]
+GEMV_CASES = [(m, k, b, r) for (m, k) in [(1, 256), (37, 768), (300, 4096), (130, 14336), (37, 65536)]
               for b in (1, 2, 4, 8) for r in (False, True)]
 
 
@@ -120,7 +120,7 @@ def test_gemv_split_output_head(kq):
 
 
 MMQ_CASES = [(1, 1, 256), (5, 3, 512), (150, 70, 768), (300, 130, 3584), (131, 70, 18944),
-             (3584, 640, 256), (4096, 1024, 256)]
+             (3584, 640, 256), (4096, 1024, 256), (130, 70, 65536)]
 
 
 @pytest.mark.parametrize("m,n,k", MMQ_CASES, ids=[f"m{m}-n{n}-k{k}" for m, n, k in MMQ_CASES])
