@@ -533,10 +533,17 @@ FETCH_SCALE_NOTE = ("FETCH_SIZE and WRITE_SIZE are scaled by bytes / counter rea
 
 
 def source_hash(kernel: str) -> str:
+    """Hash of the kernel source's code: comments and whitespace are removed
+    first, so editing a comment does not retire a counter measurement."""
     import hashlib
+    import re
 
-    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    code = " ".join(text.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def _step_labels(cfg: int):

@@ -710,16 +710,17 @@ hipError_t launch_gemv_q4k(const void* w, const void* xq, float* y, const float*
                            int64_t m, int64_t k, int batch, int lds_limit, int cus,
                            hipStream_t stream) {
     using namespace gemv4;
-    // Launch shapes measured on MI355X (back-to-back launches over rotating
-    // weight copies, Llama-3-8B decode shapes).  Batch 1: one row pair per
-    // wavefront, one pass ahead, persistent grid -- eight wavefronts and three
-    // workgroups per CU for tall or long rows (gate|up 28672x4096: 12.3 us,
-    // down 4096x14336: 9.4 us), else four wavefronts and four workgroups
-    // (4096x4096: 4.8 us).  Batches 2-4 use the four-wavefront persistent
-    // form (QKV 6144x4096 at batch 4: 8.2 us) unless the activation only fits
-    // in several LDS pieces or needs more than 64 KB, where one pass in
-    // flight over eight wavefronts per row group works best (down 4096x14336
-    // at batch 4: 14.6 us against 15.4 with three passes in flight).
+    // Launch shapes chosen by measurement on MI355X (back-to-back launches
+    // over rotating weight copies, Llama-3-8B decode shapes).  Batch 1: one
+    // row pair per wavefront, one pass ahead, persistent grid -- eight
+    // wavefronts and three workgroups per CU for tall or long rows (gate|up
+    // 28672x4096, down 4096x14336), else four wavefronts and four workgroups
+    // (4096x4096); two or three passes ahead were slower on all three.
+    // Batches 2-4 use the four-wavefront persistent form (QKV 6144x4096 at
+    // batch 4) unless the activation needs more than 64 KB of LDS: at batch 4
+    // the K split when the whole activation still fits one workgroup's LDS
+    // (down 4096x14336), else one pass in flight over eight wavefronts per
+    // row group, staged in pieces.
     const int S = (int)(k / kQK);
     const int64_t s_round = (S + 7) & ~7;
     const int64_t whole = (int64_t)lds_per_sb(batch) * s_round;
