@@ -711,6 +711,23 @@ def summarize_counters(cfg: int, counters_csv: str):
         if med.get("SQ_INSTS_VALU_MFMA_MOPS_I8"):   # one count = 512 int8 ops
             mops = 512 * med["SQ_INSTS_VALU_MFMA_MOPS_I8"]
             out.append(f"  int8 MFMA ops 512 x SQ_INSTS_VALU_MFMA_MOPS_I8 = {mops:.4e} = {mops / work:.3f} x 2MNK")
+        # engine clock: GRBM_GUI_ACTIVE per XCD over the dispatch's own
+        # timestamps (the counter also counts a few microseconds of activity
+        # around a dispatch, so short launches read high)
+        clk, durs = [], []
+        for st in steps:
+            for r in st[t]:
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and r.get("End_Timestamp"):
+                    ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                    if ns > 0:
+                        clk.append(float(r["Counter_Value"]) / MI355X_XCDS / ns)
+                        durs.append(ns / 1e3)
+                    break
+        if clk:
+            clk.sort()
+            durs.sort()
+            out.append(f"  clock {clk[len(clk) // 2]:9.3f} GHz  (GRBM_GUI_ACTIVE / {MI355X_XCDS} over the median "
+                       f"dispatch time {durs[len(durs) // 2]:.1f} us of this counter run)")
     return "\n".join(out)
 
 
