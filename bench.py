@@ -479,10 +479,8 @@ def cpu_baseline(wl: Workload, seconds: float):
 
     oracle.build(force=False)
     threads = oracle.max_threads()
-    reps = 0
-    t0 = time.perf_counter()
-    outs = None
-    while True:
+
+    def one_step():
         xq = {xn: oracle.quantize_q8_1(wl.host[xn]) for xn in wl.x}
         outs = []
         for op in wl.ops:
@@ -491,10 +489,23 @@ def cpu_baseline(wl: Workload, seconds: float):
             res = wl.host.get(op.get("residual")) if "residual" in op else None
             outs.append(oracle.matmul(kind, wl.host[op["w"]], xq[op["x"]], op["m"], rows, op["k"],
                                       residual=res))
-        reps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
+        return xq, outs
+
+    def timed(budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            got = one_step()
+            reps += 1
+            if time.perf_counter() - t0 >= budget:
+                return got, reps, time.perf_counter() - t0
+
+    (xq, outs), reps, dt = timed(seconds)
+    # the same step on one thread, over a quarter of the time
+    oracle.set_threads(1)
+    try:
+        _, reps1, dt1 = timed(seconds / 4)
+    finally:
+        oracle.set_threads(threads)
     # parity of the GPU step outputs (copy 0) with the oracle
     wl.step(0)
     torch.cuda.synchronize()
@@ -508,10 +519,12 @@ def cpu_baseline(wl: Workload, seconds: float):
         "value": round(gbps, 3),
         "unit": "GB/s",
         "cores": threads,
+        "value_1_thread": round(wl.weight_bytes_step * reps1 / dt1 / 1e9, 3),
         "cpu_model": _cpu_model(),
         "kind": "oracle",
         "sample": f"the whole step ({wl.wl['name']}: q8_1 quantisation of every input plus every "
-                  f"matmul, f64 dequantise-then-dot) repeated {reps}x in {dt:.1f} s",
+                  f"matmul, f64 dequantise-then-dot) repeated {reps}x in {dt:.1f} s on {threads} "
+                  f"threads; value_1_thread: {reps1}x in {dt1:.1f} s on one",
     }, {"q8_1_bitexact": bool(q_ok), "max_err_over_den": worst, "tolerance": 1e-5}
 
 
