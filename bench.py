@@ -809,6 +809,7 @@ def main(argv=None):
     use_graph = not args.no_graph
 
     secondary = {}
+    failed = False
     main_cfg = 1
     cfgs = [args.only] if args.only is not None else ([1] if args.no_secondary else [1, 2, 3, 4, 5, 6, 7, 8, 9])
     result = None
@@ -894,6 +895,11 @@ def main(argv=None):
             if not args.no_cpu:
                 log(f"cpu baseline (~{args.cpu_seconds} s)")
                 cb, parity = cpu_baseline(wl, args.cpu_seconds)
+                parity["ok"] = bool(parity["q8_1_bitexact"]
+                                    and parity["max_err_over_den"] <= parity["tolerance"])
+                if not parity["ok"]:   # the timing of a wrong result is no measurement
+                    log(f"PARITY FAILED against the oracle: {parity}")
+                    failed = True
                 result["cpu_baseline"] = cb
                 result["parity_vs_oracle"] = parity
             result["kernels"] = per_op
@@ -912,7 +918,7 @@ def main(argv=None):
     elif secondary:
         result["secondary"] = secondary
     print(json.dumps(result), flush=True)
-    return 0
+    return 1 if failed else 0
 
 
 if __name__ == "__main__":
