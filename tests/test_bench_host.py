@@ -3,8 +3,10 @@
 * The source hash that keys the committed HBM-traffic records ignores
   comments and whitespace but not code.
 * The counter summary turns a counter collection into matrix-core and VALU
-  busy fractions, int8 MFMA work against 2*M*N*K and the engine clock; checked
-  on a small synthetic collection whose answers are known by construction.
+  busy fractions, int8 MFMA work against 2*M*N*K and the engine clock; the
+  traffic summary scales FETCH_SIZE / WRITE_SIZE by the run's own weight
+  copies; the trace summary gives per-launch medians.  Each is checked on a
+  small synthetic collection whose answers are known by construction.
 """
 import csv
 
@@ -77,3 +79,62 @@ def test_counter_summary_fractions_work_and_clock(tmp_path):
         assert "= 2.000 x 2MNK" in block, block
         assert "clock     2.000 GHz" in block, block
         assert "dispatch time 100.0 us" in block, block
+
+
+def _decode_run(path, counter, steps, per_label, copy_factor):
+    """A counter collection of workload 1 (quantise + GEMV, three times per
+    step) preceded by five copies of each weight tensor whose readings are
+    `copy_factor` x their bytes; `per_label` gives each launch's bytes."""
+    weights = [9437184, 66060288, 33030144]      # attn_out, gate|up, down
+    fields = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+              "Start_Timestamp", "End_Timestamp"]
+    rows, disp, t0 = [], 0, 1_000_000
+
+    def add(name, nbytes, dur):
+        nonlocal disp, t0
+        disp += 1
+        rows.append({"Correlation_Id": disp, "Dispatch_Id": disp, "Kernel_Name": name,
+                     "Counter_Name": counter, "Counter_Value": f"{nbytes / 1024:.6f}",
+                     "Start_Timestamp": t0, "End_Timestamp": t0 + dur})
+        t0 += dur + 500
+
+    for wb in weights:
+        for _ in range(5):
+            add("__amd_rocclr_copyBuffer", wb * copy_factor, 20_000)
+    q = "kq::(anonymous namespace)::quantize_q8_1_kernel(float const*, int)"
+    g = "void kq::gemv4::gemv_q4k_persistent<1, 1, 1, 8, kq::gemv4::Seg1>(kq::gemv4::Seg1)"
+    for _ in range(steps):
+        for lab in ("quantize x_attn", "attn_out", "quantize x_ffn", "gate|up", "quantize x_down", "down"):
+            add(q if lab.startswith("quantize") else g, per_label[lab], 2_000 if lab.startswith("quantize") else 10_000)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_traffic_summary_scales_by_the_copies(tmp_path):
+    alg, _ = bench._op_bytes(1)
+    fetch = {lab: 4096.0 for lab in ("quantize x_attn", "quantize x_ffn", "quantize x_down")}
+    write = dict(fetch)
+    for lab in ("attn_out", "gate|up", "down"):
+        fetch[lab] = alg[lab] * 1.01 / 2     # FETCH_SIZE reads half of the bytes moved
+        write[lab] = 0.0
+    _decode_run(tmp_path / "f.csv", "FETCH_SIZE", 4, fetch, 0.5)
+    _decode_run(tmp_path / "w.csv", "WRITE_SIZE", 4, write, 1.0)
+    text, traffic = bench.summarize(1, fetch_csv=str(tmp_path / "f.csv"), write_csv=str(tmp_path / "w.csv"))
+    assert "4 steps matched" in text and "from 15 weight copies" in text
+    assert traffic["fetch_scale"] == 2.0 and traffic["write_scale"] == 1.0
+    assert text.count("ratio 1.0100") == 3, text
+    assert abs(traffic["hbm_bytes_per_launch"] / traffic["algorithmic_bytes_per_launch"] - 1.01) < 1e-6
+    assert traffic["source_sha256_16"] == bench.source_hash("gemv_q4k")
+
+
+def test_trace_summary_medians(tmp_path):
+    path = tmp_path / "trace.csv"
+    per = {lab: 1.0 for lab in ("quantize x_attn", "attn_out", "quantize x_ffn", "gate|up",
+                                "quantize x_down", "down")}
+    _decode_run(path, "none", 5, per, 1.0)
+    text, _ = bench.summarize(1, trace_csv=str(path))
+    assert "5 steps matched" in text
+    assert any(l.startswith("gate|up") and "10.00" in l for l in text.split("\n")), text
+    assert any(l.startswith("quantize x_down") and "2.00" in l for l in text.split("\n")), text
