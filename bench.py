@@ -39,6 +39,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -598,6 +599,22 @@ def _steps_in(rows, cfg):
     return labels, kinds, steps
 
 
+def _op_weight_bytes(cfg: int):
+    """Weight bytes per matmul launch label of workload cfg."""
+    from kq_inputs import WORKLOADS
+
+    wl = WORKLOADS[cfg]
+    shapes = {name: (kind, a, b) for name, kind, a, b in wl["tensors"]}
+    out = {}
+    for op in wl.get("bench_ops", wl["ops"]):
+        if "w" not in op:
+            continue
+        names = op["w"] if isinstance(op["w"], list) else [op["w"]]
+        out[op["label"]] = sum(shapes[nm][1] * shapes[nm][2] // 256 * (144 if shapes[nm][0] == "q4k" else 210)
+                               for nm in names)
+    return out
+
+
 def _op_bytes(cfg: int):
     """Algorithmic bytes per launch label: weights + q8_1 input + f32 output
     (+ f32 residual), and the weight sizes the run copies."""
@@ -605,12 +622,10 @@ def _op_bytes(cfg: int):
 
     wl = WORKLOADS[cfg]
     ops = wl.get("bench_ops", wl["ops"])
-    shapes = {name: (kind, a, b) for name, kind, a, b in wl["tensors"]}
+    wbytes = _op_weight_bytes(cfg)
     out, weights = {}, set()
     for op in ops:
-        names = op["w"] if isinstance(op["w"], list) else [op["w"]]
-        wb = sum(shapes[nm][1] * shapes[nm][2] // 256 * (144 if shapes[nm][0] == "q4k" else 210)
-                 for nm in names)
+        wb = wbytes[op["label"]]
         weights.add(wb)
         rows = op.get("batch", op.get("n"))
         b = wb + rows * (op["k"] // 32) * 36 + rows * op["m"] * 4
@@ -633,10 +648,38 @@ def summarize(cfg: int, trace_csv=None, fetch_csv=None, write_csv=None):
         _, _, steps = _steps_in(rows, cfg)
         out.append(f"kernel trace: {len(steps)} steps matched in {trace_csv}")
         out.append(f"{'launch':22s} {'kernel':16s} {'median_us':>10s} {'min_us':>8s}")
+        med = {}
         for t, lab in enumerate(labels):
             d = sorted(int(s[t][0]["End_Timestamp"]) - int(s[t][0]["Start_Timestamp"]) for s in steps)
             if d:
+                med[lab] = d[len(d) // 2] / 1e3
                 out.append(f"{lab:22s} {kinds[t]:16s} {d[len(d)//2]/1e3:10.2f} {d[0]/1e3:8.2f}")
+        # rates of the matmul launches at those medians
+        from kq_inputs import WORKLOADS
+
+        ops = {op["label"]: op for op in WORKLOADS[cfg].get("bench_ops", WORKLOADS[cfg]["ops"])}
+        wbytes = _op_weight_bytes(cfg)
+        for t, lab in enumerate(labels):
+            if lab not in med or lab not in wbytes:
+                continue
+            if kinds[t].startswith("mmq"):
+                op = ops[lab]
+                tops = 2.0 * op["m"] * op["n"] * op["k"] / (med[lab] * 1e-6) / 1e12
+                out.append(f"  {lab}: 2*M*N*K = {2 * op['m'] * op['n'] * op['k']:.4e} ops at the median: "
+                           f"{tops:.0f} TOPS = {100 * tops / INT8_PEAK_TOPS:.1f} % of "
+                           f"{INT8_PEAK_TOPS / 1e3:.1f} POPS")
+            else:
+                out.append(f"  {lab}: weight bytes {wbytes[lab]:,} at the median: "
+                           f"{wbytes[lab] / (med[lab] * 1e-6) / 1e9:,.0f} GB/s")
+        stats = os.path.join(os.path.dirname(trace_csv), "run_kernel_stats.csv")
+        if os.path.exists(stats):
+            out.append("rocprofv3 --stats (run_kernel_stats.csv), kq kernels (every call of the run):")
+            for r in csv.DictReader(open(stats)):
+                if "kq::" in r["Name"]:
+                    m = re.search(r"(\w+_(?:kernel|persistent|ksplit)(<[^>]*>)?)", r["Name"])
+                    nm = m.group(1) if m else r["Name"][:40]
+                    out.append(f"  {nm:48s} calls {int(r['Calls']):5d}  avg {float(r['AverageNs'])/1e3:9.2f} us"
+                               f"  min {float(r['MinNs'])/1e3:8.2f}  max {float(r['MaxNs'])/1e3:8.2f}")
     op_bytes, weight_sizes = _op_bytes(cfg)
     per, scale = {}, {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
