@@ -294,11 +294,12 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
 // Tokens per workgroup, 128 (NTW = 2: two workgroups per CU) or 64 (NTW =
 // 1: 168 VGPRs and 49 KB of LDS, three per CU, whose staging then hides
 // better behind the others' arithmetic).  Measured on one box at 2048
-// tokens, a full round of the 64-token form takes ~0.7 of a round of the
+// tokens, a full round of the 64-token form takes ~0.75 of a round of the
 // 128-token one, so the form with the fewer weighted rounds is launched:
-// QKV 4608 rows 207 -> 162 us, gate/up 627 -> 603-620 us with 64 tokens;
-// down 3584 rows stays at 128 (448 tiles fit one round of 512 slots; 896
-// small tiles would take two rounds: 623 against 664 us).
+// QKV 4608 rows (1152 small tiles in two rounds of 768 slots against 576
+// large ones in two rounds of 512) takes 64 tokens, 206 -> 158 us; gate/up
+// 18944 rows (seven small rounds against five large) and down 3584 rows
+// (two small rounds against one large) take 128.
 hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                           int64_t k, int cus, hipStream_t stream) {
     const int S = (int)(k / kQK);
@@ -308,7 +309,7 @@ hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, in
     const int64_t s1 = (int64_t)cus * std::max(1, occupancy((const void*)mmq_q4k_kernel<1>, 256, 0));
     // the 64-token grid must also fit 65535 workgroups in y (n up to 65535*128
     // is accepted, which only the 128-token form covers)
-    const bool small = (n + 63) / 64 <= 65535 && 7 * ((t1 + s1 - 1) / s1) < 10 * ((t2 + s2 - 1) / s2);
+    const bool small = (n + 63) / 64 <= 65535 && 3 * ((t1 + s1 - 1) / s1) < 4 * ((t2 + s2 - 1) / s2);
     const int bn = small ? 64 : 128;
     dim3 grid((unsigned)mt, (unsigned)((n + bn - 1) / bn));
     if (small)
