@@ -94,9 +94,10 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
         // ---- staging, every global load issued before the first LDS write.
         // Weights: two threads per row; thread (row, e) takes the 16-byte
         // chunks e, e+2, ... of the row's 144-byte superblock (9 chunks); the
-        // even thread also decodes the header chunk into (D, -Mn) per
-        // sub-block.  Activations: BN tokens x 8 q8_1 blocks, 2 NTW (token,
-        // block) pairs per thread.
+        // even thread also decodes the header chunk into D per sub-block,
+        // the eight m as bf16 and -dmin.  Activations: BN tokens x 8 q8_1
+        // blocks, 2 NTW (token, block) pairs per thread, each also writing
+        // the three bf16 parts of its z.
         {
             // recompute the staging addresses every superblock: kept live
             // across the MFMA loop they would cost registers it needs
@@ -222,7 +223,7 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
 
 #pragma unroll 1
         for (int pp = 0; pp < 4; ++pp) {
-            const int jl = 2 * pp + h2;   // this lane's block within the pair for the f32 MFMAs
+            const int jl = 2 * pp + h2;   // this lane's block within the pair for the f32 MFMA
             v4i A[2][2];
             float Dp[2];
 #pragma unroll
