@@ -1,36 +1,44 @@
 // mmq_q4k.hip -- Q4_K x q8_1 matrix-matrix product on the int8 matrix cores.
 //
 // minfer "The CUDA backend" 2.3 describes the method: the weights are never
-// dequantised -- their raw block bytes are staged in on-chip memory and
-// decoded in registers where the integer matrix instruction needs them; the
-// activations are quantised once per call by a prepass; the integer tile
-// product accumulates exactly in int32; the float scales are applied after
-// the integer loop.  On gfx950 one v_mfma_i32_32x32x32_i8 covers K = 32, i.e.
-// exactly one q8_1 block, so every MFMA result is the integer dot A of one
-// (weight row, token, 32-block) and receives its own scale:
+// dequantised -- their raw block bytes are staged on chip and decoded in
+// registers where the integer matrix instruction needs them; the activations
+// are quantised once per call by a prepass; the integer tile product
+// accumulates exactly in int32; the float scales are applied after the
+// integer loop.  On gfx950 one v_mfma_i32_32x32x32_i8 covers K = 32, exactly
+// one q8_1 block, so every MFMA result is the integer dot A of one (token,
+// weight row, 32-block) and takes its own scales:
 //     T = d8 * (D * A - Mn * Bq),  D = d*sc, Mn = dmin*m, Bq = sum of q8 codes.
 //
-// Tiling: a workgroup (4 wavefronts, 2 x 2) computes 128 weight rows x BN =
-// 64 NTW tokens; each wavefront a 64 x 32 NTW block of 2 x NTW 32 x 32 MFMA
-// tiles (NTW = 2, or 1 where three smaller workgroups per CU take fewer
-// rounds of the grid, see launch_mmq_q4k).  The K
-// loop walks one superblock (256 values, 8 q8_1 blocks) at a time, every
-// global load of a stage issued before the first LDS write:
-//   * raw Q4_K superblocks of the 128 rows -> LDS (16-byte loads);
-//     per row and sub-block D (f32), per row the eight m (bf16) and -dmin;
-//   * q8_1 blocks of the BN tokens -> LDS as int8 codes (rows padded to
-//     272 bytes against bank conflicts) plus per (token, block) d8 and
-//     z = d8*Bq, the latter as three bf16 parts whose sum is exactly z;
-//   * the minimum terms of the whole superblock: two bf16 MFMAs over the
-//     8 blocks x 3 parts give sum_j m_j z_j (exact products, f32 sums),
-//     times -dmin per row: the start of the superblock's partial;
-//   * per pair of blocks (the low and high nibbles of the same 32 code
-//     bytes): nibbles -> two int8 operands in registers, two int8 MFMAs
-//     give the exact block dots; one f32 MFMA forms both blocks' scale outer
-//     products D (x) d8; the VALU only converts the dots and applies the
-//     scales (2 instructions per output and block).  Per-superblock partials
-//     are added to the output accumulator once per superblock, so each
-//     output sees about 11 + k/256 f32 roundings in sequence.
+// Epilogue without a conversion.  The MFMA accumulator starts at the bit
+// pattern of 1.5*2^23, so its int32 result read as f32 is exactly
+// 1.5*2^23 + A (|A| <= 15*127*32 < 2^22 keeps it in one binade).  One FMA
+// with the per-row constants D and -1.5*2^23*D (exact: D has at most 17
+// significant bits) gives round(D*A), and a second FMA adds its product with
+// the token's d8.  Both are full-rate VALU instructions; the lane layout of
+// the output (one weight row per lane, sixteen tokens per lane) makes D a
+// per-lane value and d8 a per-element one, so no outer product of scales is
+// formed on the matrix cores.
+//
+// Minimum term: sum_j m_j z_j with z = d8*Bq (exact in f32, 24 bits) split by
+// truncation into three bf16 parts, so two v_mfma_f32_32x32x16_bf16 over
+// 8 blocks x 3 parts give it with exact products; times -dmin it starts the
+// superblock's partial.  Per-superblock partials are added to the output
+// accumulator once per superblock: each output sees about 11 + k/256 f32
+// roundings in sequence, whatever k is.
+//
+// Workgroup: 12 wavefronts (three per SIMD), 192 weight rows x 128 tokens;
+// wavefront (wr, wt) owns rows 64wr..64wr+63 (two 32-row tiles) and tokens
+// 32wt..32wt+31.  The K loop walks one superblock (256 values, 8 q8_1
+// blocks) per step through two LDS stages:
+//   * the raw bytes of step sb+1 -- 16-byte chunks of the Q4_K superblocks
+//     of 192 rows, the 16-byte code halves and header dwords of 128 tokens x
+//     8 q8_1 blocks -- are copied from memory straight into LDS
+//     (global_load_lds) while step sb computes;
+//   * a derive phase decodes each row's header once per workgroup (D and
+//     -1.5*2^23*D per sub-block, m as bf16, -dmin) and each token block's
+//     d8 (rewritten in place as f32) and z parts;
+//   * the compute phase reads everything from LDS.
 // Outputs beyond m or n are computed from clamped (valid) rows/tokens and not
 // stored.  No atomics; results are bitwise reproducible.
 #include "kq_device.h"
@@ -43,282 +51,325 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef float v32f __attribute__((ext_vector_type(32)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-constexpr int BM = 128;            // weight rows per workgroup
-constexpr int kCodeStride = 272;   // LDS bytes per token row of codes (256 + 16 pad)
-constexpr int kTokStride = 9;      // floats per token in the d8 plane (8 + 1 pad)
-constexpr int kZStride = 40;       // bf16 per token in the z plane (4 x 8 + 8 pad)
+constexpr int WR = 3, WT = 4;        // wavefront grid: row groups x token groups
+constexpr int NWAVE = WR * WT;       // 12 wavefronts: three per SIMD
+constexpr int BM = 64 * WR;          // 192 weight rows per workgroup
+constexpr int BN = 32 * WT;          // 128 tokens per workgroup
+constexpr int NTHR = 64 * NWAVE;     // 768 threads
+constexpr int kZStride = 40;         // bf16 per token in the z plane (32 + 8 pad)
+constexpr uint32_t kMagicBits = 0x4B400000u;   // 1.5 * 2^23
+constexpr float kMagic = 12582912.0f;
 
-template <int NTW>
-struct Smem {
-    static constexpr int BN = 64 * NTW;  // tokens per workgroup
-    uint8_t wraw[BM * kQ4KBytes];        // raw superblocks, 144 bytes per row
-    float dsc[8][BM];                    // D = d*sc    per (block, row)
-    uint32_t mins[BM][4];                // m of blocks 0..7 per row, as bf16 (exact)
-    float ndmin[BM];                     // -dmin per row
-    int8_t codes[BN * kCodeStride];      // q8 codes per token
-    float d8[BN * kTokStride];           // per (token, block)
-    uint16_t zs[BN * kZStride];          // z = d8 * (sum of the block's codes) per
-                                         // (token, block) as three bf16 parts
-                                         // [hi x 8][mid x 8][lo x 8][0 x 8]
+// Raw bytes of one superblock step, written by global_load_lds, laid out so
+// the compute phase's reads (32 consecutive rows or tokens, one 16-byte
+// chunk each) hit distinct LDS banks and every per-block offset is an
+// immediate of one per-lane base:
+//   * weight code chunk c (bytes 16c..16c+15 of the 128 code bytes) of row
+//     r at slot 128*(r/16) + 16*c + r%16 (sixteen rows side by side);
+//   * weight headers (d, dmin, twelve scale bytes) at slot r;
+//   * token code chunk c = 2j+h (q8_1 block j, half h) of token t at slot
+//     17*t + c (one pad slot per token);
+//   * token headers {f16 d8, f16 s} of (t, j) at dword 8*t + j.
+constexpr int kXStride = 17;         // 16-byte slots per token in the code region
+struct Stage {
+    uint4 wc[BM * 8];
+    uint4 wh[BM];
+    uint4 xc[BN * kXStride];
+    uint32_t xh[BN * 8];
 };
 
-template <int NTW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NTW == 1 ? 3 : 2, NTW == 1 ? 3 : 2)))
+struct Smem {
+    Stage st[2];
+    float2 dn[8][BM];        // per block j, row: D_j and -1.5*2^23*D_j
+    float d8[8][BN];         // per block j, token: d8 as f32
+    uint4 mb[BM];            // m_0..m_7 of the row as bf16 (exact: m < 64)
+    float nd[BM];            // -dmin of the row
+    uint16_t z[BN][kZStride];   // [hi x 8][mid x 8][lo x 8][0 x 8][pad]: bf16 parts of z
+};
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
+static_assert(NTHR == 4 * BM, "row headers are decoded by four threads per row");
+
+// Copies from memory straight into LDS: lane i's bytes, read at sbase + voff,
+// land at the (wavefront-uniform) LDS address + size*i.  Written as inline
+// assembly so the compiler does not tie every later LDS read to these
+// copies: it cannot tell the two stages apart and would wait for the next
+// step's copies before reading the current step.  The kernel waits for
+// them itself (vmcnt(0) and a barrier before a stage is read).  m0 is
+// written by the copies and used by nothing else in this file.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)p);
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, void* lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(sbase), "s"(lds_addr(lds)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const uint8_t* sbase, uint32_t voff, void* lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(voff), "s"(sbase), "s"(lds_addr(lds)) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// The copy instructions of a step (64 lanes each): 24 for weight codes (16
+// rows x 4 chunks; 16 lanes read one chunk of 16 consecutive rows), 3 for
+// weight headers (64 rows), 34 for token code slots (consecutive lanes read
+// consecutive 16-byte chunks of one token; a pad slot re-reads the token's
+// last chunk), 16 for token headers (8 tokens x 8 dwords).  Wavefronts 0..3
+// issue them, one kind each (0: weight codes, 1 and 2: halves of the token
+// codes, 3: token and weight headers): on each SIMD the oldest wavefront,
+// which the arbitration favours, takes the stalls of the memory pipeline
+// while the SIMD's two other wavefronts compute.  Rows and tokens beyond the
+// tensor are clamped to its last row / token.
+__device__ __forceinline__ void issue_stage(Stage& st, int wave, int lane, const uint8_t* w,
+                                            const uint8_t* xq, int sb, int m0, int n0, int M,
+                                            int N, int S) {
+    const uint32_t xrow = (uint32_t)S * 8 * kQ81Bytes, wrow = (uint32_t)S * kQ4KBytes;
+    const uint8_t* wb = w + (int64_t)sb * kQ4KBytes;
+    const uint8_t* xb = xq + (int64_t)sb * (8 * kQ81Bytes);
+    if (wave == 0) {
+#pragma unroll 4
+        for (int u = 0; u < 24; ++u) {
+            const int r = 16 * (u >> 1) + (lane & 15), c = 4 * (u & 1) + (lane >> 4);
+            dma16(wb, (uint32_t)min(m0 + r, M - 1) * wrow + 16 + 16 * c, &st.wc[64 * u]);
+        }
+    } else if (wave < 3) {
+#pragma unroll 1
+        for (int u = 17 * (wave - 1); u < 17 * wave; ++u) {
+            const int s = 64 * u + lane;
+            const int t = s / kXStride;
+            const int c = min(s - kXStride * t, 15);
+            dma16(xb, (uint32_t)min(n0 + t, N - 1) * xrow + kQ81Bytes * (c >> 1) + 4 + 16 * (c & 1),
+                  &st.xc[64 * u]);
+        }
+    } else if (wave == 3) {
+#pragma unroll 4
+        for (int u = 0; u < 16; ++u) {
+            const int s = 64 * u + lane;
+            dma4(xb, (uint32_t)min(n0 + (s >> 3), N - 1) * xrow + kQ81Bytes * (s & 7), &st.xh[64 * u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+            dma16(wb, (uint32_t)min(m0 + 64 * u + lane, M - 1) * wrow, &st.wh[64 * u]);
+    }
+}
+
+// One q8_1 block j of the superblock for this wavefront's two 32-row tiles.
+template <int J>
+__device__ __forceinline__ void block_step(v16f (&part)[2], const v16i& magic, const Stage& st,
+                                           const Smem& sm, int xa, int wa, int dnrow, int d8tok) {
+    // d8 of the sixteen tokens of this lane's outputs
+    float d8v[16];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 v = *(const float4*)((const char*)&sm.d8[J][0] + d8tok + 32 * g4);
+        d8v[4 * g4] = v.x; d8v[4 * g4 + 1] = v.y; d8v[4 * g4 + 2] = v.z; d8v[4 * g4 + 3] = v.w;
+    }
+    const uint4 ca = *(const uint4*)((const char*)st.xc + xa + 32 * J);
+    const v4i a = v4i{(int)ca.x, (int)ca.y, (int)ca.z, (int)ca.w};
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        // low nibbles of code pair J/2 for even J, high nibbles for odd J
+        const uint4 q = *(const uint4*)((const char*)st.wc + wa + 4096 * rt + 512 * (J >> 1));
+        const int sh = 4 * (J & 1);
+        const v4i b = v4i{(int)((q.x >> sh) & 0x0f0f0f0fu), (int)((q.y >> sh) & 0x0f0f0f0fu),
+                          (int)((q.z >> sh) & 0x0f0f0f0fu), (int)((q.w >> sh) & 0x0f0f0f0fu)};
+        const float2 dnv = *(const float2*)((const char*)&sm.dn[J][0] + dnrow + 256 * rt);
+        const v16f f = __builtin_bit_cast(v16f, __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, magic, 0, 0, 0));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float t = __builtin_fmaf(f[i], dnv.x, dnv.y);   // round(D*A)
+            part[rt][i] = __builtin_fmaf(t, d8v[i], part[rt][i]);
+        }
+    }
+}
+
+template <bool CLAMP>
+__global__ __launch_bounds__(NTHR, 1)
 void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq,
-                    float* __restrict__ y, int M, int N, int S) {
-    constexpr int BN = Smem<NTW>::BN;
-    __shared__ __align__(16) Smem<NTW> sm;
+                    float* __restrict__ y, int M, int N, int S, int mtiles, int ntiles) {
+    __shared__ __align__(16) Smem sm;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;  // wave position in the 2 x 2 grid
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h2 = lane >> 5;
-    const int m0 = blockIdx.x * BM;
-    const int n0 = blockIdx.y * BN;
-    const int64_t row_bytes = (int64_t)S * kQ4KBytes;
-    const int nb_row = S * 8;
+    const int wr = wave / WT, wt = wave % WT;
 
-    float acc[2][NTW][16];
+    // Tile of this workgroup.  Consecutive workgroups go to different XCDs
+    // (round robin); tiles are regrouped so each XCD walks a contiguous run
+    // of tiles, the token tiles of one row block after another, and shares
+    // those rows' weights in its L2.
+    int tm, tn;
+    {
+        const int64_t total = (int64_t)mtiles * ntiles;
+        const int64_t lin = blockIdx.x;
+        const int64_t q = total / 8, r = total % 8;
+        const int64_t xcd = lin % 8, slot = lin / 8;
+        const int64_t t = xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+        tm = (int)(t / ntiles);
+        tn = (int)(t % ntiles);
+    }
+    // A tile at the end of m or n starts early enough to lie inside the
+    // tensor (its first rows/tokens repeat the previous tile's and are not
+    // stored); the CLAMP form (a problem smaller than one tile) clamps.
+    const int m0 = CLAMP ? tm * BM : min(tm * BM, M - BM);
+    const int n0 = CLAMP ? tn * BN : min(tn * BN, N - BN);
+    const int mown = tm * BM, nown = tn * BN;   // first row / token this tile stores
+
+    issue_stage(sm.st[0], wave, lane, w, xq, 0, m0, n0, M, N, S);
+
+    // the fourth bf16 part of z is zero and never rewritten
+    for (int i = tid; i < BN * 8; i += NTHR) sm.z[i >> 3][24 + (i & 7)] = 0;
+
+    v16i magic;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int i = 0; i < 16; ++i) magic[i] = (int)kMagicBits;
+    asm volatile("" : "+v"(magic));   // one register block, read by every MFMA
+
+    v16f acc[2];
 #pragma unroll
-        for (int b = 0; b < NTW; ++b)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+        for (int i = 0; i < 16; ++i) acc[rt][i] = 0.0f;
+
+    // per-lane byte offsets of the compute phase's reads
+    const int tk = 32 * wt;                       // token offset of this wavefront
+    const int ta = tk + l32;                      // token of this lane's MFMA operand row
+    const int rw = 64 * wr + l32;                 // this lane's row in the first tile
+    const int xa = 16 * (kXStride * ta + h2);     // token codes: + 32*j
+    const int wa = 16 * (128 * (rw >> 4) + (rw & 15)) + 256 * h2;   // weight codes: + 512*(j/2) + 4096*rt
+    const int dnrow = 8 * rw;                     // (D, nc) of row rw in a block's row: + 256*rt
+    const int d8tok = 4 * (tk + 4 * h2);          // d8 of tokens tk+8g+4h2.. in a block's row: + 32*g
 
     for (int sb = 0; sb < S; ++sb) {
-        // ---- staging, every global load issued before the first LDS write.
-        // Weights: two threads per row; thread (row, e) takes the 16-byte
-        // chunks e, e+2, ... of the row's 144-byte superblock (9 chunks); the
-        // even thread also decodes the header chunk into D per sub-block,
-        // the eight m as bf16 and -dmin.  Activations: BN tokens x 8 q8_1
-        // blocks, 2 NTW (token, block) pairs per thread, each also writing
-        // the three bf16 parts of its z.
+        Stage& st = sm.st[sb & 1];
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's copies have landed
+        __syncthreads();                      // everyone's copies; the previous step's reads done
+
+        // ---- derive: token blocks (d8 as f32, z parts), then row headers
+        for (int i = tid; i < BN * 8; i += NTHR) {
+            const int j = i / BN, t = i % BN;   // consecutive lanes: consecutive tokens
+            const uint4 c0 = st.xc[kXStride * t + 2 * j];
+            const uint4 c1 = st.xc[kXStride * t + 2 * j + 1];
+            int bq = dot4(c0.x, 0x01010101u, 0);
+            bq = dot4(c0.y, 0x01010101u, bq);
+            bq = dot4(c0.z, 0x01010101u, bq);
+            bq = dot4(c0.w, 0x01010101u, bq);
+            bq = dot4(c1.x, 0x01010101u, bq);
+            bq = dot4(c1.y, 0x01010101u, bq);
+            bq = dot4(c1.z, 0x01010101u, bq);
+            bq = dot4(c1.w, 0x01010101u, bq);
+            const float d8 = half_bits_to_float(st.xh[8 * t + j]);
+            // z = d8*Bq is exact in f32; three bf16 parts by truncation,
+            // each the next eight significant bits (the last remainder has
+            // at most eight, so it is exact in bf16 too)
+            const float zf = d8 * (float)bq;
+            const uint32_t zh = __float_as_uint(zf) & 0xffff0000u;
+            const float r1 = zf - __uint_as_float(zh);
+            const uint32_t zm = __float_as_uint(r1) & 0xffff0000u;
+            const float r2 = r1 - __uint_as_float(zm);
+            const bool fin = __builtin_isfinite(zf);
+            sm.z[t][j] = (uint16_t)(zh >> 16);
+            sm.z[t][8 + j] = fin ? (uint16_t)(zm >> 16) : (uint16_t)0;
+            sm.z[t][16 + j] = fin ? (uint16_t)(__float_as_uint(r2) >> 16) : (uint16_t)0;
+            sm.d8[j][t] = d8;
+        }
+        // row headers: four threads per row (in four wavefront groups), two sub-blocks each
         {
-            // recompute the staging addresses every superblock: kept live
-            // across the MFMA loop they would cost registers it needs
-            int ts = tid;
-            asm volatile("" : "+v"(ts));
-            const int rr = ts >> 1, e = ts & 1;
-            const int gr = min(m0 + rr, M - 1);
-            const uint8_t* p = w + (int64_t)gr * row_bytes + (int64_t)sb * kQ4KBytes;
-            uint4 cw[5];
-#pragma unroll
-            for (int c = 0; c < 5; ++c) {
-                const int ch = e + 2 * c;
-                if (ch < 9) cw[c] = load16(p + 16 * ch);
-            }
-            uint4 c0[2 * NTW], c1[2 * NTW];
-            uint32_t hd[2 * NTW];
-#pragma unroll
-            for (int i = 0; i < 2 * NTW; ++i) {
-                const int idx = ts + 256 * i;
-                const int t = idx >> 3, j = idx & 7;
-                const int gt = min(n0 + t, N - 1);
-                const uint8_t* blk = xq + ((int64_t)gt * nb_row + sb * 8 + j) * kQ81Bytes;
-                hd[i] = *(const uint32_t*)blk;
-                c0[i] = load16(blk + 4);
-                c1[i] = load16(blk + 20);
-            }
-#pragma unroll
-            for (int c = 0; c < 5; ++c) {
-                const int ch = e + 2 * c;
-                if (ch < 9) *(uint4*)(sm.wraw + rr * kQ4KBytes + 16 * ch) = cw[c];
-            }
-            if (e == 0) {   // (D, Mn) per sub-block from the header chunk
-                const uint4 hdr = cw[0];
-                const float d = half_bits_to_float(hdr.x), dmin = half_bits_to_float(hdr.x >> 16);
-                const uint32_t lowS = hdr.y & 0x3f3f3f3fu, lowM = hdr.z & 0x3f3f3f3fu;
-                const uint32_t hiS = (hdr.w & 0x0f0f0f0fu) | ((hdr.y >> 2) & 0x30303030u);
-                const uint32_t hiM = ((hdr.w >> 4) & 0x0f0f0f0fu) | ((hdr.z >> 2) & 0x30303030u);
-                uint32_t mb[4];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t s4 = j < 4 ? lowS : hiS, m4 = j < 4 ? lowM : hiM;
-                    const int sh = 8 * (j & 3);
-                    sm.dsc[j][rr] = d * (float)((s4 >> sh) & 0xff);
-                    // m < 64 has at most six significant bits: its bf16 is exact
-                    const uint32_t mbits = __float_as_uint((float)((m4 >> sh) & 0xff)) >> 16;
-                    if (j & 1) mb[j >> 1] |= mbits << 16;
-                    else mb[j >> 1] = mbits;
-                }
-                *(uint4*)sm.mins[rr] = make_uint4(mb[0], mb[1], mb[2], mb[3]);
-                sm.ndmin[rr] = -dmin;
-            }
-#pragma unroll
-            for (int i = 0; i < 2 * NTW; ++i) {
-                const int idx = tid + 256 * i;
-                const int t = idx >> 3, j = idx & 7;
-                const uint32_t cc[8] = {c0[i].x, c0[i].y, c0[i].z, c0[i].w,
-                                        c1[i].x, c1[i].y, c1[i].z, c1[i].w};
-                int sum = 0;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) sum = dot4(cc[q], 0x01010101u, sum);
-                const float d8 = half_bits_to_float(hd[i]);
-                uint4* dst = (uint4*)(sm.codes + t * kCodeStride + 32 * j);
-                dst[0] = c0[i];
-                dst[1] = c1[i];
-                sm.d8[t * kTokStride + j] = d8;
-                // z in three bf16 parts, each the next eight significant bits
-                // (truncation leaves an exact remainder; a finite z has 24)
-                const float z = d8 * (float)sum;
-                const uint32_t zh = __float_as_uint(z) & 0xffff0000u;
-                const float r1 = z - __uint_as_float(zh);
-                const uint32_t zm = __float_as_uint(r1) & 0xffff0000u;
-                const float r2 = r1 - __uint_as_float(zm);
-                const bool fin = __builtin_isfinite(z);
-                uint16_t* zt = sm.zs + t * kZStride + j;
-                zt[0] = (uint16_t)(zh >> 16);
-                zt[8] = fin ? (uint16_t)(zm >> 16) : (uint16_t)0;
-                zt[16] = fin ? (uint16_t)(__float_as_uint(r2) >> 16) : (uint16_t)0;
-                zt[24] = 0;
-            }
+            const int r = tid % BM, qb = tid / BM;    // 768 threads = 4 x 192 rows
+            const uint4 hdr = st.wh[r];
+            const float d = half_bits_to_float(hdr.x);
+            // six-bit scales and mins: bytes 4..7 hold sc_0..3 (low six bits)
+            // and the top bits of sc_4..7; bytes 8..11 the same for m; bytes
+            // 12..15 the low nibbles of sc_4..7 and m_4..7
+            const uint32_t sw = qb < 2 ? hdr.y & 0x3f3f3f3fu
+                                       : (hdr.w & 0x0f0f0f0fu) | ((hdr.y >> 2) & 0x30303030u);
+            const uint32_t mw = qb < 2 ? hdr.z & 0x3f3f3f3fu
+                                       : ((hdr.w >> 4) & 0x0f0f0f0fu) | ((hdr.z >> 2) & 0x30303030u);
+            const int sh = 16 * (qb & 1);               // bytes 2(qb&1), 2(qb&1)+1 of the word
+            const float D0 = d * (float)((sw >> sh) & 0xffu), D1 = d * (float)((sw >> (sh + 8)) & 0xffu);
+            sm.dn[2 * qb][r] = make_float2(D0, -kMagic * D0);
+            sm.dn[2 * qb + 1][r] = make_float2(D1, -kMagic * D1);
+            // m < 64 is exact in bf16: the top half of its f32 pattern
+            const uint32_t m0b = __float_as_uint((float)((mw >> sh) & 0xffu)) >> 16;
+            const uint32_t m1b = __float_as_uint((float)((mw >> (sh + 8)) & 0xffu)) >> 16;
+            ((uint32_t*)&sm.mb[r])[qb] = m0b | (m1b << 16);
+            if (qb == 0) sm.nd[r] = -half_bits_to_float(hdr.x >> 16);
         }
         __syncthreads();
+        // the next step's copies, into the other stage (free since the first barrier)
+        if (sb + 1 < S) issue_stage(sm.st[(sb + 1) & 1], wave, lane, w, xq, sb + 1, m0, n0, M, N, S);
 
-        // Per-superblock partial of every output, per 32 x 32 tile:
-        //   part  = -dmin * sum_j m_j z_j      two bf16 MFMAs over the 8
-        //           blocks x 3 parts of z (products exact, f32 sums), one
-        //           f32 multiply per output;
-        // then each pair of blocks (2p, 2p+1) -- the low and high nibbles of
-        // the same code bytes -- adds
-        //   S     = D (x) d8           f32 MFMA, two outer products
-        //   part += float(A_2p) * S_2p + float(A_2p+1) * S_2p+1   (VALU)
-        // with A the exact int32 block dots from the int8 MFMA.
-        v16f part[2][NTW];
+        // ---- compute: two 32-row tiles x 32 tokens per wavefront
+        v16f part[2];
         {
-            v8bf am[2], bz[NTW][2];
+            const v8bf za0 = __builtin_bit_cast(v8bf, *(const uint4*)&sm.z[ta][8 * h2]);
+            const v8bf za1 = __builtin_bit_cast(v8bf, *(const uint4*)&sm.z[ta][16 + 8 * h2]);
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-                am[mt] = __builtin_bit_cast(v8bf, *(const uint4*)sm.mins[wm * 64 + mt * 32 + l32]);
+            for (int rt = 0; rt < 2; ++rt) {
+                const int r = rw + 32 * rt;
+                const v8bf mbv = __builtin_bit_cast(v8bf, sm.mb[r]);
+                const v16f zero = {};
+                v16f pm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za0, mbv, zero, 0, 0, 0);
+                pm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za1, mbv, pm, 0, 0, 0);
+                const float nd = sm.nd[r];
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const uint16_t* zt = sm.zs + (wn * 32 * NTW + nt * 32 + l32) * kZStride + 8 * h2;
-                bz[nt][0] = __builtin_bit_cast(v8bf, *(const uint4*)zt);
-                bz[nt][1] = __builtin_bit_cast(v8bf, *(const uint4*)(zt + 16));
-            }
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                // -dmin of this lane's 16 output rows: 4 runs of 4
-                float nd[16];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const float4 v = *(const float4*)(sm.ndmin + wm * 64 + mt * 32 + 8 * g + 4 * h2);
-                    nd[4 * g] = v.x; nd[4 * g + 1] = v.y; nd[4 * g + 2] = v.z; nd[4 * g + 3] = v.w;
-                }
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) {
-                    const v16f zero = {};
-                    v16f pm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[mt], bz[nt][0], zero, 0, 0, 0);
-                    pm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[mt], bz[nt][1], pm, 0, 0, 0);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) part[mt][nt][i] = nd[i] * pm[i];
-                }
+                for (int i = 0; i < 16; ++i) part[rt][i] = nd * pm[i];
             }
         }
-
-#pragma unroll 1
-        for (int pp = 0; pp < 4; ++pp) {
-            const int jl = 2 * pp + h2;   // this lane's block within the pair for the f32 MFMA
-            v4i A[2][2];
-            float Dp[2];
+        // One block at a time: the scheduling fences keep the compiler from
+        // hoisting later blocks' loads (and their registers) into this one.
+        block_step<0>(part, magic, st, sm, xa, wa, dnrow, d8tok);
+        __builtin_amdgcn_sched_barrier(0);
+        block_step<1>(part, magic, st, sm, xa, wa, dnrow, d8tok);
+        __builtin_amdgcn_sched_barrier(0);
+        block_step<2>(part, magic, st, sm, xa, wa, dnrow, d8tok);
+        __builtin_amdgcn_sched_barrier(0);
+        block_step<3>(part, magic, st, sm, xa, wa, dnrow, d8tok);
+        __builtin_amdgcn_sched_barrier(0);
+        block_step<4>(part, magic, st, sm, xa, wa, dnrow, d8tok);
+        __builtin_amdgcn_sched_barrier(0);
+        block_step<5>(part, magic, st, sm, xa, wa, dnrow, d8tok);
+        __builtin_amdgcn_sched_barrier(0);
+        block_step<6>(part, magic, st, sm, xa, wa, dnrow, d8tok);
+        __builtin_amdgcn_sched_barrier(0);
+        block_step<7>(part, magic, st, sm, xa, wa, dnrow, d8tok);
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const int r = wm * 64 + mt * 32 + l32;
-                const uint4 q = *(const uint4*)(sm.wraw + r * kQ4KBytes + 16 + 32 * pp + 16 * h2);
-                A[mt][0] = v4i{(int)(q.x & 0x0f0f0f0fu), (int)(q.y & 0x0f0f0f0fu),
-                               (int)(q.z & 0x0f0f0f0fu), (int)(q.w & 0x0f0f0f0fu)};
-                A[mt][1] = v4i{(int)((q.x >> 4) & 0x0f0f0f0fu), (int)((q.y >> 4) & 0x0f0f0f0fu),
-                               (int)((q.z >> 4) & 0x0f0f0f0fu), (int)((q.w >> 4) & 0x0f0f0f0fu)};
-                Dp[mt] = sm.dsc[jl][r];
-            }
-            v4i B[NTW][2];
-            float dp[NTW];
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const int t = wn * 32 * NTW + nt * 32 + l32;
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const uint4 a = *(const uint4*)(sm.codes + t * kCodeStride + 32 * (2 * pp + e) + 16 * h2);
-                    B[nt][e] = v4i{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
-                }
-                dp[nt] = sm.d8[t * kTokStride + jl];
-            }
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) {
-                    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-                    const v32f zf = {};
-                    const v16i R0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mt][0], B[nt][0], zero, 0, 0, 0);
-                    const v16i R1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[mt][1], B[nt][1], zero, 0, 0, 0);
-                    const v32f S = __builtin_amdgcn_mfma_f32_32x32x1f32(Dp[mt], dp[nt], zf, 0, 0, 0);
-                    v16f pt = part[mt][nt];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        pt[i] += (float)R0[i] * S[i];
-                        pt[i] += (float)R1[i] * S[16 + i];
-                    }
-                    part[mt][nt] = pt;
-                }
-        }
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < NTW; ++b)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[a][b][i] += part[a][b][i];
-        __syncthreads();
+        for (int rt = 0; rt < 2; ++rt) acc[rt] += part[rt];
     }
 
-    // ---- store: lane holds token (l32) and 16 rows of each tile
+    // ---- store: lane holds weight row l32 of each tile and 16 tokens
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int rt = 0; rt < 2; ++rt) {
+        const int m = m0 + 64 * wr + 32 * rt + l32;
+        if (m < mown || m >= M) continue;
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-            const int n = n0 + wn * 32 * NTW + nt * 32 + l32;
-            if (n >= N) continue;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = m0 + wm * 64 + mt * 32 + 8 * (i >> 2) + 4 * h2 + (i & 3);
-                if (m < M) y[(int64_t)n * M + m] = acc[mt][nt][i];
-            }
+        for (int i = 0; i < 16; ++i) {
+            const int n = n0 + 32 * wt + 8 * (i >> 2) + 4 * h2 + (i & 3);
+            if (n >= nown && n < N) y[(int64_t)n * M + m] = acc[rt][i];
         }
+    }
 }
 
 }  // namespace
 
-// Tokens per workgroup, 128 (NTW = 2: two workgroups per CU) or 64 (NTW =
-// 1: 168 VGPRs and 49 KB of LDS, three per CU, whose staging then hides
-// better behind the others' arithmetic).  Measured on one box at 2048
-// tokens, a full round of the 64-token form takes ~0.75 of a round of the
-// 128-token one, so the form with the fewer weighted rounds is launched:
-// QKV 4608 rows (1152 small tiles in two rounds of 768 slots against 576
-// large ones in two rounds of 512) takes 64 tokens, 206 -> 158 us; gate/up
-// 18944 rows (seven small rounds against five large) and down 3584 rows
-// (two small rounds against one large) take 128.
 hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                           int64_t k, int cus, hipStream_t stream) {
+    (void)cus;
     const int S = (int)(k / kQK);
-    const int64_t mt = (m + BM - 1) / BM;
-    const int64_t t2 = mt * ((n + 127) / 128), t1 = mt * ((n + 63) / 64);
-    const int64_t s2 = (int64_t)cus * std::max(1, occupancy((const void*)mmq_q4k_kernel<2>, 256, 0));
-    const int64_t s1 = (int64_t)cus * std::max(1, occupancy((const void*)mmq_q4k_kernel<1>, 256, 0));
-    // the 64-token grid must also fit 65535 workgroups in y (n up to 65535*128
-    // is accepted, which only the 128-token form covers)
-    const bool small = (n + 63) / 64 <= 65535 && 3 * ((t1 + s1 - 1) / s1) < 4 * ((t2 + s2 - 1) / s2);
-    const int bn = small ? 64 : 128;
-    dim3 grid((unsigned)mt, (unsigned)((n + bn - 1) / bn));
-    if (small)
-        hipLaunchKernelGGL(mmq_q4k_kernel<1>, grid, dim3(256), 0, stream, (const uint8_t*)w,
-                           (const uint8_t*)xq, y, (int)m, (int)n, S);
+    const int64_t mt = (m + BM - 1) / BM, nt = (n + BN - 1) / BN;
+    if (mt * nt > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)(mt * nt));
+    if (m < BM || n < BN)
+        hipLaunchKernelGGL(mmq_q4k_kernel<true>, grid, dim3(NTHR), 0, stream, (const uint8_t*)w,
+                           (const uint8_t*)xq, y, (int)m, (int)n, S, (int)mt, (int)nt);
     else
-        hipLaunchKernelGGL(mmq_q4k_kernel<2>, grid, dim3(256), 0, stream, (const uint8_t*)w,
-                           (const uint8_t*)xq, y, (int)m, (int)n, S);
+        hipLaunchKernelGGL(mmq_q4k_kernel<false>, grid, dim3(NTHR), 0, stream, (const uint8_t*)w,
+                           (const uint8_t*)xq, y, (int)m, (int)n, S, (int)mt, (int)nt);
     return hipGetLastError();
 }
 
