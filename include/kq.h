@@ -54,6 +54,12 @@
  *     on every run (no atomics, fixed reduction order);
  *   - sizes of zero rows / tokens (m == 0, n == 0, rows == 0, batch rows of an
  *     empty matrix) are valid and launch nothing;
+ *   - every f16 scale (d, dmin, d8) may be zero, subnormal or normal and is
+ *     decoded exactly; an output that reads a non-finite scale (an f16 inf
+ *     or NaN -- kq_quantize_q8_1 writes d8 = +inf for a block whose largest
+ *     magnitude exceeds about 65504*127 = 8.3e6) has an unspecified value
+ *     (finite, inf or NaN), and only the outputs of that weight row or that
+ *     token are affected;
  *   - calls are thread-safe; the error text is per host thread.
  */
 #ifndef KQ_H_

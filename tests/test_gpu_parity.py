@@ -209,14 +209,16 @@ def test_gemv_deterministic(kq, kind):
 
 # ----------------------------------------------------------------- MMQ -----
 
-# Workgroup token tiles on a 256-CU MI355X.  Q6_K: the small shapes take
-# 32 tokens; 3584 x 640 and 4096 x 1024 are the first grids of 64 and 128
-# tokens to give every CU a workgroup.  Q4_K: every shape but 3584 x 2048
-# takes 64 tokens; that one (448 tiles of 128 tokens, one round of 512
-# slots) keeps 128.
+# Workgroup tiles on a 256-CU MI355X.  Q6_K: the small shapes take 32
+# tokens; 3584 x 640 and 4096 x 1024 are the first grids of 64 and 128
+# tokens to give every CU a workgroup.  Q4_K: 192 rows x 128 tokens, with a
+# clamped form for problems smaller than one tile in either direction
+# (m < 192 or n < 128); 7168 x 2048 is 608 tiles, more than two rounds of
+# one workgroup per CU, with ragged last row tiles.
 MMQ_SHAPES = [(1, 1, 256), (5, 3, 512), (128, 128, 256), (200, 150, 1024), (129, 257, 768),
               (300, 64, 3584), (64, 300, 2048), (131, 70, 18944), (3584, 640, 256),
-              (4096, 1024, 256), (3584, 2048, 256), (130, 70, 65536)]
+              (4096, 1024, 256), (3584, 2048, 256), (130, 70, 65536), (7168, 2048, 256),
+              (191, 127, 512), (193, 129, 512)]
 MMQ_CASES = [(kind, *shape) for kind in ("q4k", "q6k") for shape in MMQ_SHAPES]
 
 
@@ -333,6 +335,101 @@ def test_mmq_prefill_sampled(kq, cfg, i):
     y_ref, den = oracle.matmul_pairs(kind, w, xq_ref, m, n, k, tok, row)
     check_close(y[tok, row], y_ref, den, f"cfg{cfg} {op['label']} ({tok.size} outputs)")
     assert np.all(np.isfinite(y))
+
+
+PREFILL_FULL = [(4, i) for i, op in enumerate(WORKLOADS[4]["ops"]) if op["label"] in ("down", "qkv")]
+
+
+@pytest.mark.parametrize("cfg,i", PREFILL_FULL,
+                         ids=[f"cfg{c}-{WORKLOADS[c]['ops'][i]['label']}" for c, i in PREFILL_FULL])
+def test_mmq_prefill_full(kq, cfg, i):
+    """Every output of a full-size prefill launch against the oracle: down
+    3584 x 18944 x 2048 (19 x 16 tiles, more than one round) and qkv
+    4608 x 3584 x 2048 (24 x 16 tiles)."""
+    op = WORKLOADS[cfg]["ops"][i]
+    kind = op["op"][-3:]
+    m, n, k = op["m"], op["n"], op["k"]
+    say(f"mmq {kind} cfg{cfg} {op['label']} m={m} n={n} k={k} (every output)")
+    w = tensor(cfg, op["w"])
+    x = tensor(cfg, op["x"])
+    xq = kq.quantize_q8_1(dev(x))
+    xq_h = host(xq)
+    y = host(mmq(kq, kind)(dev(w), xq, m, n, k))
+    y_ref, den = oracle.matmul(kind, w, xq_h, m, n, k)
+    check_close(y, y_ref, den, f"cfg{cfg} {op['label']} ({m * n} outputs)")
+
+
+# Activations scaled so that every q8_1 scale d8 = amax/127 lands in the f16
+# subnormal range [2^-24, 2^-14) or rounds to zero: N(0,1) values (amax about
+# 2.5 to 4.5) times 2^e, with e from -10 down to -24 by row unless given.
+def _subnormal_acts(seed, rows, k, exps=None):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, k)).astype(np.float32)
+    e = -10 - (np.arange(rows) % 15) if exps is None else np.asarray(exps)
+    return (x * np.exp2(e.astype(np.float64))[:, None]).astype(np.float32)
+
+
+def _d8_values(xq):
+    blk = xq.reshape(-1, 36)
+    return oracle.f16_bits_to_f32(blk[:, 0:2].copy().view(np.uint16).ravel())
+
+
+SUBNORMAL_MMQ = [("q4k", 400, 300, 1024), ("q4k", 150, 100, 768),      # full and clamped tiles
+                 ("q6k", 300, 40, 1024), ("q6k", 3584, 640, 256), ("q6k", 4096, 1024, 256)]
+
+
+@pytest.mark.parametrize("kind,m,n,k", SUBNORMAL_MMQ, ids=[f"{c[0]}-m{c[1]}-n{c[2]}" for c in SUBNORMAL_MMQ])
+def test_mmq_subnormal_d8(kq, kind, m, n, k):
+    say(f"mmq {kind} subnormal d8 m={m} n={n} k={k}")
+    w, _, _ = random_case(m + n + 5, kind, m, k, 1)
+    xq = oracle.quantize_q8_1(_subnormal_acts(m + n, n, k))
+    d8 = _d8_values(xq)
+    assert np.all(d8 < 2.0 ** -14) and np.any((d8 > 0) & (d8 < 2.0 ** -20)) and np.any(d8 == 0)
+    y_ref, den = oracle.matmul(kind, w, xq, m, n, k)
+    y = host(mmq(kq, kind)(dev(w), dev(xq), m, n, k))
+    check_close(y, y_ref, den, f"mmq {kind} subnormal d8")
+
+
+@pytest.mark.parametrize("kind", ["q4k", "q6k"])
+@pytest.mark.parametrize("batch", [1, 4])
+def test_gemv_subnormal_d8(kq, kind, batch):
+    m, k = 1000, 4096
+    say(f"gemv {kind} subnormal d8 m={m} k={k} batch={batch}")
+    w, _, res = random_case(batch + 40, kind, m, k, batch, with_residual=True)
+    exps = [-17] if batch == 1 else [-10, -13, -16, -18]
+    xq = oracle.quantize_q8_1(_subnormal_acts(batch, batch, k, exps))
+    d8 = _d8_values(xq)
+    assert np.all(d8 < 2.0 ** -14) and np.all(d8 > 0)
+    res = (res * np.float32(2.0 ** -20)).astype(np.float32)
+    y_ref, den = oracle.matmul(kind, w, xq, m, batch, k, residual=res)
+    check_close(run_gemv(kq, kind, w, xq, m, k, batch, res), y_ref, den, f"gemv {kind} subnormal d8")
+
+
+@pytest.mark.parametrize("kind", ["q4k", "q6k"])
+def test_nonfinite_scale_confined(kq, kind):
+    """An f16 inf scale in one weight row (d of its first superblock) and in
+    one token (a q8_1 block whose values exceed 65504*127) leaves every other
+    output of the GEMV and of both MMQ forms within the oracle bound."""
+    m, n, k, bad_row, bad_tok = 300, 260, 1024, 11, 7
+    say(f"{kind} non-finite scales confined m={m} n={n} k={k}")
+    w, x, _ = random_case(4242, kind, m, k, n)
+    x[bad_tok, 64] = np.float32(1e7)
+    sb = w.reshape(m, k // 256, -1)
+    off = 0 if kind == "q4k" else 208
+    sb[bad_row, 0, off:off + 2] = np.array([0x7C00], dtype=np.uint16).view(np.uint8)
+    xq = oracle.quantize_q8_1(x)
+    assert _d8_values(xq[bad_tok])[2] == np.inf
+    y_ref, den = oracle.matmul(kind, w, xq, m, n, k)
+    keep = np.ones((n, m), dtype=bool)
+    keep[bad_tok, :] = False
+    keep[:, bad_row] = False
+    for nn, mm in ((n, m), (100, 150)):           # full and (q4k) clamped tiles
+        y = host(mmq(kq, kind)(dev(w[:mm]), dev(xq[:nn]), mm, nn, k))
+        kp = keep[:nn, :mm]
+        check_close(y[kp], y_ref[:nn, :mm][kp], den[:nn, :mm][kp], f"mmq {kind} n{nn} m{mm}")
+    g = run_gemv(kq, kind, w, xq[5:9], m, k, 4)
+    kp = keep[5:9]
+    check_close(g[kp], y_ref[5:9][kp], den[5:9][kp], f"gemv {kind} batch 4")
 
 
 @pytest.mark.parametrize("kind", ["q4k", "q6k"])
