@@ -191,22 +191,27 @@ def timed_steps(wl: Workload, steps: int, warmup: int, graphs=None):
     return start.elapsed_time(end) / steps
 
 
-def kernel_durations(wl: Workload, target_ms: float = 20.0):
-    """Average duration (ms) of every launch of the step.  For each launch a
-    HIP graph holds it once per weight copy, back to back on one stream; the
-    graph is replayed between two HIP events recorded on the stream the
-    kernels run on, and the elapsed time is divided by the launch count."""
+def kernel_durations(wl: Workload, target_ms: float = 10.0, rounds: int = 5):
+    """Duration (ms) of every launch of the step.  For each launch a HIP graph
+    holds it once per weight copy, back to back on one stream.  In each of
+    `rounds` interleaved rounds every launch's graph is replayed between two
+    HIP events recorded on the stream the kernels run on, and the elapsed
+    time is divided by the launch count.  Returns (label, kind, mean, median,
+    min) over the rounds."""
     import torch
 
     side = torch.cuda.Stream()
-    out = []
     launches = wl.launches(0)
-    for j, (label, kind, _) in enumerate(launches):
+    graphs = []
+    for j in range(len(launches)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
             for c in range(wl.ncopies):
                 wl.launches(c)[j][2]()
-        stream = torch.cuda.current_stream()
+        graphs.append(g)
+    stream = torch.cuda.current_stream()
+    reps = []
+    for g in graphs:
         g.replay()
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
@@ -215,14 +220,23 @@ def kernel_durations(wl: Workload, target_ms: float = 20.0):
         g.replay()
         b.record(stream)
         torch.cuda.synchronize()
-        reps = max(3, min(200, int(target_ms / max(a.elapsed_time(b), 1e-3))))
-        a.record(stream)
-        for _ in range(reps):
-            g.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        out.append((label, kind, a.elapsed_time(b) / (reps * wl.ncopies)))
-        del g
+        reps.append(max(3, min(200, int(target_ms / max(a.elapsed_time(b), 1e-3)))))
+    per = [[] for _ in graphs]
+    for _ in range(rounds):
+        for j, g in enumerate(graphs):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps[j]):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            per[j].append(a.elapsed_time(b) / (reps[j] * wl.ncopies))
+    out = []
+    for j, (label, kind, _) in enumerate(launches):
+        v = sorted(per[j])
+        out.append((label, kind, sum(v) / len(v), v[len(v) // 2], v[0]))
+    del graphs
     return out
 
 
@@ -394,6 +408,75 @@ def measure_split(cfg: int):
     return {"workload": wl["name"], "layouts": out}
 
 
+class ClockPower:
+    """Engine clock and board power sampled from the driver's sysfs files
+    while a workload runs: the current level of pp_dpm_sclk (the line marked
+    '*') and hwmon power1_input (microwatts), every `period` seconds on a
+    helper thread.  The summary keeps the samples taken while the engine
+    clock was above its idle level."""
+
+    def __init__(self, period: float = 0.02):
+        import glob
+        import threading
+
+        self.period = period
+        self.samples = []
+        self.sclk = self.power = None
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            if os.path.exists(os.path.join(dev, "pp_dpm_sclk")):
+                self.sclk = os.path.join(dev, "pp_dpm_sclk")
+                pw = sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_input")))
+                self.power = pw[0] if pw else None
+                break
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        mhz = watts = None
+        try:
+            for line in open(self.sclk):
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*Mhz", line, flags=re.I)
+                    mhz = int(m.group(1)) if m else None
+            if self.power:
+                watts = int(open(self.power).read().strip()) / 1e6
+        except (OSError, ValueError):
+            pass
+        return mhz, watts
+
+    def _run(self):
+        while not self._stop.is_set():
+            self.samples.append(self._read())
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.sclk:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.sclk:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.sclk:
+            return {"source": None, "note": "no pp_dpm_sclk under /sys/class/drm"}
+        busy = [(c, w) for c, w in self.samples if c is not None and c > 500]
+        out = {"source": f"{self.sclk} ('*' level), {self.power} (uW)",
+               "samples": len(self.samples), "busy_samples": len(busy)}
+        if busy:
+            cs = sorted(c for c, _ in busy)
+            ws = sorted(w for _, w in busy if w is not None)
+            out.update({"sclk_MHz_median": cs[len(cs) // 2], "sclk_MHz_min": cs[0],
+                        "sclk_MHz_max": cs[-1]})
+            if ws:
+                out.update({"power_W_median": round(ws[len(ws) // 2], 1),
+                            "power_W_max": round(ws[-1], 1)})
+        return out
+
+
 def measure(cfg: int, steps: int, warmup: int, use_graph: bool):
     import torch
 
@@ -401,72 +484,123 @@ def measure(cfg: int, steps: int, warmup: int, use_graph: bool):
     wl.step(0)                      # first calls outside any capture
     torch.cuda.synchronize()
     graphs = build_graphs(wl) if use_graph else None
-    ms = timed_steps(wl, steps, warmup, graphs)
-    durs = kernel_durations(wl)
+    with ClockPower() as cp:
+        ms = timed_steps(wl, steps, warmup, graphs)
+        durs = kernel_durations(wl)
     del graphs
-    return wl, ms, durs
+    return wl, ms, durs, cp.summary()
+
+
+# Forms of kq_read_probe swept for the read ceiling: (workgroups per CU, 0
+# for one workgroup per chunk; 16-byte loads in flight per thread).
+PROBE_FORMS = [(0, u) for u in (4, 8, 16, 32)] + [(w, u) for w in (1, 2, 3, 4, 8) for u in (8, 16, 32)]
+
+
+def _probe_label(form):
+    w, u = form
+    return f"one-shot, {u} loads/thread" if w == 0 else f"persistent {w} WG/CU, {u} loads/thread"
+
+
+def _cus() -> int:
+    import torch
+
+    return torch.cuda.get_device_properties(0).multi_processor_count
 
 
 def stream_read_ceiling(nbytes: int = 2 << 30, reps: int = 10):
-    """Measured streaming-read ceiling of the device: kq_read_probe (16-byte
-    loads, one workgroup per 32 KiB, an xor per wavefront stored) over a
-    2 GiB buffer, larger than the Infinity Cache, event-timed, median of
-    `reps` launches.  The 8 TB/s spec peak stays the roofline; this is the
-    practical read rate beside it."""
+    """Measured streaming-read ceiling of the device: every form of
+    kq_read_probe in PROBE_FORMS (one-shot and persistent grids, 4 to 32
+    16-byte loads in flight per thread) over a 2 GiB buffer, larger than the
+    Infinity Cache, event-timed, median of `reps` launches each; the best
+    form is the ceiling.  The 8 TB/s spec peak stays the roofline; this is
+    the practical read rate beside it."""
     import torch
 
     import q6_q8_matmul_amd as kq
 
+    cus = _cus()
     buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    out = torch.empty(kq.kq_read_probe_words(nbytes), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    for _ in range(2):
-        kq.kq_read_probe(buf, nbytes, out, stream.cuda_stream)
-    ts = []
-    for _ in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        kq.kq_read_probe(buf, nbytes, out, stream.cuda_stream)
-        b.record(stream)
-        b.synchronize()
-        ts.append(a.elapsed_time(b) * 1e-3)
-    del buf, out
+    sweep = {}
+    for form in PROBE_FORMS:
+        grid = form[0] * cus
+        out = torch.empty(kq.kq_read_probe_words(nbytes, grid, form[1]), dtype=torch.int32, device="cuda")
+        for _ in range(2):
+            kq.kq_read_probe(buf, nbytes, out, grid, form[1], stream.cuda_stream)
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            kq.kq_read_probe(buf, nbytes, out, grid, form[1], stream.cuda_stream)
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        t = sorted(ts)[len(ts) // 2]
+        sweep[_probe_label(form)] = round(nbytes / t / 1e9, 1)
+        del out
+    del buf
     torch.cuda.empty_cache()
-    t = sorted(ts)[len(ts) // 2]
-    return {"GBps": round(nbytes / t / 1e9, 1), "bytes": nbytes,
-            "how": "kq_read_probe (16-byte loads) over 2 GiB, median of 10 event-timed launches"}
+    best = max(sweep, key=sweep.get)
+    return {"GBps": sweep[best], "form": best, "bytes": nbytes, "sweep_GBps": sweep,
+            "how": "kq_read_probe over 2 GiB in every form of the sweep (one-shot and persistent "
+                   "grids, 4-32 16-byte loads in flight per thread), median of 10 event-timed "
+                   "launches each; the best form is the ceiling"}
 
 
 def read_floors_us(wl: Workload):
-    """Per GEMV launch of the step, the time kq_read_probe takes to read the
-    same weight tensor, rotated over the same copies and timed the same way
-    as the launch itself (graph replay of one launch per copy)."""
+    """Per GEMV launch of the step, the least time any kq_read_probe form of
+    PROBE_FORMS takes to read the same weight tensor, rotated over the same
+    copies and timed the same way as the launch itself (graph replay of one
+    launch per copy).  Returns {label: (us, form)}."""
     import torch
 
     import q6_q8_matmul_amd as kq
 
+    cus = _cus()
     out = {}
     for op in wl.ops:
         if not op["op"].startswith("gemv"):
             continue
         bufs = [wl.w[c][op["w"]] for c in range(wl.ncopies)]
         nbytes = bufs[0].numel() // 16 * 16
-        res = torch.empty(kq.kq_read_probe_words(nbytes), dtype=torch.int32, device="cuda")
-        launches = [lambda b=b: kq.kq_read_probe(b, nbytes, res) for b in bufs]
-        ms = _graph_time_ms(lambda: [f() for f in launches], per_graph=1) / len(launches)
-        out[op["label"]] = round(ms * 1e3, 2)
-        del res
+        best = None
+        for form in PROBE_FORMS:
+            grid = form[0] * cus
+            res = torch.empty(kq.kq_read_probe_words(nbytes, grid, form[1]), dtype=torch.int32, device="cuda")
+            launches = [lambda b=b: kq.kq_read_probe(b, nbytes, res, grid, form[1]) for b in bufs]
+            ms = _graph_time_ms(lambda: [f() for f in launches], target_ms=5.0, per_graph=1) / len(launches)
+            if best is None or ms < best[0]:
+                best = (ms, form)
+            del res
+        out[op["label"]] = (round(best[0] * 1e3, 2), _probe_label(best[1]))
     return out
 
 
-def _cpu_model() -> str:
+def _cpu_model() -> dict:
+    """lscpu's model fields of the host (under a hypervisor the model name
+    may be generic; family/model/stepping still identify the part)."""
+    import subprocess
+
+    out = {}
     try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
-    except OSError:
+        text = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in text.splitlines():
+            key, _, val = line.partition(":")
+            key = key.strip()
+            if key in ("Model name", "Vendor ID", "CPU family", "Model", "Stepping",
+                       "Hypervisor vendor", "CPU(s)"):
+                out[key] = val.strip()
+    except (OSError, subprocess.SubprocessError):
         pass
-    return "unknown"
+    if "Model name" not in out:
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    out["Model name"] = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            out["Model name"] = "unknown"
+    return out
 
 
 def cpu_baseline(wl: Workload, seconds: float):
@@ -521,7 +655,8 @@ def cpu_baseline(wl: Workload, seconds: float):
         "unit": "GB/s",
         "cores": threads,
         "value_1_thread": round(wl.weight_bytes_step * reps1 / dt1 / 1e9, 3),
-        "cpu_model": _cpu_model(),
+        "cpu_model": _cpu_model().get("Model name", "unknown"),
+        "cpu_lscpu": _cpu_model(),
         "kind": "oracle",
         "sample": f"the whole step ({wl.wl['name']}: q8_1 quantisation of every input plus every "
                   f"matmul, f64 dequantise-then-dot) repeated {reps}x in {dt:.1f} s on {threads} "
@@ -547,17 +682,24 @@ FETCH_SCALE_NOTE = ("FETCH_SIZE and WRITE_SIZE are scaled by bytes / counter rea
 
 
 def source_hash(kernel: str) -> str:
-    """Hash of the kernel source's code: comments and whitespace are removed
-    first, so editing a comment does not retire a counter measurement."""
+    """Hash of what a counter measurement depends on: the code of the
+    kernel's source and of the shared device header (comments and
+    whitespace removed, so editing a comment retires nothing) and the
+    compiler flags of the build."""
     import hashlib
-    import re
 
-    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), encoding="utf-8") as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    code = " ".join(text.split())
-    return hashlib.sha256(code.encode()).hexdigest()[:16]
+    from q6_q8_matmul_amd.build import HIPCC_FLAGS
+
+    parts = []
+    for rel in (KERNEL_SOURCES[kernel], "q6_q8_matmul_amd/csrc/kq_device.h"):
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        parts.append(" ".join(text.split()))
+    flags = " ".join(f for f in HIPCC_FLAGS if not f.startswith("/") and f != "-I")
+    parts.append(flags)
+    return hashlib.sha256("\n".join(parts).encode()).hexdigest()[:16]
 
 
 def _step_labels(cfg: int):
@@ -706,13 +848,17 @@ def summarize(cfg: int, trace_csv=None, fetch_csv=None, write_csv=None):
     if "FETCH_SIZE" in scale and "WRITE_SIZE" in scale:
         hbm = {lab: per["FETCH_SIZE"][lab] * scale["FETCH_SIZE"] + per["WRITE_SIZE"][lab] * scale["WRITE_SIZE"]
                for lab in op_bytes if lab in per["FETCH_SIZE"]}
-        out.append("HBM bytes per launch (scaled FETCH + WRITE) against algorithmic bytes:")
+        raw = {lab: per["FETCH_SIZE"][lab] + per["WRITE_SIZE"][lab] for lab in hbm}
+        out.append("HBM bytes per launch: raw FETCH + WRITE (KiB x 1024), scaled, algorithmic:")
+        out.append(f"  {'launch':22s} {'raw':>16s} {'scaled':>16s} {'algorithmic':>16s}  scaled/alg")
         for lab, v in hbm.items():
-            out.append(f"  {lab:22s} {v:16,.0f}  {op_bytes[lab]:16,}  ratio {v / op_bytes[lab]:.4f}")
+            out.append(f"  {lab:22s} {raw[lab]:16,.0f} {v:16,.0f} {op_bytes[lab]:16,}  {v / op_bytes[lab]:.4f}")
         kern = kinds[labels.index(next(iter(hbm)))]
         traffic = {"kernel": "kq_" + kern, "workload": _workload_name(cfg),
                    "source_sha256_16": source_hash(kern),
                    "fetch_scale": round(scale["FETCH_SIZE"], 5), "write_scale": round(scale["WRITE_SIZE"], 5),
+                   "fetch_bytes_raw": {k: round(per["FETCH_SIZE"][k]) for k in hbm},
+                   "write_bytes_raw": {k: round(per["WRITE_SIZE"][k]) for k in hbm},
                    "hbm_bytes": {k: round(v) for k, v in hbm.items()},
                    "algorithmic_bytes": op_bytes,
                    "hbm_bytes_per_launch": round(sum(hbm.values()) / len(hbm)),
@@ -738,6 +884,7 @@ def summarize_counters(cfg: int, counters_csv: str):
     rows = list(csv.DictReader(open(counters_csv)))
     labels, kinds, steps = _steps_in(rows, cfg)
     ops = {op["label"]: op for op in WORKLOADS[cfg].get("bench_ops", WORKLOADS[cfg]["ops"])}
+    record = {}
     out = [f"counters: {len(steps)} steps matched in {counters_csv}",
            f"normalisation: kernel cycles = GRBM_GUI_ACTIVE / {MI355X_XCDS} XCDs; "
            f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ({SIMDS_PER_CU} SIMDs x {MI355X_CUS} CUs x kernel cycles); "
@@ -760,10 +907,17 @@ def summarize_counters(cfg: int, counters_csv: str):
         cyc = med.get("GRBM_GUI_ACTIVE", 0) / MI355X_XCDS
         if cyc > 0:
             simd_cycles = SIMDS_PER_CU * MI355X_CUS * cyc
+            rec = record.setdefault(kinds[t], {"kernel": "kq_" + kinds[t], "workload": _workload_name(cfg),
+                                               "source_sha256_16": source_hash(kinds[t]), "launches": {}})
+            lrec = rec["launches"].setdefault(lab, {})
             if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
-                out.append(f"  MFMA busy {100 * med['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:6.1f} %")
+                busy = med['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles
+                lrec["mfma_busy"] = round(busy, 4)
+                out.append(f"  MFMA busy {100 * busy:6.1f} %")
             if "SQ_ACTIVE_INST_VALU" in med:
-                out.append(f"  VALU busy {100 * 4 * med['SQ_ACTIVE_INST_VALU'] / simd_cycles:6.1f} %")
+                vbusy = 4 * med['SQ_ACTIVE_INST_VALU'] / simd_cycles
+                lrec["valu_busy"] = round(vbusy, 4)
+                out.append(f"  VALU busy {100 * vbusy:6.1f} %")
         if med.get("SQ_INSTS_VALU_MFMA_MOPS_I8"):   # one count = 512 int8 ops
             mops = 512 * med["SQ_INSTS_VALU_MFMA_MOPS_I8"]
             out.append(f"  int8 MFMA ops 512 x SQ_INSTS_VALU_MFMA_MOPS_I8 = {mops:.4e} = {mops / work:.3f} x 2MNK")
@@ -784,6 +938,10 @@ def summarize_counters(cfg: int, counters_csv: str):
             durs.sort()
             out.append(f"  clock {clk[len(clk) // 2]:9.3f} GHz  (GRBM_GUI_ACTIVE / {MI355X_XCDS} over the median "
                        f"dispatch time {durs[len(durs) // 2]:.1f} us of this counter run)")
+            if kinds[t] in record:
+                record[kinds[t]]["launches"].setdefault(lab, {})["clock_GHz"] = round(clk[len(clk) // 2], 3)
+    for rec in record.values():
+        out.append("counters_json: " + json.dumps(rec))
     return "\n".join(out)
 
 
@@ -803,6 +961,49 @@ def read_traffic(kernel: str, workload: str):
         if line.startswith("traffic_json: "):
             d = json.loads(line[len("traffic_json: "):])
             if d.get("source_sha256_16") == source_hash(kernel):
+                return d
+    return None
+
+
+def mmq_roofline(entry):
+    """Roofline object of the prefill half of the metric: the Q4_K MMQ
+    launches of the prefill workload, 2*M*N*K int8 ops per launch over the
+    launch's mean duration, against the dense int8 MFMA peak; matrix-core
+    and VALU busy fractions from the committed counter summary when it was
+    taken on the current source."""
+    if not entry:
+        return None
+    ks = [e for e in entry["kernels"] if e["kernel"] == "kq_mmq_q4k"]
+    if not ks:
+        return None
+    ops = [2.0 * e["shape"][0] * e["shape"][1] * e["shape"][2] for e in ks]
+    secs = [e["avg_us"] * 1e-6 for e in ks]
+    achieved = sum(ops) / sum(secs) / 1e12
+    out = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+           "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None, "kernel": "kq_mmq_q4k",
+           "workload": entry["workload"], "ops_per_launch": round(sum(ops) / len(ops)),
+           "avg_launch_us": round(sum(secs) * 1e6 / len(secs), 2),
+           "per_launch": {e["op"]: {"tops": e["tops"], "frac": e["frac_int8_peak"],
+                                    "median_us": e.get("median_us"), "min_us": e.get("min_us")} for e in ks}}
+    rec = read_counters("mmq_q4k", entry["workload"])
+    if rec:
+        for lab, v in rec["launches"].items():
+            if lab in out["per_launch"]:
+                out["per_launch"][lab].update({k: v[k] for k in ("mfma_busy", "valu_busy", "clock_GHz") if k in v})
+        out["counters"] = f"profiles/mmq_q4k_{entry['workload']}_counters.txt"
+    return out
+
+
+def read_counters(kernel: str, workload: str):
+    """MFMA/VALU busy fractions per launch of `kernel` from the committed
+    counter summary, if the kernel source is unchanged since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("counters_json: "):
+            d = json.loads(line[len("counters_json: "):])
+            if d.get("kernel") == "kq_" + kernel and d.get("source_sha256_16") == source_hash(kernel):
                 return d
     return None
 
@@ -868,15 +1069,16 @@ def main(argv=None):
             torch.cuda.empty_cache()
             continue
         prefill = cfg in (4, 9)
-        steps = args.steps if not prefill else max(3, args.steps // 20)
-        warm = args.warmup if not prefill else max(1, args.warmup // 10)
+        steps = args.steps if not prefill else max(20, args.steps // 10)
+        warm = args.warmup if not prefill else max(5, args.warmup // 4)
         log(f"workload {cfg}: {steps} steps, {warm} warm-up, graphs={use_graph}")
-        wl, ms, durs = measure(cfg, steps, warm, use_graph)
+        wl, ms, durs, clocks = measure(cfg, steps, warm, use_graph)
         per_op = []
         for i, op in enumerate(wl.ops):
-            label, kind, avg_ms = [d for d in durs if d[0] == op["label"]][0]
+            label, kind, avg_ms, med_ms, min_ms = [d for d in durs if d[0] == op["label"]][0]
             e = {"op": op["label"], "kernel": "kq_" + op["op"], "shape": [op["m"], op["k"], op.get("batch", op.get("n"))],
-                 "avg_us": round(avg_ms * 1e3, 2)}
+                 "avg_us": round(avg_ms * 1e3, 2), "median_us": round(med_ms * 1e3, 2),
+                 "min_us": round(min_ms * 1e3, 2)}
             if op["op"].startswith("mmq"):
                 tops = wl.op_ops(i) / (avg_ms * 1e-3) / 1e12
                 e["tops"] = round(tops, 2)
@@ -886,11 +1088,20 @@ def main(argv=None):
                 e["weight_GBps"] = round(gbps, 1)
                 e["frac_hbm"] = round(gbps / HBM_PEAK_GBPS, 4)
             per_op.append(e)
-        quant = [{"op": d[0], "avg_us": round(d[2] * 1e3, 2)} for d in durs if d[1] == "quantize"]
+        if any(op["op"].startswith("gemv") for op in wl.ops):
+            floors = read_floors_us(wl)
+            for e in per_op:
+                if e["op"] in floors:
+                    e["read_floor_us"], e["read_floor_form"] = floors[e["op"]]
+                    e["frac_of_read_floor"] = round(e["read_floor_us"] / e["avg_us"], 4)
+        quant = [{"op": d[0], "avg_us": round(d[2] * 1e3, 2), "median_us": round(d[3] * 1e3, 2),
+                  "min_us": round(d[4] * 1e3, 2)} for d in durs if d[1] == "quantize"]
         step_rate = wl.weight_bytes_step / (ms * 1e-3) / 1e9
         entry = {"workload": wl.wl["name"], "ms_per_step": round(ms, 5),
                  "weight_bytes_per_step": wl.weight_bytes_step, "weight_copies": wl.ncopies,
-                 "step_weight_GBps": round(step_rate, 1), "kernels": per_op, "quantize": quant}
+                 "step_weight_GBps": round(step_rate, 1), "kernels": per_op, "quantize": quant,
+                 "timing": "kernel figures: mean, median and min over 5 interleaved rounds of graph replays",
+                 "clock_power": clocks}
         if prefill:
             tot_ops = sum(wl.op_ops(i) for i in range(len(wl.ops)))
             entry["step_int8_TOPS"] = round(tot_ops / (ms * 1e-3) / 1e12, 2)
@@ -930,11 +1141,6 @@ def main(argv=None):
             ceiling = stream_read_ceiling()
             ceiling["gemv_frac_of_ceiling"] = round(achieved / ceiling["GBps"], 4)
             result["stream_read_ceiling"] = ceiling
-            floors = read_floors_us(wl)
-            for e in per_op:
-                if e["op"] in floors:
-                    e["read_floor_us"] = floors[e["op"]]
-                    e["frac_of_read_floor"] = round(floors[e["op"]] / e["avg_us"], 4)
             if not args.no_cpu:
                 log(f"cpu baseline (~{args.cpu_seconds} s)")
                 cb, parity = cpu_baseline(wl, args.cpu_seconds)
@@ -948,6 +1154,8 @@ def main(argv=None):
             result["kernels"] = per_op
             result["quantize"] = quant
             result["weight_copies"] = wl.ncopies
+            result["timing"] = entry["timing"]
+            result["clock_power"] = clocks
         else:
             secondary[f"cfg{cfg}"] = entry
         del wl
@@ -956,9 +1164,12 @@ def main(argv=None):
             log(f"workload {cfg}: raw vs split Q6_K layout")
             secondary[f"cfg{cfg}_split_layout"] = measure_split(cfg)
             torch.cuda.empty_cache()
+    mmq = mmq_roofline(secondary.get("cfg4"))
     if result is None:
-        result = {"metric": METRIC, "secondary": secondary}
-    elif secondary:
+        result = {"metric": METRIC}
+    if mmq:
+        result["roofline_mmq"] = mmq
+    if secondary:
         result["secondary"] = secondary
     print(json.dumps(result), flush=True)
     return 1 if failed else 0

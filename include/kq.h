@@ -276,19 +276,26 @@ int kq_swiglu_q8_1(const float* gate, const float* up, float* y, void* xq, int64
  * Measurement helper, not part of the k-quant path: the decode GEMVs stream
  * their weights once (minfer "The CUDA backend" 2.2), and the benchmark
  * reports their rate beside what a plain read of the same bytes reaches on
- * the same device.  kq_read_probe reads nbytes at p once with 16-byte loads
- * (one workgroup per 32 KiB) and stores, per 8 KiB wavefront share, the xor
- * of its 32-bit words into out: out[4 * c + w] = xor over u = 0..7, l =
- * 0..63 of the 16-byte word 2048 c + 256 u + 64 w + l (words past the end
- * read as zero).
+ * the same device.  kq_read_probe reads nbytes at p once with 16-byte loads.
+ * The bytes are cut into chunks of 256*loads 16-byte words; a grid of G
+ * 256-thread workgroups takes them round robin (workgroup b reads chunks
+ * b, b + G, ...), thread t loading the words 256 u + t of a chunk, u <
+ * loads, all issued before any is used.  G = grid, at most the chunk count;
+ * grid = 0 gives one workgroup per chunk.  Per wavefront w of workgroup b:
+ *   out[4 b + w] = xor, over the workgroup's chunks c, u < loads, l < 64,
+ *                  of the 32-bit words of 16-byte word
+ *                  256*loads*c + 256 u + 64 w + l (words past the end read
+ *                  as zero).
  *   p      device, 16-byte aligned, nbytes > 0 a multiple of 16, < 2^40.
- *   out    device uint32 [kq_read_probe_words(nbytes)], 4-byte aligned,
- *          not overlapping p.
- * kq_read_probe_words: that count, 4 * ceil(nbytes / 32768); -1 for an
- * invalid nbytes.  Errors as the other calls (KQ_ERR_ARG, nothing launched).
+ *   grid   0 <= grid < 2^31;  loads: 4, 8, 16 or 32.
+ *   out    device uint32 [kq_read_probe_words(nbytes, grid, loads)], 4-byte
+ *          aligned, not overlapping p.
+ * kq_read_probe_words: that count, 4 * G; -1 for invalid arguments.  Errors
+ * as the other calls (KQ_ERR_ARG, nothing launched).
  */
-int64_t kq_read_probe_words(int64_t nbytes);
-int kq_read_probe(const void* p, int64_t nbytes, uint32_t* out, void* stream);
+int64_t kq_read_probe_words(int64_t nbytes, int64_t grid, int32_t loads);
+int kq_read_probe(const void* p, int64_t nbytes, uint32_t* out, int64_t grid, int32_t loads,
+                  void* stream);
 
 /* Text of the last error on this host thread ("" if none). */
 const char* kq_last_error(void);

@@ -58,8 +58,8 @@ def lib() -> ctypes.CDLL:
         L.kq_rmsnorm_q8_1.argtypes = [p, p, p, ctypes.c_float, p, p, i64, i64, p]
         L.kq_swiglu_q8_1.argtypes = [p, p, p, p, i64, i64, p]
         L.kq_gemv_q4k_seg.argtypes = [i32, p, p, p, p, p, i64, i32, p]
-        L.kq_read_probe.argtypes = [p, i64, p, p]
-        L.kq_read_probe_words.argtypes = [i64]
+        L.kq_read_probe.argtypes = [p, i64, p, i64, i32, p]
+        L.kq_read_probe_words.argtypes = [i64, i64, i32]
         L.kq_read_probe_words.restype = i64
         for fn in (L.kq_quantize_q8_1, L.kq_gemv_q4k, L.kq_gemv_q6k, L.kq_mmq_q4k,
                    L.kq_mmq_q6k, L.kq_mmq_q6k_split, L.kq_gemv_q6k_split, L.kq_repack_q6k,
@@ -146,12 +146,12 @@ def kq_q6k_split_bytes(m: int, k: int) -> int:
     return int(lib().kq_q6k_split_bytes(m, k))
 
 
-def kq_read_probe_words(nbytes: int) -> int:
-    return int(lib().kq_read_probe_words(nbytes))
+def kq_read_probe_words(nbytes: int, grid: int = 0, loads: int = 8) -> int:
+    return int(lib().kq_read_probe_words(nbytes, grid, loads))
 
 
-def kq_read_probe(p, nbytes: int, out, stream=None) -> None:
-    _check(lib().kq_read_probe(_ptr(p), nbytes, _ptr(out), _stream(stream)))
+def kq_read_probe(p, nbytes: int, out, grid: int = 0, loads: int = 8, stream=None) -> None:
+    _check(lib().kq_read_probe(_ptr(p), nbytes, _ptr(out), grid, loads, _stream(stream)))
 
 
 def kq_gemv_q4k_seg(w, m, y, residual, xq, k: int, batch: int, stream=None) -> None:

@@ -260,25 +260,35 @@ int kq_mmq_q6k_split(const void* wr, const void* xq, float* y, int64_t m, int64_
     return launched(fn, kq::launch_mmq_q6k_split(wr, xq, y, m, n, k, cus, (hipStream_t)stream));
 }
 
-int64_t kq_read_probe_words(int64_t nbytes) {
-    if (nbytes <= 0 || nbytes % 16 != 0 || nbytes >= (1LL << 40)) return -1;
-    return kq::read_probe_words(nbytes);
+static bool probe_shape_ok(int64_t nbytes, int64_t grid, int32_t loads) {
+    return nbytes > 0 && nbytes % 16 == 0 && nbytes < (1LL << 40) && grid >= 0 &&
+           grid <= 0x7fffffffLL && (loads == 4 || loads == 8 || loads == 16 || loads == 32) &&
+           kq::read_probe_words(nbytes, grid, loads) / 4 <= 0x7fffffffLL;
 }
 
-int kq_read_probe(const void* p, int64_t nbytes, uint32_t* out, void* stream) {
+int64_t kq_read_probe_words(int64_t nbytes, int64_t grid, int32_t loads) {
+    if (!probe_shape_ok(nbytes, grid, loads)) return -1;
+    return kq::read_probe_words(nbytes, grid, loads);
+}
+
+int kq_read_probe(const void* p, int64_t nbytes, uint32_t* out, int64_t grid, int32_t loads,
+                  void* stream) {
     const char* fn = "kq_read_probe";
     if (!p || !out) return fail(KQ_ERR_ARG, "%s: null pointer (p=%p out=%p)", fn, p, (void*)out);
     if (nbytes <= 0 || nbytes % 16 != 0 || nbytes >= (1LL << 40))
         return fail(KQ_ERR_ARG, "%s: nbytes=%lld must be a positive multiple of 16 below 2^40", fn,
                     (long long)nbytes);
+    if (!probe_shape_ok(nbytes, grid, loads))
+        return fail(KQ_ERR_ARG, "%s: grid=%lld loads=%d (grid in [0, 2^31), loads 4, 8, 16 or 32)",
+                    fn, (long long)grid, (int)loads);
     if (!aligned(p, 16) || !aligned(out, 4))
         return fail(KQ_ERR_ARG, "%s: misaligned pointer (p=%p needs 16, out=%p needs 4)", fn, p,
                     (void*)out);
-    const int64_t words = kq::read_probe_words(nbytes);
+    const int64_t words = kq::read_probe_words(nbytes, grid, loads);
     if (overlap(out, words * 4, p, nbytes))
         return fail(KQ_ERR_ARG, "%s: out=%p overlaps p=%p", fn, (void*)out, p);
     if (int rc = check_device(fn, nullptr)) return rc;
-    return launched(fn, kq::launch_read_probe(p, nbytes, out, (hipStream_t)stream));
+    return launched(fn, kq::launch_read_probe(p, nbytes, out, grid, loads, (hipStream_t)stream));
 }
 
 int64_t kq_q6k_split_bytes(int64_t m, int64_t k) {
@@ -377,6 +387,6 @@ int kq_swiglu_q8_1(const float* gate, const float* up, float* y, void* xq, int64
 
 const char* kq_last_error(void) { return g_err; }
 
-int kq_abi_version(void) { return 1; }
+int kq_abi_version(void) { return 2; }
 
 }  // extern "C"

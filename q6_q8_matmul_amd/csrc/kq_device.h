@@ -141,8 +141,9 @@ hipError_t launch_gemv_q4k_seg(int nseg, const void* const* w, const int64_t* m,
 hipError_t launch_gemv_q6k(const void* w, const void* xq, float* y, const float* residual,
                            int64_t m, int64_t k, int batch, int lds_limit, int cus,
                            hipStream_t stream);
-int64_t read_probe_words(int64_t nbytes);
-hipError_t launch_read_probe(const void* p, int64_t nbytes, uint32_t* out, hipStream_t stream);
+int64_t read_probe_words(int64_t nbytes, int64_t grid, int loads);
+hipError_t launch_read_probe(const void* p, int64_t nbytes, uint32_t* out, int64_t grid, int loads,
+                             hipStream_t stream);
 hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                           int64_t k, int cus, hipStream_t stream);
 hipError_t launch_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n,

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(kq):
 
 
 def test_abi_version(kq):
-    assert kq.kq_abi_version() == 1
+    assert kq.kq_abi_version() == 2
 
 
 # Fake, aligned, never-dereferenced addresses: every call below fails argument
@@ -285,24 +285,30 @@ def test_gemv_seg_empty_and_null_arrays(kq):
     assert rc == kq.KQ_ERR_ARG and "null array" in kq.kq_last_error()
 
 
-@pytest.mark.parametrize("nbytes,words", [(16, 4), (32768, 4), (32784, 8), (2 << 30, 4 * 65536)])
-def test_read_probe_words(kq, nbytes, words):
-    assert kq.kq_read_probe_words(nbytes) == words
+@pytest.mark.parametrize("nbytes,grid,loads,words", [
+    (16, 0, 8, 4), (32768, 0, 8, 4), (32784, 0, 8, 8), (2 << 30, 0, 8, 4 * 65536),
+    (2 << 30, 512, 16, 4 * 512), (2 << 30, 0, 32, 4 * 16384), (32784, 100, 4, 4 * 3),
+    (16, 7, 32, 4)])
+def test_read_probe_words(kq, nbytes, grid, loads, words):
+    assert kq.kq_read_probe_words(nbytes, grid, loads) == words
 
 
-@pytest.mark.parametrize("nbytes", [0, -16, 8, 1 << 40])
-def test_read_probe_words_rejects(kq, nbytes):
-    assert kq.kq_read_probe_words(nbytes) == -1
+@pytest.mark.parametrize("nbytes,grid,loads", [(0, 0, 8), (-16, 0, 8), (8, 0, 8), (1 << 40, 0, 8),
+                                               (4096, -1, 8), (4096, 0, 12), (4096, 1 << 31, 8)])
+def test_read_probe_words_rejects(kq, nbytes, grid, loads):
+    assert kq.kq_read_probe_words(nbytes, grid, loads) == -1
 
 
 @pytest.mark.parametrize("args,needle", [
-    ((None, 4096, Y, None), "null pointer"),
-    ((W, 4096, None, None), "null pointer"),
-    ((W, 0, Y, None), "nbytes=0"),
-    ((W, 4100, Y, None), "nbytes=4100"),
-    ((W + 8, 4096, Y, None), "misaligned"),
-    ((W, 4096, Y + 2, None), "misaligned"),
-    ((W, 4096, W + 64, None), "overlaps"),
+    ((None, 4096, Y, 0, 8, None), "null pointer"),
+    ((W, 4096, None, 0, 8, None), "null pointer"),
+    ((W, 0, Y, 0, 8, None), "nbytes=0"),
+    ((W, 4100, Y, 0, 8, None), "nbytes=4100"),
+    ((W, 4096, Y, 0, 7, None), "loads=7"),
+    ((W, 4096, Y, -2, 8, None), "grid=-2"),
+    ((W + 8, 4096, Y, 0, 8, None), "misaligned"),
+    ((W, 4096, Y + 2, 0, 8, None), "misaligned"),
+    ((W, 4096, W + 64, 0, 8, None), "overlaps"),
 ])
 def test_read_probe_rejects(kq, args, needle):
     rc = kq.lib().kq_read_probe(*args)

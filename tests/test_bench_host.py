@@ -9,18 +9,33 @@
   small synthetic collection whose answers are known by construction.
 """
 import csv
+import json
 
 import bench
 
 
 def test_source_hash_ignores_comments_not_code(tmp_path, monkeypatch):
+    import q6_q8_matmul_amd.build as build
+
     (tmp_path / "a.hip").write_text("int f(int x) { return x + 1; } // one\n/* a\n block */\n")
     (tmp_path / "b.hip").write_text("// header\nint f(int x)  {\n  return x + 1;   // uno\n}\n")
     (tmp_path / "c.hip").write_text("int f(int x) { return x + 2; } // one\n")
+    hdr = tmp_path / "q6_q8_matmul_amd" / "csrc" / "kq_device.h"
+    hdr.parent.mkdir(parents=True)
+    hdr.write_text("inline int g() { return 3; }  // shared\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "KERNEL_SOURCES", {"a": "a.hip", "b": "b.hip", "c": "c.hip"})
-    assert bench.source_hash("a") == bench.source_hash("b")
-    assert bench.source_hash("a") != bench.source_hash("c")
+    ha = bench.source_hash("a")
+    assert ha == bench.source_hash("b")
+    assert ha != bench.source_hash("c")
+    # the shared device header and the compiler flags are part of the key
+    hdr.write_text("/* shared */ inline int g() {\n return 3; }\n")
+    assert bench.source_hash("a") == ha
+    hdr.write_text("inline int g() { return 4; }\n")
+    assert bench.source_hash("a") != ha
+    hdr.write_text("inline int g() { return 3; }\n")
+    monkeypatch.setattr(build, "HIPCC_FLAGS", build.HIPCC_FLAGS + ["-O2"])
+    assert bench.source_hash("a") != ha
 
 
 def _collection(path, steps, ghz, mfma_busy, valu_busy, mops_factor):
@@ -79,6 +94,9 @@ def test_counter_summary_fractions_work_and_clock(tmp_path):
         assert "= 2.000 x 2MNK" in block, block
         assert "clock     2.000 GHz" in block, block
         assert "dispatch time 100.0 us" in block, block
+    rec = [json.loads(l.split(": ", 1)[1]) for l in lines if l.startswith("counters_json: ")]
+    assert len(rec) == 1 and rec[0]["kernel"] == "kq_mmq_q6k"
+    assert rec[0]["launches"]["down"] == {"mfma_busy": 0.25, "valu_busy": 0.5, "clock_GHz": 2.0}
 
 
 def _decode_run(path, counter, steps, per_label, copy_factor):
@@ -124,7 +142,10 @@ def test_traffic_summary_scales_by_the_copies(tmp_path):
     text, traffic = bench.summarize(1, fetch_csv=str(tmp_path / "f.csv"), write_csv=str(tmp_path / "w.csv"))
     assert "4 steps matched" in text and "from 15 weight copies" in text
     assert traffic["fetch_scale"] == 2.0 and traffic["write_scale"] == 1.0
-    assert text.count("ratio 1.0100") == 3, text
+    assert sum(l.rstrip().endswith(" 1.0100") for l in text.split("\n")) == 3, text
+    for lab in ("attn_out", "gate|up", "down"):
+        assert traffic["fetch_bytes_raw"][lab] == round(fetch[lab])
+        assert traffic["hbm_bytes"][lab] == round(2.0 * fetch[lab])
     assert abs(traffic["hbm_bytes_per_launch"] / traffic["algorithmic_bytes_per_launch"] - 1.01) < 1e-6
     assert traffic["source_sha256_16"] == bench.source_hash("gemv_q4k")
 
@@ -138,3 +159,29 @@ def test_trace_summary_medians(tmp_path):
     assert "5 steps matched" in text
     assert any(l.startswith("gate|up") and "10.00" in l for l in text.split("\n")), text
     assert any(l.startswith("quantize x_down") and "2.00" in l for l in text.split("\n")), text
+
+
+def test_clock_power_reads_the_marked_level(tmp_path):
+    sclk = tmp_path / "pp_dpm_sclk"
+    sclk.write_text("S: 100Mhz\n0: 500Mhz\n1: 2400Mhz *\n")
+    pw = tmp_path / "power1_input"
+    pw.write_text("1234500000\n")
+    cp = bench.ClockPower()
+    cp.sclk, cp.power = str(sclk), str(pw)
+    assert cp._read() == (2400, 1234.5)
+    cp.samples = [(100, 240.0), (2400, 1200.0), (2100, 1300.0), (2300, 1250.0)]
+    s = cp.summary()
+    assert s["busy_samples"] == 3 and s["sclk_MHz_median"] == 2300 and s["sclk_MHz_min"] == 2100
+    assert s["power_W_median"] == 1250.0 and s["power_W_max"] == 1300.0
+
+
+def test_mmq_roofline_sums_ops_over_time():
+    ks = [{"op": "gate", "kernel": "kq_mmq_q4k", "shape": [1000, 2000, 500], "avg_us": 1.0,
+           "tops": 2000.0, "frac_int8_peak": 0.4},
+          {"op": "v", "kernel": "kq_mmq_q6k", "shape": [5, 5, 5], "avg_us": 9.0},
+          {"op": "down", "kernel": "kq_mmq_q4k", "shape": [1000, 2000, 500], "avg_us": 3.0,
+           "tops": 666.7, "frac_int8_peak": 0.1333}]
+    r = bench.mmq_roofline({"workload": "none_such", "kernels": ks})
+    # 2 launches of 2*1000*2000*500 = 2e9 ops in 4 us: 1000 TOPS
+    assert r["achieved"] == 1000.0 and r["frac"] == 0.2 and r["bound"] == "mfma"
+    assert set(r["per_launch"]) == {"gate", "down"} and "counters" not in r
