@@ -102,6 +102,11 @@ class Workload:
                 self.xq[xn] = torch.empty((rows, k // 32 * 36), dtype=torch.uint8, device="cuda")
         self.res = {}
         self.y = []
+        self.ws = {}
+        for i, op in enumerate(self.ops):
+            if op["op"] == "mmq_q6k":
+                nb = kq.kq_mmq_q6k_workspace_bytes(op["m"], op["n"], op["k"])
+                self.ws[i] = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
         for op in self.ops:
             rows = op.get("batch", op.get("n"))
             self.y.append(torch.empty((rows, op["m"]), dtype=torch.float32, device="cuda"))
@@ -131,11 +136,15 @@ class Workload:
                 out.append((op["label"], op["op"],
                             lambda fn=fn, w=w, xq=xq, y=y, res=res, op=op:
                             fn(w, xq, y, res, op["m"], op["k"], op["batch"])))
-            else:
-                fn = kq.kq_mmq_q4k if op["op"] == "mmq_q4k" else kq.kq_mmq_q6k
+            elif op["op"] == "mmq_q6k":          # the K split when the product is small
+                ws = self.ws[i]
                 out.append((op["label"], op["op"],
-                            lambda fn=fn, w=w, xq=xq, y=y, op=op:
-                            fn(w, xq, y, op["m"], op["n"], op["k"])))
+                            lambda w=w, xq=xq, y=y, op=op, ws=ws:
+                            kq.kq_mmq_q6k_ws(w, xq, y, op["m"], op["n"], op["k"], ws, ws.numel())))
+            else:
+                out.append((op["label"], op["op"],
+                            lambda w=w, xq=xq, y=y, op=op:
+                            kq.kq_mmq_q4k(w, xq, y, op["m"], op["n"], op["k"])))
         return out
 
     def step(self, c: int):
@@ -475,6 +484,43 @@ class ClockPower:
                 out.update({"power_W_median": round(ws[len(ws) // 2], 1),
                             "power_W_max": round(ws[-1], 1)})
         return out
+
+
+def measure_ksplit(cfg: int):
+    """The Q6_K prefill products of workload cfg without a workspace
+    (kq_mmq_q6k) and with the workspace the K split asks for
+    (kq_mmq_q6k_ws), each replayed as a HIP graph over rotating weight
+    copies."""
+    import torch
+
+    import q6_q8_matmul_amd as kq
+    from kq_inputs import WORKLOADS, tensor
+
+    wl = WORKLOADS[cfg]
+    out = []
+    for op in wl["ops"]:
+        if op["op"] != "mmq_q6k":
+            continue
+        m, n, k = op["m"], op["n"], op["k"]
+        h = tensor(cfg, op["w"])
+        ncopy = copies_for(h.nbytes)
+        ws_ = [torch.from_numpy(h).cuda()]
+        ws_ += [ws_[0].clone() for _ in range(ncopy - 1)]
+        xq = kq.quantize_q8_1(torch.from_numpy(tensor(cfg, op["x"])).cuda())
+        y = torch.empty((n, m), dtype=torch.float32, device="cuda")
+        nb = kq.kq_mmq_q6k_workspace_bytes(m, n, k)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+        e = {"op": op["label"], "shape": [m, k, n], "workspace_bytes": nb}
+        for name, launch in (("no_workspace", lambda w: kq.kq_mmq_q6k(w, xq, y, m, n, k)),
+                             ("k_split", lambda w: kq.kq_mmq_q6k_ws(w, xq, y, m, n, k, ws, nb))):
+            it = iter(range(1 << 30))
+            us = _graph_time_ms(lambda: launch(ws_[next(it) % ncopy]), per_graph=ncopy) * 1e3
+            e[f"{name}_us"] = round(us, 2)
+            e[f"{name}_tops"] = round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)
+        out.append(e)
+        del ws_, ws
+        torch.cuda.empty_cache()
+    return {"workload": wl["name"], "products": out}
 
 
 def measure(cfg: int, steps: int, warmup: int, use_graph: bool):
@@ -1163,6 +1209,10 @@ def main(argv=None):
         if cfg in (3, 9):
             log(f"workload {cfg}: raw vs split Q6_K layout")
             secondary[f"cfg{cfg}_split_layout"] = measure_split(cfg)
+            torch.cuda.empty_cache()
+        if cfg == 9:
+            log(f"workload {cfg}: Q6_K products with and without the K split")
+            secondary[f"cfg{cfg}_k_split"] = measure_ksplit(cfg)
             torch.cuda.empty_cache()
     mmq = mmq_roofline(secondary.get("cfg4"))
     if result is None:

@@ -17,6 +17,8 @@
  *     tokens on the int8 matrix cores (minfer "The CUDA backend" 2.3, MMQ,
  *     and 3.2.6; cajeta "One model, start to last token" 3: Q4_K and Q6_K
  *     tiles).
+ *   - kq_mmq_q6k_ws: the Q6_K prefill product split along k for products
+ *     too small to fill the device, with a caller-provided workspace.
  *   - kq_rmsnorm_q8_1 / kq_swiglu_q8_1: producers that write the q8_1 blocks
  *     of their output themselves, so the GEMV that follows needs no separate
  *     quantisation launch (leone-cuda "CUDA kernel design": RMSNorm and
@@ -188,6 +190,34 @@ int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, in
  */
 int kq_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
                void* stream);
+
+/*
+ * kq_mmq_q6k with a caller-provided workspace, for products too small to
+ * fill the device (cajeta "One model, start to last token" 3.1: a split
+ * along the reduction dimension adds workgroups when the output tiles alone
+ * leave compute units idle, and a fixup pass combines the pieces).
+ *   kq_mmq_q6k_workspace_bytes(m, n, k): bytes of workspace the split form
+ *     of this product needs on the current device -- 0 when the product is
+ *     not split, -1 for invalid sizes or device (kq_last_error says which).
+ *     The split is taken when the product's 128-token tiles number fewer
+ *     than two per compute unit: the k/256 superblocks are cut into P <= 4
+ *     ranges, range z of every output tile runs as its own workgroup, and
+ *     the workspace holds ranges 1..P-1 as f32 [P-1][n][m]; a second launch
+ *     then adds them to y (which holds range 0) in the order z = 1, 2, ...
+ *   kq_mmq_q6k_ws: the same product.  ws is a device buffer of ws_bytes
+ *     bytes, 16-byte aligned, not overlapping w, xq or y, owned by the
+ *     caller and used only by work enqueued by this call (do not share it
+ *     between calls that may run at the same time).  When ws_bytes is below
+ *     what the split needs (ws may then be NULL) the call runs exactly as
+ *     kq_mmq_q6k.  Results are deterministic for a given device, size and
+ *     workspace size; the split sums in another order than kq_mmq_q6k, so
+ *     the two agree within the oracle's bound, not bit for bit.
+ *   Other arguments and errors as kq_mmq_q6k; ws_bytes < 0, or ws_bytes > 0
+ *   with ws NULL, is KQ_ERR_ARG.
+ */
+int64_t kq_mmq_q6k_workspace_bytes(int64_t m, int64_t n, int64_t k);
+int kq_mmq_q6k_ws(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
+                  void* ws, int64_t ws_bytes, void* stream);
 
 /*
  * The split Q6_K layout, made once at load by kq_repack_q6k (cajeta "One

@@ -146,6 +146,16 @@ hipError_t launch_read_probe(const void* p, int64_t nbytes, uint32_t* out, int64
                              hipStream_t stream);
 hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                           int64_t k, int cus, hipStream_t stream);
+// Launch plan of a prefill product: NT 32-token tiles per workgroup, the K
+// range cut into `parts` pieces of sb_per superblocks (parts > 1 needs a
+// workspace of ws_bytes = (parts - 1) * m * n * 4 bytes).
+struct MmqPlan {
+    int nt, parts, sb_per;
+    int64_t ws_bytes;
+};
+MmqPlan plan_mmq_q6k(int64_t m, int64_t n, int64_t k, int cus, int64_t max_ws);
+hipError_t launch_mmq_q6k_plan(const void* w, const void* xq, float* y, int64_t m, int64_t n,
+                               int64_t k, const MmqPlan& plan, void* ws, hipStream_t stream);
 hipError_t launch_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                           int64_t k, int cus, hipStream_t stream);
 hipError_t launch_mmq_q6k_split(const void* wr, const void* xq, float* y, int64_t m, int64_t n,

@@ -37,6 +37,8 @@
 // stored.  No atomics; results are bitwise reproducible.
 #include "kq_device.h"
 
+#include <algorithm>
+
 namespace kq {
 namespace {
 
@@ -77,10 +79,15 @@ __device__ __forceinline__ void split4(uint32_t q, u16x2 nsc, u16x2 c32, uint32_
 
 // SPLIT: the weights are in the split layout (208-byte bodies at w, 16-byte
 // aligned, and the f16 d of superblock row * S + s at wd[row * S + s]).
+// K split: workgroup z of the grid's third dimension takes superblocks
+// [z * sb_per, min(S, (z + 1) * sb_per)); z = 0 writes its sums to y, z > 0
+// to part + (z - 1) * M * N (the same [token][row] layout), and a second
+// launch adds the parts to y in the order z = 1, 2, ...
 template <int NT, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ wd,
-                    const uint8_t* __restrict__ xq, float* __restrict__ y, int M, int N, int S) {
+                    const uint8_t* __restrict__ xq, float* y, float* part, int M, int N, int S,
+                    int sb_per) {
     constexpr int BN = Smem<NT>::BN;
     __shared__ __align__(16) Smem<NT> sm;
 
@@ -93,6 +100,8 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ 
     const int64_t row_bytes = (int64_t)S * kQ6KBytes;
     const int nb_row = S * 8;
     const int r = wave * 32 + l32;   // this lane's weight row within the tile
+    const int sb_beg = (int)blockIdx.z * sb_per, sb_end = min(S, sb_beg + sb_per);
+    float* out = blockIdx.z == 0 ? y : part + (int64_t)(blockIdx.z - 1) * M * N;
 
     float acc[NT][16];
 #pragma unroll
@@ -100,7 +109,7 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ 
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
 
-    for (int sb = 0; sb < S; ++sb) {
+    for (int sb = sb_beg; sb < sb_end; ++sb) {
         // ---- staging, every global load issued before the first LDS write.
         // Weights: two threads per row; thread (row, e) takes the 16-byte
         // chunks e, e+2, ... of the superblock's bytes 0..207 (13 chunks),
@@ -247,7 +256,37 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ 
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int m = m0 + wave * 32 + 8 * (i >> 2) + 4 * h2 + (i & 3);
-            if (m < M) y[(int64_t)n * M + m] = acc[nt][i];
+            if (m < M) out[(int64_t)n * M + m] = acc[nt][i];
+        }
+    }
+}
+
+// y[i] += part[0][i] + part[1][i] + ... in that order (count values; the
+// float4 form when y is 16-byte aligned and count a multiple of 4).
+__global__ __launch_bounds__(256) void splitk_sum_kernel(float* __restrict__ y,
+                                                         const float* __restrict__ part,
+                                                         int64_t count, int nparts) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    if (((uintptr_t)y & 15) == 0 && (count & 3) == 0) {
+        float4* y4 = (float4*)y;
+        const float4* p4 = (const float4*)part;
+        const int64_t c4 = count >> 2;
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < c4; i += stride) {
+            float4 v = y4[i];
+            for (int z = 0; z < nparts; ++z) {
+                const float4 q = p4[(int64_t)z * c4 + i];
+                v.x += q.x;
+                v.y += q.y;
+                v.z += q.z;
+                v.w += q.w;
+            }
+            y4[i] = v;
+        }
+    } else {
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += stride) {
+            float v = y[i];
+            for (int z = 0; z < nparts; ++z) v += part[(int64_t)z * count + i];
+            y[i] = v;
         }
     }
 }
@@ -264,25 +303,63 @@ static int mmq_q6k_nt(int64_t m, int64_t n, int cus) {
     return 1;
 }
 
+// K-split plan (measured on MI355X, Qwen2-7B prefill shapes at 2048 tokens
+// and smaller token counts): when the 128-token grid has fewer than two
+// workgroups per CU the K range is cut into 4 parts (at most S/2), with the
+// widest token tile whose split grid still gives every CU two workgroups
+// (else 32 tokens).  512 x 3584 x 2048: 56 -> 43 us; 3584 x 18944 x 2048:
+// 757 -> 708 us (448 tiles are 1.75 rounds of two per CU, 1792 are 3.5).
+// A split that needs more than max_ws bytes of workspace is not taken.
+MmqPlan plan_mmq_q6k(int64_t m, int64_t n, int64_t k, int cus, int64_t max_ws) {
+    const int S = (int)(k / kQK);
+    const int64_t mt = (m + BM - 1) / BM;
+    auto tiles = [&](int nt) { return mt * ((n + 32 * nt - 1) / (32 * nt)); };
+    const MmqPlan whole{mmq_q6k_nt(m, n, cus), 1, S, 0};
+    if (tiles(4) >= 2 * (int64_t)cus || S < 4) return whole;
+    const int want = std::min(4, S / 2);
+    const int sb_per = (S + want - 1) / want;
+    const int parts = (S + sb_per - 1) / sb_per;
+    int nt = 1;
+    for (int c = 4; c > 1; c >>= 1)
+        if (tiles(c) * parts >= 2 * (int64_t)cus) {
+            nt = c;
+            break;
+        }
+    const MmqPlan split{nt, parts, sb_per, (int64_t)(parts - 1) * m * n * 4};
+    return split.ws_bytes <= max_ws ? split : whole;
+}
+
 template <bool SPLIT>
 static hipError_t launch_mmq_q6k_any(const uint8_t* w, const uint16_t* wd, const void* xq, float* y,
-                                     int64_t m, int64_t n, int S, int cus, hipStream_t stream) {
-    const int nt = mmq_q6k_nt(m, n, cus);
-    dim3 grid((unsigned)((m + BM - 1) / BM), (unsigned)((n + 32 * nt - 1) / (32 * nt)));
+                                     int64_t m, int64_t n, int S, const MmqPlan& p, float* part,
+                                     hipStream_t stream) {
+    const int nt = p.nt;
+    dim3 grid((unsigned)((m + BM - 1) / BM), (unsigned)((n + 32 * nt - 1) / (32 * nt)), (unsigned)p.parts);
     auto launch = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, w, wd, (const uint8_t*)xq, y, (int)m,
-                           (int)n, S);
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, w, wd, (const uint8_t*)xq, y, part,
+                           (int)m, (int)n, S, p.sb_per);
     };
     if (nt == 4) launch(mmq_q6k_kernel<4, SPLIT>);
     else if (nt == 2) launch(mmq_q6k_kernel<2, SPLIT>);
     else launch(mmq_q6k_kernel<1, SPLIT>);
+    if (p.parts > 1) {
+        const int64_t count = m * n;
+        const int64_t blocks = std::min<int64_t>((count / 4 + 255) / 256, 4096);
+        hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y,
+                           (const float*)part, count, p.parts - 1);
+    }
     return hipGetLastError();
+}
+
+hipError_t launch_mmq_q6k_plan(const void* w, const void* xq, float* y, int64_t m, int64_t n,
+                               int64_t k, const MmqPlan& plan, void* ws, hipStream_t stream) {
+    return launch_mmq_q6k_any<false>((const uint8_t*)w, nullptr, xq, y, m, n, (int)(k / kQK), plan,
+                                     (float*)ws, stream);
 }
 
 hipError_t launch_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                           int64_t k, int cus, hipStream_t stream) {
-    return launch_mmq_q6k_any<false>((const uint8_t*)w, nullptr, xq, y, m, n, (int)(k / kQK), cus,
-                                     stream);
+    return launch_mmq_q6k_plan(w, xq, y, m, n, k, plan_mmq_q6k(m, n, k, cus, 0), nullptr, stream);
 }
 
 hipError_t launch_mmq_q6k_split(const void* wr, const void* xq, float* y, int64_t m, int64_t n,
@@ -290,7 +367,8 @@ hipError_t launch_mmq_q6k_split(const void* wr, const void* xq, float* y, int64_
     const int S = (int)(k / kQK);
     const int64_t G = m * S;
     const uint8_t* bodies = (const uint8_t*)wr + (2 * G + 15) / 16 * 16;
-    return launch_mmq_q6k_any<true>(bodies, (const uint16_t*)wr, xq, y, m, n, S, cus, stream);
+    return launch_mmq_q6k_any<true>(bodies, (const uint16_t*)wr, xq, y, m, n, S,
+                                    plan_mmq_q6k(m, n, k, cus, 0), nullptr, stream);
 }
 
 }  // namespace kq

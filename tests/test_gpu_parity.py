@@ -460,6 +460,65 @@ def test_mmq_deterministic(kq, kind):
         assert np.array_equal(a, host(mmq(kq, kind)(wd, xd, m, n, k)))
 
 
+# ------------------------------------------------------------- K split -----
+
+# Products too small to fill the device take the K split when given the
+# workspace: the value projection 512 x 3584 at 2048 and 512 tokens, twice the
+# rows, ragged tiles, the least k that splits (four superblocks), and the
+# prefill down projection (448 tiles of 128 tokens, split in four).
+KSPLIT = [(512, 2048, 3584), (512, 512, 3584), (1024, 2048, 3584), (300, 100, 2048), (129, 70, 1024),
+          (33, 5, 1280), (3584, 2048, 18944)]
+
+
+@pytest.mark.parametrize("m,n,k", KSPLIT, ids=[f"m{c[0]}-n{c[1]}-k{c[2]}" for c in KSPLIT])
+def test_mmq_q6k_ksplit(kq, m, n, k):
+    say(f"mmq q6k K split m={m} n={n} k={k}")
+    nb = kq.kq_mmq_q6k_workspace_bytes(m, n, k)
+    assert nb > 0 and nb % (m * n * 4) == 0 and nb // (m * n * 4) <= 3
+    w, x, _ = random_case(m * 7 + n + k, "q6k", m, k, n)
+    xq = oracle.quantize_q8_1(x)
+    wd, xd = dev(w), dev(xq)
+    ws = torch.full((nb,), 0x7F, dtype=torch.uint8, device="cuda")      # stale contents
+    y = host(kq.mmq_q6k_ws(wd, xd, m, n, k, ws=ws))
+    assert np.array_equal(y, host(kq.mmq_q6k_ws(wd, xd, m, n, k, ws=ws))), "not reproducible"
+    if m * n * k <= 1 << 34:
+        y_ref, den = oracle.matmul("q6k", w, xq, m, n, k)
+        check_close(y, y_ref, den, f"mmq q6k split m{m} n{n} k{k}")
+    else:
+        tok, row = _sample_pairs(m, n, np.random.default_rng(m))
+        y_ref, den = oracle.matmul_pairs("q6k", w, xq, m, n, k, tok, row)
+        check_close(y[tok, row], y_ref, den, f"mmq q6k split m{m} n{n} k{k} ({tok.size} outputs)")
+    # a workspace one byte short: the unsplit product, bit for bit
+    short = kq.mmq_q6k_ws(wd, xd, m, n, k, ws=ws[: nb - 1])
+    assert torch.equal(short, kq.mmq_q6k(wd, xd, m, n, k))
+
+
+def test_mmq_q6k_ksplit_not_taken_when_tiles_fill(kq):
+    """A product whose 128-token tiles already give every CU two workgroups
+    needs no workspace and gives the kq_mmq_q6k bits."""
+    m, n, k = 4096, 1024, 512
+    say(f"mmq q6k no split m={m} n={n} k={k}")
+    assert kq.kq_mmq_q6k_workspace_bytes(m, n, k) == 0
+    w, x, _ = random_case(31, "q6k", m, k, n)
+    wd, xd = dev(w), dev(oracle.quantize_q8_1(x))
+    assert torch.equal(kq.mmq_q6k_ws(wd, xd, m, n, k), kq.mmq_q6k(wd, xd, m, n, k))
+
+
+def test_mmq_q6k_ws_rejects_bad_workspace(kq):
+    m, n, k = 512, 256, 3584
+    say("mmq q6k workspace errors")
+    nb = kq.kq_mmq_q6k_workspace_bytes(m, n, k)
+    w, x, _ = random_case(32, "q6k", m, k, n)
+    wd, xd = dev(w), dev(oracle.quantize_q8_1(x))
+    y = torch.full((n, m), 7.0, device="cuda")
+    ws = torch.empty(nb + 64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(kq.KQError, match="misaligned workspace"):
+        kq.kq_mmq_q6k_ws(wd, xd, y, m, n, k, ws.data_ptr() + 4, nb, None)
+    with pytest.raises(kq.KQError, match="overlaps"):
+        kq.kq_mmq_q6k_ws(wd, xd, y, m, n, k, y, nb, None)
+    assert torch.all(y == 7.0).item()
+
+
 # ------------------------------------------------------ error handling ------
 
 def test_bad_arguments_launch_nothing(kq):
