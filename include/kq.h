@@ -220,6 +220,26 @@ int kq_mmq_q6k_ws(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                   void* ws, int64_t ws_bytes, void* stream);
 
 /*
+ * kq_mmq_q6k_ws without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the split's ranges go to a
+ * static device array of KQ_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on every GPU it runs on until the process ends.  The call
+ * allocates nothing.
+ *   Same arguments, plan and bits as kq_mmq_q6k_ws given a workspace of
+ *   kq_mmq_q6k_workspace_bytes(m, n, k) bytes.  A product whose split needs
+ *   more than KQ_NOALLOC_SCRATCH_BYTES is rejected with KQ_ERR_ARG (the text
+ *   names the size; use kq_mmq_q6k_ws or kq_mmq_q6k for it).
+ *   Every call on a GPU uses that GPU's one array: calls that may run at the
+ *   same time on one GPU (other streams, other host threads) race and give
+ *   wrong results; serialise them.  Each call writes every scratch byte it
+ *   reads before reading it, so nothing needs clearing between calls.
+ */
+#define KQ_NOALLOC_SCRATCH_BYTES (32LL << 20)
+int kq_mmq_q6k_noalloc(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
+                       void* stream);
+
+/*
  * The split Q6_K layout, made once at load by kq_repack_q6k (cajeta "One
  * model, start to last token" 2, residency: a Q6_K weight is split into a
  * scale prefix and 208-byte bodies so the kernels read it with aligned

@@ -52,6 +52,7 @@ def lib() -> ctypes.CDLL:
         L.kq_mmq_q6k.argtypes = [p, p, p, i64, i64, i64, p]
         L.kq_mmq_q6k_split.argtypes = [p, p, p, i64, i64, i64, p]
         L.kq_mmq_q6k_ws.argtypes = [p, p, p, i64, i64, i64, p, i64, p]
+        L.kq_mmq_q6k_noalloc.argtypes = [p, p, p, i64, i64, i64, p]
         L.kq_mmq_q6k_workspace_bytes.argtypes = [i64, i64, i64]
         L.kq_mmq_q6k_workspace_bytes.restype = i64
         L.kq_gemv_q6k_split.argtypes = [p, p, p, p, i64, i64, i32, p]
@@ -65,7 +66,7 @@ def lib() -> ctypes.CDLL:
         L.kq_read_probe_words.argtypes = [i64, i64, i32]
         L.kq_read_probe_words.restype = i64
         for fn in (L.kq_quantize_q8_1, L.kq_gemv_q4k, L.kq_gemv_q6k, L.kq_mmq_q4k,
-                   L.kq_mmq_q6k, L.kq_mmq_q6k_split, L.kq_mmq_q6k_ws, L.kq_gemv_q6k_split, L.kq_repack_q6k,
+                   L.kq_mmq_q6k, L.kq_mmq_q6k_split, L.kq_mmq_q6k_ws, L.kq_mmq_q6k_noalloc, L.kq_gemv_q6k_split, L.kq_repack_q6k,
                    L.kq_rmsnorm_q8_1, L.kq_swiglu_q8_1, L.kq_gemv_q4k_seg, L.kq_read_probe):
             fn.restype = ctypes.c_int
         L.kq_last_error.argtypes = []
@@ -142,6 +143,10 @@ def kq_mmq_q6k_workspace_bytes(m: int, n: int, k: int) -> int:
 def kq_mmq_q6k_ws(w, xq, y, m: int, n: int, k: int, ws, ws_bytes: int, stream=None) -> None:
     _check(lib().kq_mmq_q6k_ws(_ptr(w), _ptr(xq), _ptr(y), m, n, k, _ptr(ws), ws_bytes,
                                _stream(stream)))
+
+
+def kq_mmq_q6k_noalloc(w, xq, y, m: int, n: int, k: int, stream=None) -> None:
+    _check(lib().kq_mmq_q6k_noalloc(_ptr(w), _ptr(xq), _ptr(y), m, n, k, _stream(stream)))
 
 
 def kq_mmq_q6k_split(wr, xq, y, m: int, n: int, k: int, stream=None) -> None:

@@ -284,6 +284,37 @@ int kq_mmq_q6k_ws(const void* w, const void* xq, float* y, int64_t m, int64_t n,
     return launched(fn, kq::launch_mmq_q6k_plan(w, xq, y, m, n, k, plan, ws, (hipStream_t)stream));
 }
 
+static_assert(KQ_NOALLOC_SCRATCH_BYTES == kq::kNoallocScratchBytes, "scratch size mismatch");
+
+int kq_mmq_q6k_noalloc(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
+                       void* stream) {
+    const char* fn = "kq_mmq_q6k_noalloc";
+    if (int rc = mmq_common(fn, 210, w, xq, y, m, n, k)) return rc;
+    if (m == 0 || n == 0) return ok();
+    int cus = 0;
+    if (int rc = check_device(fn, nullptr, &cus)) return rc;
+    const kq::MmqPlan plan = kq::plan_mmq_q6k(m, n, k, cus, INT64_MAX);
+    if (plan.ws_bytes > KQ_NOALLOC_SCRATCH_BYTES)
+        return fail(KQ_ERR_ARG,
+                    "%s: m=%lld n=%lld k=%lld needs %lld bytes of scratch, more than the %lld of the "
+                    "static scratch (use kq_mmq_q6k_ws or kq_mmq_q6k)",
+                    fn, (long long)m, (long long)n, (long long)k, (long long)plan.ws_bytes,
+                    (long long)KQ_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (plan.ws_bytes > 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess)
+            return fail(KQ_ERR_HIP, "%s: hipGetDevice failed", fn);
+        const hipError_t e = kq::noalloc_scratch(dev, &ws);
+        if (e != hipSuccess)
+            return fail(KQ_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                        hipGetErrorString(e));
+        if (overlap(ws, plan.ws_bytes, y, m * n * 4))
+            return fail(KQ_ERR_ARG, "%s: y=%p overlaps the static scratch", fn, (void*)y);
+    }
+    return launched(fn, kq::launch_mmq_q6k_plan(w, xq, y, m, n, k, plan, ws, (hipStream_t)stream));
+}
+
 int kq_mmq_q6k_split(const void* wr, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
                      void* stream) {
     const char* fn = "kq_mmq_q6k_split";

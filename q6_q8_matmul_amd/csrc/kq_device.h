@@ -154,6 +154,10 @@ struct MmqPlan {
     int64_t ws_bytes;
 };
 MmqPlan plan_mmq_q6k(int64_t m, int64_t n, int64_t k, int cus, int64_t max_ws);
+// Static scratch of the allocation-free Q6_K product (bytes), and its
+// address on `device` (which must be the current device).
+constexpr int64_t kNoallocScratchBytes = 32LL << 20;
+hipError_t noalloc_scratch(int device, void** ptr);
 hipError_t launch_mmq_q6k_plan(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                                int64_t k, const MmqPlan& plan, void* ws, hipStream_t stream);
 hipError_t launch_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n,

@@ -38,6 +38,7 @@
 #include "kq_device.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace kq {
 namespace {
@@ -355,6 +356,28 @@ hipError_t launch_mmq_q6k_plan(const void* w, const void* xq, float* y, int64_t 
                                int64_t k, const MmqPlan& plan, void* ws, hipStream_t stream) {
     return launch_mmq_q6k_any<false>((const uint8_t*)w, nullptr, xq, y, m, n, (int)(k / kQK), plan,
                                      (float*)ws, stream);
+}
+
+// Workspace of the allocation-free entry point: a static device array, one
+// copy per GPU the library runs on, held until the process ends.  Host code
+// never uses the array's name as an address: hipGetSymbolAddress gives each
+// device's copy, once per device, and that address is kept.
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+namespace {
+std::atomic<void*> g_scratch_ptr[64];
+}
+
+hipError_t noalloc_scratch(int device, void** ptr) {
+    if (device < 0 || device >= 64) return hipErrorInvalidDevice;
+    void* p = g_scratch_ptr[device].load(std::memory_order_acquire);
+    if (!p) {
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[device].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 hipError_t launch_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n,

@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
         "kq_q6k_split_bytes", "kq_repack_q6k", "kq_gemv_q6k_split", "kq_mmq_q6k_split",
         "kq_rmsnorm_q8_1", "kq_swiglu_q8_1", "kq_gemv_q4k_seg", "kq_last_error",
         "kq_abi_version", "kq_read_probe", "kq_read_probe_words", "kq_mmq_q6k_ws",
-        "kq_mmq_q6k_workspace_bytes"])
+        "kq_mmq_q6k_workspace_bytes", "kq_mmq_q6k_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(kq):
@@ -103,7 +103,7 @@ def test_gemv_rejects(kq, fn, args, needle):
     assert fn in kq.kq_last_error()
 
 
-@pytest.mark.parametrize("fn", ["kq_mmq_q4k", "kq_mmq_q6k", "kq_mmq_q6k_split"])
+@pytest.mark.parametrize("fn", ["kq_mmq_q4k", "kq_mmq_q6k", "kq_mmq_q6k_split", "kq_mmq_q6k_noalloc"])
 @pytest.mark.parametrize("args,needle", [
     ((None, X, Y, 8, 8, 256, None), "null pointer"),
     ((W, X, Y, 8, 8, 100, None), "k=100"),
