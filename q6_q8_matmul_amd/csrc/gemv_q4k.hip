@@ -331,18 +331,23 @@ template <int BATCH, int RPW>
 __device__ __forceinline__ void finish_rows(float (&acc)[RPW][BATCH], float* y,
                                             const float* residual, int pair0, int half, int lane,
                                             int m) {
+    // the columns of a row in one transposing butterfly over its half
+    // wavefront: lane 32b/NB of the half holds column b
+    constexpr int NB = pow2_ceil(BATCH);
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int r = 2 * (pair0 + i) + half;
+        float v[NB];
 #pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
-            const float v = half_wave_sum(acc[i][b]);
-            if ((lane & 31) == 0 && r < m) {
-                const int64_t o = (int64_t)b * m + r;
-                y[o] = residual ? residual[o] + v : v;
-            }
-            acc[i][b] = 0.0f;
+        for (int b = 0; b < NB; ++b) v[b] = b < BATCH ? acc[i][b] : 0.0f;
+        const float t = lane_sums<NB, 32>(v, lane);
+        const int l = lane & 31, b = l / (32 / NB);
+        if (l % (32 / NB) == 0 && b < BATCH && r < m) {
+            const int64_t o = (int64_t)b * m + r;
+            y[o] = residual ? residual[o] + t : t;
         }
+#pragma unroll
+        for (int bb = 0; bb < BATCH; ++bb) acc[i][bb] = 0.0f;
     }
 }
 

@@ -306,23 +306,27 @@ __device__ __forceinline__ void compute_pass(const R (&r)[RPW], float (&acc)[RPW
     }
 }
 
-// Sum of each (row, column) accumulator over the wavefront, residual add and
-// store (lane 0).
+// Sum of each (row, column) accumulator over the wavefront (the columns of
+// a row in one transposing butterfly: lane 64b/NB holds column b), residual
+// add and store.
 template <int BATCH, int RPW>
 __device__ __forceinline__ void finish_rows(float (&acc)[RPW][BATCH], float* y,
                                             const float* residual, int row0, int m, int lane) {
+    constexpr int NB = pow2_ceil(BATCH);
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int r = row0 + i;
+        float v[NB];
 #pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
-            const float t = wave_sum(acc[i][b]);
-            if (lane == 0 && r < m) {
-                const int64_t o = (int64_t)b * m + r;
-                y[o] = residual ? residual[o] + t : t;
-            }
-            acc[i][b] = 0.0f;
+        for (int b = 0; b < NB; ++b) v[b] = b < BATCH ? acc[i][b] : 0.0f;
+        const float t = lane_sums<NB, 64>(v, lane);
+        const int b = lane / (64 / NB);
+        if (lane % (64 / NB) == 0 && b < BATCH && r < m) {
+            const int64_t o = (int64_t)b * m + r;
+            y[o] = residual ? residual[o] + t : t;
         }
+#pragma unroll
+        for (int bb = 0; bb < BATCH; ++bb) acc[i][bb] = 0.0f;
     }
 }
 
@@ -477,10 +481,26 @@ template <bool SPLIT>
 hipError_t dispatch(const void* w, const uint16_t* wd, const void* xq, float* y,
                     const float* residual, int64_t m, int64_t k, int batch, int cus,
                     hipStream_t stream) {
-    // Launch shape for the 128256 x 4096 output head: one row per
-    // wavefront (a lane's share of a row holds 64 values, so two rows per
-    // wavefront would take 100-170 VGPRs), four wavefronts per workgroup, one
-    // pass ahead, persistent grid of up to six workgroups per compute unit.
+    // Launch shapes measured on the 128256 x 4096 output head (two weight
+    // copies rotating, 431 MB each): four wavefronts per workgroup and a
+    // persistent grid.  Raw layout: one row per wavefront, one pass ahead,
+    // four workgroups per CU at batch 1 (79 us; six: 81), six at batch 2..8
+    // (batch 4: 97 us).  Split layout: two rows per wavefront at batch 1
+    // (75 us), one row two passes ahead at batches 2..4 (batch 4: 88 us,
+    // one pass ahead: 93).  A row's share per lane is 64 values, so two rows
+    // per wavefront take 140-160 VGPRs on the raw layout, where they were
+    // slower.
+    if constexpr (SPLIT) {
+        switch (batch) {
+            case 1: return launch_variant<1, 2, 1, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 4, stream, wd);
+            case 2: return launch_variant<2, 1, 2, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 4, stream, wd);
+            case 3: return launch_variant<3, 1, 2, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 4, stream, wd);
+            case 4: return launch_variant<4, 1, 2, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 4, stream, wd);
+            default: break;
+        }
+    } else if (batch == 1) {
+        return launch_variant<1, 1, 1, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 4, stream, wd);
+    }
     switch (batch) {
         case 1: return launch_variant<1, 1, 1, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 6, stream, wd);
         case 2: return launch_variant<2, 1, 1, 4, SPLIT>(w, xq, y, residual, m, k, 65536, cus, 6, stream, wd);

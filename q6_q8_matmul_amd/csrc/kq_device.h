@@ -59,6 +59,40 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// N lane sums at once (a transposing butterfly).  The values v[0..N) of the
+// SPAN lanes of a span (SPAN = 32 or 64; N a power of two <= SPAN) are added
+// over the span with the same pairs in the same order as N separate xor
+// butterflies from lane bit log2(SPAN) - 1 down, so each sum is bitwise the
+// one such a butterfly gives; but at each of the first log2 N steps a lane
+// keeps only the half of its values that its lane bit selects and sends the
+// other half to its partner, so the N sums take N - 1 + log2(SPAN / N)
+// exchanges instead of N log2 SPAN.  Returns, in lane L, the sum of value
+// (L mod SPAN) / (SPAN / N).  The halves are chosen with a bit mask: a
+// conditional choice between array elements becomes an indexed access that
+// the compiler expands over the whole array.
+template <int N, int SPAN>
+__device__ __forceinline__ float lane_sums(float (&v)[N], int lane) {
+    static_assert((N & (N - 1)) == 0 && N <= SPAN && (SPAN == 32 || SPAN == 64), "shape");
+    int m = SPAN / 2;
+#pragma unroll
+    for (int c = N; c > 1; c >>= 1, m >>= 1) {
+        const uint32_t up = (lane & m) ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int i = 0; i < c / 2; ++i) {
+            const uint32_t lo = __float_as_uint(v[i]), hi = __float_as_uint(v[i + c / 2]);
+            const float keep = __uint_as_float((hi & up) | (lo & ~up));
+            const float send = __uint_as_float((lo & up) | (hi & ~up));
+            v[i] = keep + __shfl_xor(send, m, 64);
+        }
+    }
+    float s = v[0];
+#pragma unroll
+    for (; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+    return s;
+}
+
+constexpr int pow2_ceil(int n) { return n <= 1 ? 1 : 2 * pow2_ceil((n + 1) / 2); }
+
 // q8_1 quantisation of one 32-value block by eight consecutive lanes
 // (j = lane & 7 of an aligned group of 8, all active); lane j owns values
 // 4j .. 4j+3 in v and writes code dword j; lane 0 also writes the header
