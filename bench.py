@@ -774,7 +774,9 @@ def _steps_in(rows, cfg):
     labels, kinds = _step_labels(cfg)
     by_disp = {}
     for r in rows:
-        if "kq::" in r["Kernel_Name"]:
+        # the K-split sum that follows a split Q6_K product is reported by
+        # --stats, not matched as a launch of the step
+        if "kq::" in r["Kernel_Name"] and "splitk_sum" not in r["Kernel_Name"]:
             by_disp.setdefault(r.get("Dispatch_Id") or r.get("Correlation_Id"), []).append(r)
     disp = sorted(by_disp.values(), key=lambda v: int(v[0]["Start_Timestamp"]))
     steps, j, n = [], 0, len(kinds)
@@ -936,7 +938,7 @@ def summarize_counters(cfg: int, counters_csv: str):
            f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ({SIMDS_PER_CU} SIMDs x {MI355X_CUS} CUs x kernel cycles); "
            f"VALU busy = SQ_ACTIVE_INST_VALU (4-cycle issue slots) x 4 / the same"]
     for t, lab in enumerate(labels):
-        if not kinds[t].startswith("mmq"):
+        if kinds[t] == "quantize":
             continue
         med = {}
         for name in MMQ_COUNTERS:
@@ -945,8 +947,9 @@ def summarize_counters(cfg: int, counters_csv: str):
             if v:
                 med[name] = v[len(v) // 2]
         op = ops[lab]
-        work = 2.0 * op["m"] * op["n"] * op["k"]
-        out.append(f"{lab} ({kinds[t]}, {op['m']}x{op['k']} x {op['n']} tokens, 2MNK = {work:.4e}):")
+        rows = op.get("n", op.get("batch"))
+        work = 2.0 * op["m"] * rows * op["k"]
+        out.append(f"{lab} ({kinds[t]}, {op['m']}x{op['k']} x {rows} columns, 2MNK = {work:.4e}):")
         for name in MMQ_COUNTERS:
             if name in med:
                 out.append(f"  {name:28s} median {med[name]:16,.0f}")
@@ -964,6 +967,14 @@ def summarize_counters(cfg: int, counters_csv: str):
                 vbusy = 4 * med['SQ_ACTIVE_INST_VALU'] / simd_cycles
                 lrec["valu_busy"] = round(vbusy, 4)
                 out.append(f"  VALU busy {100 * vbusy:6.1f} %")
+        if kinds[t].startswith("gemv") and med.get("SQ_INSTS_VALU"):
+            # one Q4_K wavefront pass covers 16 superblock-rows, a Q6_K one 16
+            sbrows = op["m"] * (op["k"] // 256)
+            per = med["SQ_INSTS_VALU"] / (sbrows / 16)
+            out.append(f"  VALU instructions per wavefront pass (16 superblock-rows) {per:8.1f}")
+            rec = record.setdefault(kinds[t], {"kernel": "kq_" + kinds[t], "workload": _workload_name(cfg),
+                                               "source_sha256_16": source_hash(kinds[t]), "launches": {}})
+            rec["launches"].setdefault(lab, {})["valu_per_pass"] = round(per, 1)
         if med.get("SQ_INSTS_VALU_MFMA_MOPS_I8"):   # one count = 512 int8 ops
             mops = 512 * med["SQ_INSTS_VALU_MFMA_MOPS_I8"]
             out.append(f"  int8 MFMA ops 512 x SQ_INSTS_VALU_MFMA_MOPS_I8 = {mops:.4e} = {mops / work:.3f} x 2MNK")
@@ -1063,6 +1074,8 @@ def main(argv=None):
     ap.add_argument("--no-secondary", action="store_true", help="skip workloads 2-4")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the read-ceiling sweep (profiling runs of one workload)")
     ap.add_argument("--only", type=int, default=None, help="measure only this workload")
     ap.add_argument("--summarize", action="store_true",
                     help="summarise rocprofv3 CSV output of a run of this script (no GPU)")
@@ -1107,7 +1120,7 @@ def main(argv=None):
     # also takes the engine clock off its idle level before any workload is
     # timed (measured: the first workload of a fresh process otherwise runs
     # at a median 1.6 GHz against 2.3 GHz for the later ones).
-    ceiling = stream_read_ceiling() if 1 in cfgs else None
+    ceiling = stream_read_ceiling() if 1 in cfgs and not args.no_ceiling else None
     for cfg in cfgs:
         if cfg in (5, 6):
             log(f"workload {cfg}: fused producers")
@@ -1189,8 +1202,9 @@ def main(argv=None):
                            "hip_graphs": use_graph},
                 "roofline": roofline,
             }
-            ceiling["gemv_frac_of_ceiling"] = round(achieved / ceiling["GBps"], 4)
-            result["stream_read_ceiling"] = ceiling
+            if ceiling:
+                ceiling["gemv_frac_of_ceiling"] = round(achieved / ceiling["GBps"], 4)
+                result["stream_read_ceiling"] = ceiling
             if not args.no_cpu:
                 log(f"cpu baseline (~{args.cpu_seconds} s)")
                 cb, parity = cpu_baseline(wl, args.cpu_seconds)
