@@ -104,8 +104,9 @@ class Workload:
         self.y = []
         self.ws = {}
         for i, op in enumerate(self.ops):
-            if op["op"] == "mmq_q6k":
-                nb = kq.kq_mmq_q6k_workspace_bytes(op["m"], op["n"], op["k"])
+            if op["op"] in ("mmq_q4k", "mmq_q6k"):
+                fn = kq.kq_mmq_q4k_workspace_bytes if op["op"] == "mmq_q4k" else kq.kq_mmq_q6k_workspace_bytes
+                nb = fn(op["m"], op["n"], op["k"])
                 self.ws[i] = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
         for op in self.ops:
             rows = op.get("batch", op.get("n"))
@@ -141,10 +142,11 @@ class Workload:
                 out.append((op["label"], op["op"],
                             lambda w=w, xq=xq, y=y, op=op, ws=ws:
                             kq.kq_mmq_q6k_ws(w, xq, y, op["m"], op["n"], op["k"], ws, ws.numel())))
-            else:
+            else:                                 # Q4_K: the K split where tiles leave CUs idle
+                ws = self.ws[i]
                 out.append((op["label"], op["op"],
-                            lambda w=w, xq=xq, y=y, op=op:
-                            kq.kq_mmq_q4k(w, xq, y, op["m"], op["n"], op["k"])))
+                            lambda w=w, xq=xq, y=y, op=op, ws=ws:
+                            kq.kq_mmq_q4k_ws(w, xq, y, op["m"], op["n"], op["k"], ws, ws.numel())))
         return out
 
     def step(self, c: int):
@@ -487,10 +489,10 @@ class ClockPower:
 
 
 def measure_ksplit(cfg: int):
-    """The Q6_K prefill products of workload cfg without a workspace
-    (kq_mmq_q6k) and with the workspace the K split asks for
-    (kq_mmq_q6k_ws), each replayed as a HIP graph over rotating weight
-    copies."""
+    """The prefill products of workload cfg that the K split applies to,
+    without a workspace (kq_mmq_q4k / kq_mmq_q6k) and with the workspace the
+    split asks for (kq_mmq_q4k_ws / kq_mmq_q6k_ws), each replayed as a HIP
+    graph over rotating weight copies."""
     import torch
 
     import q6_q8_matmul_amd as kq
@@ -499,20 +501,26 @@ def measure_ksplit(cfg: int):
     wl = WORKLOADS[cfg]
     out = []
     for op in wl["ops"]:
-        if op["op"] != "mmq_q6k":
+        if not op["op"].startswith("mmq"):
             continue
+        q4 = op["op"] == "mmq_q4k"
+        plain = kq.kq_mmq_q4k if q4 else kq.kq_mmq_q6k
+        split = kq.kq_mmq_q4k_ws if q4 else kq.kq_mmq_q6k_ws
+        wsb = kq.kq_mmq_q4k_workspace_bytes if q4 else kq.kq_mmq_q6k_workspace_bytes
         m, n, k = op["m"], op["n"], op["k"]
+        nb = wsb(m, n, k)
+        if nb == 0:                       # not split: nothing to compare
+            continue
         h = tensor(cfg, op["w"])
         ncopy = copies_for(h.nbytes)
         ws_ = [torch.from_numpy(h).cuda()]
         ws_ += [ws_[0].clone() for _ in range(ncopy - 1)]
         xq = kq.quantize_q8_1(torch.from_numpy(tensor(cfg, op["x"])).cuda())
         y = torch.empty((n, m), dtype=torch.float32, device="cuda")
-        nb = kq.kq_mmq_q6k_workspace_bytes(m, n, k)
         ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
-        e = {"op": op["label"], "shape": [m, k, n], "workspace_bytes": nb}
-        for name, launch in (("no_workspace", lambda w: kq.kq_mmq_q6k(w, xq, y, m, n, k)),
-                             ("k_split", lambda w: kq.kq_mmq_q6k_ws(w, xq, y, m, n, k, ws, nb))):
+        e = {"op": op["label"], "kernel": "kq_" + op["op"], "shape": [m, k, n], "workspace_bytes": nb}
+        for name, launch in (("no_workspace", lambda w: plain(w, xq, y, m, n, k)),
+                             ("k_split", lambda w: split(w, xq, y, m, n, k, ws, nb))):
             it = iter(range(1 << 30))
             us = _graph_time_ms(lambda: launch(ws_[next(it) % ncopy]), per_graph=ncopy) * 1e3
             e[f"{name}_us"] = round(us, 2)
@@ -1228,8 +1236,8 @@ def main(argv=None):
             log(f"workload {cfg}: raw vs split Q6_K layout")
             secondary[f"cfg{cfg}_split_layout"] = measure_split(cfg)
             torch.cuda.empty_cache()
-        if cfg == 9:
-            log(f"workload {cfg}: Q6_K products with and without the K split")
+        if cfg in (4, 9):
+            log(f"workload {cfg}: products with and without the K split")
             secondary[f"cfg{cfg}_k_split"] = measure_ksplit(cfg)
             torch.cuda.empty_cache()
     mmq = mmq_roofline(secondary.get("cfg4"))

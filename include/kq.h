@@ -17,8 +17,9 @@
  *     tokens on the int8 matrix cores (minfer "The CUDA backend" 2.3, MMQ,
  *     and 3.2.6; cajeta "One model, start to last token" 3: Q4_K and Q6_K
  *     tiles).
- *   - kq_mmq_q6k_ws: the Q6_K prefill product split along k for products
- *     too small to fill the device, with a caller-provided workspace.
+ *   - kq_mmq_q4k_ws / kq_mmq_q6k_ws: the prefill products split along k
+ *     where their tiles do not fill the device, with a caller-provided
+ *     workspace.
  *   - kq_rmsnorm_q8_1 / kq_swiglu_q8_1: producers that write the q8_1 blocks
  *     of their output themselves, so the GEMV that follows needs no separate
  *     quantisation launch (leone-cuda "CUDA kernel design": RMSNorm and
@@ -190,6 +191,27 @@ int kq_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n, in
  */
 int kq_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
                void* stream);
+
+/*
+ * kq_mmq_q4k with a caller-provided workspace, for products whose tiles
+ * leave the device's last round of workgroups partly idle (cajeta "One
+ * model, start to last token" 3.1: a split along the reduction dimension
+ * adds workgroups, and a fixup pass combines the pieces).
+ *   kq_mmq_q4k_workspace_bytes(m, n, k): bytes of workspace the split form
+ *     needs on the current device -- 0 when the product is not split, -1
+ *     for invalid sizes or device.  The k/256 superblocks are cut into P <= 8
+ *     ranges, chosen by an estimate of the grid's rounds of one workgroup per
+ *     compute unit against the extra partial planes; the workspace holds
+ *     ranges 1..P-1 as f32 [P-1][n][m], and a second launch adds them to y
+ *     (which holds range 0) in the order z = 1, 2, ...
+ *   kq_mmq_q4k_ws: the same product; workspace rules, results and errors
+ *     as for kq_mmq_q6k_ws below, except that a workspace smaller than the
+ *     best split needs takes the best split that fits in ws_bytes (ws NULL
+ *     or ws_bytes 0: the unsplit kq_mmq_q4k, bit for bit).
+ */
+int64_t kq_mmq_q4k_workspace_bytes(int64_t m, int64_t n, int64_t k);
+int kq_mmq_q4k_ws(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
+                  void* ws, int64_t ws_bytes, void* stream);
 
 /*
  * kq_mmq_q6k with a caller-provided workspace, for products too small to

@@ -52,6 +52,9 @@ def lib() -> ctypes.CDLL:
         L.kq_mmq_q6k.argtypes = [p, p, p, i64, i64, i64, p]
         L.kq_mmq_q6k_split.argtypes = [p, p, p, i64, i64, i64, p]
         L.kq_mmq_q6k_ws.argtypes = [p, p, p, i64, i64, i64, p, i64, p]
+        L.kq_mmq_q4k_ws.argtypes = [p, p, p, i64, i64, i64, p, i64, p]
+        L.kq_mmq_q4k_workspace_bytes.argtypes = [i64, i64, i64]
+        L.kq_mmq_q4k_workspace_bytes.restype = i64
         L.kq_mmq_q6k_noalloc.argtypes = [p, p, p, i64, i64, i64, p]
         L.kq_mmq_q6k_workspace_bytes.argtypes = [i64, i64, i64]
         L.kq_mmq_q6k_workspace_bytes.restype = i64
@@ -66,7 +69,7 @@ def lib() -> ctypes.CDLL:
         L.kq_read_probe_words.argtypes = [i64, i64, i32]
         L.kq_read_probe_words.restype = i64
         for fn in (L.kq_quantize_q8_1, L.kq_gemv_q4k, L.kq_gemv_q6k, L.kq_mmq_q4k,
-                   L.kq_mmq_q6k, L.kq_mmq_q6k_split, L.kq_mmq_q6k_ws, L.kq_mmq_q6k_noalloc, L.kq_gemv_q6k_split, L.kq_repack_q6k,
+                   L.kq_mmq_q6k, L.kq_mmq_q6k_split, L.kq_mmq_q6k_ws, L.kq_mmq_q4k_ws, L.kq_mmq_q6k_noalloc, L.kq_gemv_q6k_split, L.kq_repack_q6k,
                    L.kq_rmsnorm_q8_1, L.kq_swiglu_q8_1, L.kq_gemv_q4k_seg, L.kq_read_probe):
             fn.restype = ctypes.c_int
         L.kq_last_error.argtypes = []
@@ -131,6 +134,18 @@ def kq_mmq_q4k(w, xq, y, m: int, n: int, k: int, stream=None) -> None:
 
 def kq_mmq_q6k(w, xq, y, m: int, n: int, k: int, stream=None) -> None:
     _check(lib().kq_mmq_q6k(_ptr(w), _ptr(xq), _ptr(y), m, n, k, _stream(stream)))
+
+
+def kq_mmq_q4k_workspace_bytes(m: int, n: int, k: int) -> int:
+    v = int(lib().kq_mmq_q4k_workspace_bytes(m, n, k))
+    if v < 0:
+        raise KQError(KQ_ERR_ARG, kq_last_error())
+    return v
+
+
+def kq_mmq_q4k_ws(w, xq, y, m: int, n: int, k: int, ws, ws_bytes: int, stream=None) -> None:
+    _check(lib().kq_mmq_q4k_ws(_ptr(w), _ptr(xq), _ptr(y), m, n, k, _ptr(ws), ws_bytes,
+                               _stream(stream)))
 
 
 def kq_mmq_q6k_workspace_bytes(m: int, n: int, k: int) -> int:
@@ -272,6 +287,20 @@ def mmq_q6k_split(wr, xq, m: int, n: int, k: int, out=None, stream=None):
     _require_cuda(wr, xq)
     y = out if out is not None else torch.empty((n, m), dtype=torch.float32, device=wr.device)
     kq_mmq_q6k_split(wr, xq, y, m, n, k, stream)
+    return y
+
+
+def mmq_q4k_ws(w, xq, m: int, n: int, k: int, ws=None, out=None, stream=None):
+    """kq_mmq_q4k_ws with a workspace tensor of the size the split needs
+    (allocated here by torch when `ws` is None)."""
+    import torch
+
+    _require_cuda(w, xq)
+    y = out if out is not None else torch.empty((n, m), dtype=torch.float32, device=w.device)
+    if ws is None:
+        nb = kq_mmq_q4k_workspace_bytes(m, n, k)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=w.device)
+    kq_mmq_q4k_ws(w, xq, y, m, n, k, ws, ws.numel() * ws.element_size(), stream)
     return y
 
 

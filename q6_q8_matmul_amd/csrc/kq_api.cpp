@@ -250,6 +250,40 @@ int kq_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n, in
     return launched(fn, kq::launch_mmq_q6k(w, xq, y, m, n, k, cus, (hipStream_t)stream));
 }
 
+int64_t kq_mmq_q4k_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+    const char* fn = "kq_mmq_q4k_workspace_bytes";
+    if (k <= 0 || k % 256 != 0 || k > KQ_MAX_K || m < 0 || m > KQ_MAX_ROWS || n < 0 ||
+        n > 65535LL * 128) {
+        fail(KQ_ERR_ARG, "%s: m=%lld n=%lld k=%lld out of range", fn, (long long)m, (long long)n,
+             (long long)k);
+        return -1;
+    }
+    if (m == 0 || n == 0) return 0;
+    int cus = 0;
+    if (check_device(fn, nullptr, &cus)) return -1;
+    return kq::plan_mmq_q4k(m, n, k, cus, INT64_MAX).ws_bytes;
+}
+
+int kq_mmq_q4k_ws(const void* w, const void* xq, float* y, int64_t m, int64_t n, int64_t k,
+                  void* ws, int64_t ws_bytes, void* stream) {
+    const char* fn = "kq_mmq_q4k_ws";
+    if (int rc = mmq_common(fn, 144, w, xq, y, m, n, k)) return rc;
+    if (ws_bytes < 0 || (ws_bytes > 0 && !ws))
+        return fail(KQ_ERR_ARG, "%s: ws=%p with ws_bytes=%lld", fn, ws, (long long)ws_bytes);
+    if (m == 0 || n == 0) return ok();
+    int cus = 0;
+    if (int rc = check_device(fn, nullptr, &cus)) return rc;
+    const kq::MmqPlan plan = kq::plan_mmq_q4k(m, n, k, cus, ws ? ws_bytes : 0);
+    if (plan.parts > 1) {
+        if (!aligned(ws, 16))
+            return fail(KQ_ERR_ARG, "%s: misaligned workspace ws=%p (needs 16)", fn, ws);
+        if (overlap(ws, plan.ws_bytes, w, m * (k / 256) * 144) ||
+            overlap(ws, plan.ws_bytes, xq, n * (k / 32) * 36) || overlap(ws, plan.ws_bytes, y, m * n * 4))
+            return fail(KQ_ERR_ARG, "%s: workspace ws=%p overlaps w, xq or y", fn, ws);
+    }
+    return launched(fn, kq::launch_mmq_q4k_plan(w, xq, y, m, n, k, plan, ws, (hipStream_t)stream));
+}
+
 int64_t kq_mmq_q6k_workspace_bytes(int64_t m, int64_t n, int64_t k) {
     const char* fn = "kq_mmq_q6k_workspace_bytes";
     if (k <= 0 || k % 256 != 0 || k > KQ_MAX_K || m < 0 || m > KQ_MAX_ROWS || n < 0 ||

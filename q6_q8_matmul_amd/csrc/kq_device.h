@@ -188,6 +188,12 @@ struct MmqPlan {
     int64_t ws_bytes;
 };
 MmqPlan plan_mmq_q6k(int64_t m, int64_t n, int64_t k, int cus, int64_t max_ws);
+MmqPlan plan_mmq_q4k(int64_t m, int64_t n, int64_t k, int cus, int64_t max_ws);
+hipError_t launch_mmq_q4k_plan(const void* w, const void* xq, float* y, int64_t m, int64_t n,
+                               int64_t k, const MmqPlan& plan, void* ws, hipStream_t stream);
+// y[i] = ((y[i] + part[0][i]) + part[1][i]) + ... over nparts planes of count.
+hipError_t launch_splitk_sum(float* y, const float* part, int64_t count, int nparts,
+                             hipStream_t stream);
 // Static scratch of the allocation-free Q6_K product (bytes), and its
 // address on `device` (which must be the current device).
 constexpr int64_t kNoallocScratchBytes = 32LL << 20;

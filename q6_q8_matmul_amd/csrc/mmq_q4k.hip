@@ -187,10 +187,14 @@ __device__ __forceinline__ void block_step(v16f (&part)[2], const v16i& magic, c
     }
 }
 
+// K split: the grid holds `parts` copies of the tile grid; copy z takes
+// superblocks [z * sb_per, min(S, (z + 1) * sb_per)) and writes its sums to
+// y (z = 0) or to part + (z - 1) * M * N (the same [token][row] layout),
+// which a second launch adds to y in the order z = 1, 2, ...
 template <bool CLAMP>
 __global__ __launch_bounds__(NTHR, 1)
-void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq,
-                    float* __restrict__ y, int M, int N, int S, int mtiles, int ntiles) {
+void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, float* y,
+                    float* part, int M, int N, int S, int mtiles, int ntiles, int sb_per) {
     __shared__ __align__(16) Smem sm;
 
     const int tid = threadIdx.x;
@@ -203,16 +207,20 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
     // (round robin); tiles are regrouped so each XCD walks a contiguous run
     // of tiles, the token tiles of one row block after another, and shares
     // those rows' weights in its L2.
-    int tm, tn;
+    int tm, tn, z;
     {
-        const int64_t total = (int64_t)mtiles * ntiles;
-        const int64_t lin = blockIdx.x;
+        const int64_t tiles = (int64_t)mtiles * ntiles;
+        const int64_t total = tiles * gridDim.y;   // every K range of every tile
+        const int64_t lin = blockIdx.x + (int64_t)blockIdx.y * gridDim.x;
         const int64_t q = total / 8, r = total % 8;
         const int64_t xcd = lin % 8, slot = lin / 8;
         const int64_t t = xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
-        tm = (int)(t / ntiles);
-        tn = (int)(t % ntiles);
+        z = (int)(t / tiles);
+        tm = (int)((t % tiles) / ntiles);
+        tn = (int)((t % tiles) % ntiles);
     }
+    const int sb_beg = z * sb_per, nsb = min(S, sb_beg + sb_per) - sb_beg;
+    float* out = z == 0 ? y : part + (int64_t)(z - 1) * M * N;
     // A tile at the end of m or n starts early enough to lie inside the
     // tensor (its first rows/tokens repeat the previous tile's and are not
     // stored); the CLAMP form (a problem smaller than one tile) clamps.
@@ -220,7 +228,7 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
     const int n0 = CLAMP ? tn * BN : min(tn * BN, N - BN);
     const int mown = tm * BM, nown = tn * BN;   // first row / token this tile stores
 
-    issue_stage(sm.st[0], wave, lane, w, xq, 0, m0, n0, M, N, S);
+    issue_stage(sm.st[0], wave, lane, w, xq, sb_beg, m0, n0, M, N, S);
 
     // the fourth bf16 part of z is zero and never rewritten
     for (int i = tid; i < BN * 8; i += NTHR) sm.z[i >> 3][24 + (i & 7)] = 0;
@@ -245,8 +253,8 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
     const int dnrow = 8 * rw;                     // (D, nc) of row rw in a block's row: + 256*rt
     const int d8tok = 4 * (tk + 4 * h2);          // d8 of tokens tk+8g+4h2.. in a block's row: + 32*g
 
-    for (int sb = 0; sb < S; ++sb) {
-        Stage& st = sm.st[sb & 1];
+    for (int s = 0; s < nsb; ++s) {
+        Stage& st = sm.st[s & 1];
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wavefront's copies have landed
         __syncthreads();                      // everyone's copies; the previous step's reads done
 
@@ -302,7 +310,8 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
         }
         __syncthreads();
         // the next step's copies, into the other stage (free since the first barrier)
-        if (sb + 1 < S) issue_stage(sm.st[(sb + 1) & 1], wave, lane, w, xq, sb + 1, m0, n0, M, N, S);
+        if (s + 1 < nsb)
+            issue_stage(sm.st[(s + 1) & 1], wave, lane, w, xq, sb_beg + s + 1, m0, n0, M, N, S);
 
         // ---- compute: two 32-row tiles x 32 tokens per wavefront
         v16f part[2];
@@ -350,27 +359,63 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int n = n0 + 32 * wt + 8 * (i >> 2) + 4 * h2 + (i & 3);
-            if (n >= nown && n < N) y[(int64_t)n * M + m] = acc[rt][i];
+            if (n >= nown && n < N) out[(int64_t)n * M + m] = acc[rt][i];
         }
     }
 }
 
 }  // namespace
 
-hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
-                          int64_t k, int cus, hipStream_t stream) {
-    (void)cus;
+// K-split plan from a cost model fitted on MI355X (Qwen2-7B prefill shapes
+// at 2048 tokens).  With one workgroup per CU a grid of G workgroups runs in
+// ceil(G / cus) rounds; a workgroup of s superblocks takes about s + 2
+// superblock steps (its first stage is not overlapped, its stores are not
+// either), one step of a full round 4.66 us (gate 18944 x 3584 x 2048: 522
+// us for 7 rounds of 16 steps).  Each extra K range adds one f32 plane of
+// m*n written and read by the sum launch, 8*m*n bytes at about 5 TB/s.
+// P = 1..8 ranges of ceil(S/P) superblocks: the least estimated time wins.
+// Measured: down 3584 x 18944 (304 tiles, 1.19 rounds) 690 -> 525 us with
+// 5 ranges, QKV 4608 x 3584 (384 tiles) 149 -> 143 us with 2, gate/up
+// (1584 tiles, 6.2 rounds) unsplit.
+MmqPlan plan_mmq_q4k(int64_t m, int64_t n, int64_t k, int cus, int64_t max_ws) {
+    const int S = (int)(k / kQK);
+    const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+    const double step_us = 4.66, plane_us = 8.0 * (double)m * (double)n / 5e12 * 1e6;
+    MmqPlan best{4, 1, S, 0};
+    double best_us = 0.0;
+    for (int P = 1; P <= 8 && P <= S; ++P) {
+        const int sb_per = (S + P - 1) / P;
+        const int parts = (S + sb_per - 1) / sb_per;
+        if (parts != P) continue;
+        const int64_t ws = (int64_t)(parts - 1) * m * n * 4;
+        if (ws > max_ws) break;
+        const int64_t rounds = (tiles * parts + cus - 1) / cus;
+        const double us = (double)rounds * (sb_per + 2) * step_us + (parts - 1) * plane_us;
+        if (P == 1 || us < best_us) {
+            best = MmqPlan{4, parts, sb_per, ws};
+            best_us = us;
+        }
+    }
+    return best;
+}
+
+hipError_t launch_mmq_q4k_plan(const void* w, const void* xq, float* y, int64_t m, int64_t n,
+                               int64_t k, const MmqPlan& p, void* ws, hipStream_t stream) {
     const int S = (int)(k / kQK);
     const int64_t mt = (m + BM - 1) / BM, nt = (n + BN - 1) / BN;
-    if (mt * nt > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)(mt * nt));
-    if (m < BM || n < BN)
-        hipLaunchKernelGGL(mmq_q4k_kernel<true>, grid, dim3(NTHR), 0, stream, (const uint8_t*)w,
-                           (const uint8_t*)xq, y, (int)m, (int)n, S, (int)mt, (int)nt);
-    else
-        hipLaunchKernelGGL(mmq_q4k_kernel<false>, grid, dim3(NTHR), 0, stream, (const uint8_t*)w,
-                           (const uint8_t*)xq, y, (int)m, (int)n, S, (int)mt, (int)nt);
-    return hipGetLastError();
+    if (mt * nt > 0x7fffffffLL || p.parts < 1 || p.parts > 65535) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)(mt * nt), (unsigned)p.parts);
+    auto kern = (m < BM || n < BN) ? mmq_q4k_kernel<true> : mmq_q4k_kernel<false>;
+    hipLaunchKernelGGL(kern, grid, dim3(NTHR), 0, stream, (const uint8_t*)w, (const uint8_t*)xq, y,
+                       (float*)ws, (int)m, (int)n, S, (int)mt, (int)nt, p.sb_per);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && p.parts > 1) e = launch_splitk_sum(y, (const float*)ws, m * n, p.parts - 1, stream);
+    return e;
+}
+
+hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
+                          int64_t k, int cus, hipStream_t stream) {
+    return launch_mmq_q4k_plan(w, xq, y, m, n, k, plan_mmq_q4k(m, n, k, cus, 0), nullptr, stream);
 }
 
 }  // namespace kq

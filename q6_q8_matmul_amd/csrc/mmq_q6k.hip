@@ -262,36 +262,6 @@ void mmq_q6k_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ 
     }
 }
 
-// y[i] += part[0][i] + part[1][i] + ... in that order (count values; the
-// float4 form when y is 16-byte aligned and count a multiple of 4).
-__global__ __launch_bounds__(256) void splitk_sum_kernel(float* __restrict__ y,
-                                                         const float* __restrict__ part,
-                                                         int64_t count, int nparts) {
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    if (((uintptr_t)y & 15) == 0 && (count & 3) == 0) {
-        float4* y4 = (float4*)y;
-        const float4* p4 = (const float4*)part;
-        const int64_t c4 = count >> 2;
-        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < c4; i += stride) {
-            float4 v = y4[i];
-            for (int z = 0; z < nparts; ++z) {
-                const float4 q = p4[(int64_t)z * c4 + i];
-                v.x += q.x;
-                v.y += q.y;
-                v.z += q.z;
-                v.w += q.w;
-            }
-            y4[i] = v;
-        }
-    } else {
-        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += stride) {
-            float v = y[i];
-            for (int z = 0; z < nparts; ++z) v += part[(int64_t)z * count + i];
-            y[i] = v;
-        }
-    }
-}
-
 }  // namespace
 
 // Tokens per workgroup: the largest of 128, 64, 32 whose grid still gives
@@ -343,13 +313,9 @@ static hipError_t launch_mmq_q6k_any(const uint8_t* w, const uint16_t* wd, const
     if (nt == 4) launch(mmq_q6k_kernel<4, SPLIT>);
     else if (nt == 2) launch(mmq_q6k_kernel<2, SPLIT>);
     else launch(mmq_q6k_kernel<1, SPLIT>);
-    if (p.parts > 1) {
-        const int64_t count = m * n;
-        const int64_t blocks = std::min<int64_t>((count / 4 + 255) / 256, 4096);
-        hipLaunchKernelGGL(splitk_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y,
-                           (const float*)part, count, p.parts - 1);
-    }
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && p.parts > 1) e = launch_splitk_sum(y, part, m * n, p.parts - 1, stream);
+    return e;
 }
 
 hipError_t launch_mmq_q6k_plan(const void* w, const void* xq, float* y, int64_t m, int64_t n,

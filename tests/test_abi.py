@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
         "kq_q6k_split_bytes", "kq_repack_q6k", "kq_gemv_q6k_split", "kq_mmq_q6k_split",
         "kq_rmsnorm_q8_1", "kq_swiglu_q8_1", "kq_gemv_q4k_seg", "kq_last_error",
         "kq_abi_version", "kq_read_probe", "kq_read_probe_words", "kq_mmq_q6k_ws",
-        "kq_mmq_q6k_workspace_bytes", "kq_mmq_q6k_noalloc"])
+        "kq_mmq_q6k_workspace_bytes", "kq_mmq_q6k_noalloc", "kq_mmq_q4k_ws",
+        "kq_mmq_q4k_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(kq):
@@ -130,19 +131,21 @@ def test_mmq_rejects(kq, fn, args, needle):
     ((W, X, Y, 8, 8, 256, R, -16, None), "ws_bytes=-16"),
     ((W, X, Y, 8, 8, 256, None, 64, None), "ws_bytes=64"),
 ])
-def test_mmq_ws_rejects(kq, args, needle):
-    rc = kq.lib().kq_mmq_q6k_ws(*args)
+@pytest.mark.parametrize("fn", ["kq_mmq_q4k_ws", "kq_mmq_q6k_ws"])
+def test_mmq_ws_rejects(kq, fn, args, needle):
+    rc = getattr(kq.lib(), fn)(*args)
     assert rc == kq.KQ_ERR_ARG, kq.kq_last_error()
-    assert needle in kq.kq_last_error() and "kq_mmq_q6k_ws" in kq.kq_last_error()
-    assert kq.lib().kq_mmq_q6k_ws(W, X, Y, 0, 8, 256, None, 0, None) == kq.KQ_OK
+    assert needle in kq.kq_last_error() and fn in kq.kq_last_error()
+    assert getattr(kq.lib(), fn)(W, X, Y, 0, 8, 256, None, 0, None) == kq.KQ_OK
 
 
 @pytest.mark.parametrize("m,n,k", [(-1, 8, 256), (8, -1, 256), (8, 8, 100), (8, 8, 0),
                                    (8, 65535 * 128 + 1, 256), (8, 8, 65536 + 256)])
-def test_mmq_workspace_bytes_rejects(kq, m, n, k):
-    assert kq.lib().kq_mmq_q6k_workspace_bytes(m, n, k) == -1
-    assert "kq_mmq_q6k_workspace_bytes" in kq.kq_last_error()
-    assert kq.lib().kq_mmq_q6k_workspace_bytes(0, 8, 256) == 0
+@pytest.mark.parametrize("fn", ["kq_mmq_q4k_workspace_bytes", "kq_mmq_q6k_workspace_bytes"])
+def test_mmq_workspace_bytes_rejects(kq, fn, m, n, k):
+    assert getattr(kq.lib(), fn)(m, n, k) == -1
+    assert fn in kq.kq_last_error()
+    assert getattr(kq.lib(), fn)(0, 8, 256) == 0
 
 
 @pytest.mark.parametrize("m,k", [(0, 256), (1, 256), (3, 1280), (7, 4096), (128256, 4096), (5, 18944)])

@@ -493,6 +493,49 @@ def test_mmq_q6k_ksplit(kq, m, n, k):
     assert torch.equal(short, kq.mmq_q6k(wd, xd, m, n, k))
 
 
+# Q4_K: the prefill down projection (304 tiles of 192 x 128, 1.2 rounds of
+# one workgroup per CU: five K ranges), QKV (384 tiles: two), and small
+# products split up to eight ways, one of them on the clamped tile form.
+KSPLIT4 = [(3584, 2048, 18944), (4608, 2048, 3584), (400, 300, 4096), (129, 70, 1024),
+           (1000, 1000, 2560)]
+
+
+@pytest.mark.parametrize("m,n,k", KSPLIT4, ids=[f"m{c[0]}-n{c[1]}-k{c[2]}" for c in KSPLIT4])
+def test_mmq_q4k_ksplit(kq, m, n, k):
+    say(f"mmq q4k K split m={m} n={n} k={k}")
+    nb = kq.kq_mmq_q4k_workspace_bytes(m, n, k)
+    assert nb > 0 and nb % (m * n * 4) == 0 and nb // (m * n * 4) <= 7
+    w, x, _ = random_case(m * 5 + n + k, "q4k", m, k, n)
+    xq = oracle.quantize_q8_1(x)
+    wd, xd = dev(w), dev(xq)
+    ws = torch.full((nb,), 0x7F, dtype=torch.uint8, device="cuda")      # stale contents
+    y = host(kq.mmq_q4k_ws(wd, xd, m, n, k, ws=ws))
+    assert np.array_equal(y, host(kq.mmq_q4k_ws(wd, xd, m, n, k, ws=ws))), "not reproducible"
+    if m * n * k <= 1 << 36:
+        y_ref, den = oracle.matmul("q4k", w, xq, m, n, k)
+        check_close(y, y_ref, den, f"mmq q4k split m{m} n{n} k{k}")
+    else:
+        tok, row = _sample_pairs(m, n, np.random.default_rng(m))
+        y_ref, den = oracle.matmul_pairs("q4k", w, xq, m, n, k, tok, row)
+        check_close(y[tok, row], y_ref, den, f"mmq q4k split m{m} n{n} k{k} ({tok.size} outputs)")
+    # a workspace one byte short: the best split that fits (fewer ranges),
+    # still within the bound; no workspace: the unsplit product, bit for bit
+    short = host(kq.mmq_q4k_ws(wd, xd, m, n, k, ws=ws[: nb - 1]))
+    if m * n * k <= 1 << 36:
+        check_close(short, y_ref, den, f"mmq q4k split, short workspace")
+    else:
+        check_close(short[tok, row], y_ref, den, f"mmq q4k split, short workspace")
+    none = torch.empty((n, m), device="cuda")
+    kq.kq_mmq_q4k_ws(wd, xd, none, m, n, k, None, 0)
+    assert torch.equal(none, kq.mmq_q4k(wd, xd, m, n, k))
+
+
+def test_mmq_q4k_ksplit_not_taken_for_gate(kq):
+    """Gate 18944 x 3584 at 2048 tokens (1584 tiles, 6.2 rounds) is not split."""
+    assert kq.kq_mmq_q4k_workspace_bytes(18944, 2048, 3584) == 0
+    assert kq.kq_mmq_q4k_workspace_bytes(7168, 2048, 256) == 0   # one superblock
+
+
 def test_mmq_q6k_ksplit_not_taken_when_tiles_fill(kq):
     """A product whose 128-token tiles already give every CU two workgroups
     needs no workspace and gives the kq_mmq_q6k bits."""
