@@ -199,10 +199,13 @@ int kq_mmq_q6k(const void* w, const void* xq, float* y, int64_t m, int64_t n, in
  * adds workgroups, and a fixup pass combines the pieces).
  *   kq_mmq_q4k_workspace_bytes(m, n, k): bytes of workspace the split form
  *     needs on the current device -- 0 when the product is not split, -1
- *     for invalid sizes or device.  The k/256 superblocks are cut into P <= 8
- *     ranges, chosen by an estimate of the grid's rounds of one workgroup per
- *     compute unit against the extra partial planes; the workspace holds
- *     ranges 1..P-1 as f32 [P-1][n][m], and a second launch adds them to y
+ *     for invalid sizes or device.  The product runs in rounds of one
+ *     192-row x 128-token tile per compute unit; the row blocks whose tiles
+ *     make up the last, partly filled round (the whole product when it is
+ *     less than one round) have their k/256 superblocks cut into P <= 8
+ *     ranges, P chosen by an estimate of the rounds saved against the extra
+ *     partial planes.  The workspace holds ranges 1..P-1 of those rows
+ *     (r >= r0) as f32 [P-1][n][m - r0], and a second launch adds them to y
  *     (which holds range 0) in the order z = 1, 2, ...
  *   kq_mmq_q4k_ws: the same product; workspace rules, results and errors
  *     as for kq_mmq_q6k_ws below, except that a workspace smaller than the

@@ -180,20 +180,24 @@ hipError_t launch_read_probe(const void* p, int64_t nbytes, uint32_t* out, int64
                              hipStream_t stream);
 hipError_t launch_mmq_q4k(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                           int64_t k, int cus, hipStream_t stream);
-// Launch plan of a prefill product: NT 32-token tiles per workgroup, the K
-// range cut into `parts` pieces of sb_per superblocks (parts > 1 needs a
-// workspace of ws_bytes = (parts - 1) * m * n * 4 bytes).
+// Launch plan of a prefill product: NT 32-token tiles per workgroup (Q6_K),
+// the K range cut into `parts` pieces of sb_per superblocks.  Q4_K: only the
+// tiles of row blocks tail_rb.. (the last, partly filled round) are split;
+// tail_rb = 0 splits every tile.  parts > 1 needs ws_bytes = (parts - 1) *
+// n * (rows of the split row blocks) * 4 bytes.
 struct MmqPlan {
     int nt, parts, sb_per;
     int64_t ws_bytes;
+    int tail_rb = 0;
 };
 MmqPlan plan_mmq_q6k(int64_t m, int64_t n, int64_t k, int cus, int64_t max_ws);
 MmqPlan plan_mmq_q4k(int64_t m, int64_t n, int64_t k, int cus, int64_t max_ws);
 hipError_t launch_mmq_q4k_plan(const void* w, const void* xq, float* y, int64_t m, int64_t n,
                                int64_t k, const MmqPlan& plan, void* ws, hipStream_t stream);
-// y[i] = ((y[i] + part[0][i]) + part[1][i]) + ... over nparts planes of count.
-hipError_t launch_splitk_sum(float* y, const float* part, int64_t count, int nparts,
-                             hipStream_t stream);
+// y[r*ldy + c] = ((y + part[0][r][c]) + part[1][r][c]) + ... for r < rows,
+// c < cols, over nparts planes [rows][cols].
+hipError_t launch_splitk_sum(float* y, int64_t ldy, const float* part, int64_t rows, int64_t cols,
+                             int nparts, hipStream_t stream);
 // Static scratch of the allocation-free Q6_K product (bytes), and its
 // address on `device` (which must be the current device).
 constexpr int64_t kNoallocScratchBytes = 32LL << 20;

@@ -187,14 +187,17 @@ __device__ __forceinline__ void block_step(v16f (&part)[2], const v16i& magic, c
     }
 }
 
-// K split: the grid holds `parts` copies of the tile grid; copy z takes
-// superblocks [z * sb_per, min(S, (z + 1) * sb_per)) and writes its sums to
-// y (z = 0) or to part + (z - 1) * M * N (the same [token][row] layout),
-// which a second launch adds to y in the order z = 1, 2, ...
+// K split of the tail: the tiles of row blocks tail_rb.. run as `parts`
+// workgroups each, workgroup z taking superblocks [z * sb_per, min(S, (z + 1)
+// * sb_per)); z = 0 writes its sums to y, z > 0 to part + (z - 1) * N * Mt
+// ([token][row - tail_rb * BM], Mt = M - tail_rb * BM), which a second launch
+// adds to y in the order z = 1, 2, ...  The other tiles take the whole K
+// range.  The grid holds the unsplit tiles, then `parts` copies of the tail.
 template <bool CLAMP>
 __global__ __launch_bounds__(NTHR, 1)
 void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, float* y,
-                    float* part, int M, int N, int S, int mtiles, int ntiles, int sb_per) {
+                    float* part, int M, int N, int S, int mtiles, int ntiles, int sb_per,
+                    int tail_rb) {
     __shared__ __align__(16) Smem sm;
 
     const int tid = threadIdx.x;
@@ -207,20 +210,35 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
     // (round robin); tiles are regrouped so each XCD walks a contiguous run
     // of tiles, the token tiles of one row block after another, and shares
     // those rows' weights in its L2.
+    // The unsplit tiles are dispatched first and the split ones after them,
+    // each set regrouped on its own, so every XCD gets an equal share of
+    // both.
     int tm, tn, z;
     {
-        const int64_t tiles = (int64_t)mtiles * ntiles;
-        const int64_t total = tiles * gridDim.y;   // every K range of every tile
-        const int64_t lin = blockIdx.x + (int64_t)blockIdx.y * gridDim.x;
+        const int64_t head = (int64_t)tail_rb * ntiles;              // unsplit tiles
+        const int64_t tail = ((int64_t)mtiles - tail_rb) * ntiles;   // split tiles
+        const int64_t lin = blockIdx.x;
+        const bool in_head = lin < head;
+        const int64_t total = in_head ? head : (int64_t)gridDim.x - head;
+        const int64_t l = in_head ? lin : lin - head;
         const int64_t q = total / 8, r = total % 8;
-        const int64_t xcd = lin % 8, slot = lin / 8;
+        const int64_t xcd = l % 8, slot = l / 8;
         const int64_t t = xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
-        z = (int)(t / tiles);
-        tm = (int)((t % tiles) / ntiles);
-        tn = (int)((t % tiles) % ntiles);
+        int64_t tile = t;
+        z = 0;
+        if (!in_head) {
+            z = (int)(t / tail);
+            tile = head + t % tail;
+        }
+        tm = (int)(tile / ntiles);
+        tn = (int)(tile % ntiles);
     }
-    const int sb_beg = z * sb_per, nsb = min(S, sb_beg + sb_per) - sb_beg;
-    float* out = z == 0 ? y : part + (int64_t)(z - 1) * M * N;
+    const bool split_tile = tm >= tail_rb && gridDim.x > (unsigned)(mtiles * ntiles);
+    const int sb_beg = split_tile ? z * sb_per : 0;
+    const int nsb = split_tile ? min(S, sb_beg + sb_per) - sb_beg : S;
+    const int ldo = z == 0 ? M : M - tail_rb * BM;    // row stride of this workgroup's output
+    const int roff = z == 0 ? 0 : tail_rb * BM;       // first row of that output
+    float* out = z == 0 ? y : part + (int64_t)(z - 1) * N * ldo;
     // A tile at the end of m or n starts early enough to lie inside the
     // tensor (its first rows/tokens repeat the previous tile's and are not
     // stored); the CLAMP form (a problem smaller than one tile) clamps.
@@ -359,7 +377,7 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int n = n0 + 32 * wt + 8 * (i >> 2) + 4 * h2 + (i & 3);
-            if (n >= nown && n < N) out[(int64_t)n * M + m] = acc[rt][i];
+            if (n >= nown && n < N) out[(int64_t)n * ldo + (m - roff)] = acc[rt][i];
         }
     }
 }
@@ -369,30 +387,41 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
 // K-split plan from a cost model fitted on MI355X (Qwen2-7B prefill shapes
 // at 2048 tokens).  With one workgroup per CU a grid of G workgroups runs in
 // ceil(G / cus) rounds; a workgroup of s superblocks takes about s + 2
-// superblock steps (its first stage is not overlapped, its stores are not
-// either), one step of a full round 4.66 us (gate 18944 x 3584 x 2048: 522
-// us for 7 rounds of 16 steps).  Each extra K range adds one f32 plane of
-// m*n written and read by the sum launch, 8*m*n bytes at about 5 TB/s.
-// P = 1..8 ranges of ceil(S/P) superblocks: the least estimated time wins.
-// Measured: down 3584 x 18944 (304 tiles, 1.19 rounds) 690 -> 525 us with
-// 5 ranges, QKV 4608 x 3584 (384 tiles) 149 -> 143 us with 2, gate/up
-// (1584 tiles, 6.2 rounds) unsplit.
+// superblock steps (its first stage is not overlapped, nor are its stores),
+// one step of a full round 4.66 us (gate 18944 x 3584 x 2048: 522 us for 7
+// rounds of 16 steps).  Each extra K range adds one f32 plane over the split
+// tiles' outputs, written and then read by the sum launch at about 5 TB/s.
+// Only the row blocks that make up the last, partly filled round are split
+// (the whole grid when it is less than one round), into P = 2..8 ranges of
+// ceil(S/P) superblocks; the least estimated time wins, P = 1 (no split)
+// included.  Measured with the split of the whole grid: down 3584 x 18944
+// (304 tiles, 1.2 rounds) 690 -> 525 us with 5 ranges, QKV 4608 x 3584 (384
+// tiles) 149 -> 143 us with 2.
 MmqPlan plan_mmq_q4k(int64_t m, int64_t n, int64_t k, int cus, int64_t max_ws) {
     const int S = (int)(k / kQK);
-    const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-    const double step_us = 4.66, plane_us = 8.0 * (double)m * (double)n / 5e12 * 1e6;
-    MmqPlan best{4, 1, S, 0};
-    double best_us = 0.0;
-    for (int P = 1; P <= 8 && P <= S; ++P) {
+    const int64_t mt = (m + BM - 1) / BM, nt = (n + BN - 1) / BN, tiles = mt * nt;
+    const double step_us = 4.66;
+    auto rounds = [&](int64_t g) { return (g + cus - 1) / cus; };
+    MmqPlan best{4, 1, S, 0, 0};
+    double best_us = (double)rounds(tiles) * (S + 2) * step_us;
+    // row blocks whose tiles fill the whole rounds stay unsplit
+    const int64_t full = tiles / cus * cus;
+    const int64_t head_rb = tiles == full ? mt : full / nt;
+    if (head_rb >= mt) return best;
+    const int64_t tail_rows = m - head_rb * BM;
+    const double plane_us = 8.0 * (double)n * (double)tail_rows / 5e12 * 1e6;
+    for (int P = 2; P <= 8 && P <= S; ++P) {
         const int sb_per = (S + P - 1) / P;
         const int parts = (S + sb_per - 1) / sb_per;
         if (parts != P) continue;
-        const int64_t ws = (int64_t)(parts - 1) * m * n * 4;
+        const int64_t ws = (int64_t)(parts - 1) * n * tail_rows * 4;
         if (ws > max_ws) break;
-        const int64_t rounds = (tiles * parts + cus - 1) / cus;
-        const double us = (double)rounds * (sb_per + 2) * step_us + (parts - 1) * plane_us;
-        if (P == 1 || us < best_us) {
-            best = MmqPlan{4, parts, sb_per, ws};
+        const int64_t head = head_rb * nt, tail = tiles - head;
+        const double us = (double)rounds(head) * (S + 2) * step_us +
+                          (double)rounds(tail * parts) * (sb_per + 2) * step_us +
+                          (parts - 1) * plane_us;
+        if (us < best_us) {
+            best = MmqPlan{4, parts, sb_per, ws, (int)head_rb};
             best_us = us;
         }
     }
@@ -403,13 +432,19 @@ hipError_t launch_mmq_q4k_plan(const void* w, const void* xq, float* y, int64_t 
                                int64_t k, const MmqPlan& p, void* ws, hipStream_t stream) {
     const int S = (int)(k / kQK);
     const int64_t mt = (m + BM - 1) / BM, nt = (n + BN - 1) / BN;
-    if (mt * nt > 0x7fffffffLL || p.parts < 1 || p.parts > 65535) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)(mt * nt), (unsigned)p.parts);
+    if (p.parts < 1 || p.tail_rb < 0 || p.tail_rb > mt) return hipErrorInvalidConfiguration;
+    const int tail_rb = p.parts > 1 ? p.tail_rb : (int)mt;
+    const int64_t grid = tail_rb * nt + (mt - tail_rb) * nt * p.parts;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     auto kern = (m < BM || n < BN) ? mmq_q4k_kernel<true> : mmq_q4k_kernel<false>;
-    hipLaunchKernelGGL(kern, grid, dim3(NTHR), 0, stream, (const uint8_t*)w, (const uint8_t*)xq, y,
-                       (float*)ws, (int)m, (int)n, S, (int)mt, (int)nt, p.sb_per);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NTHR), 0, stream, (const uint8_t*)w,
+                       (const uint8_t*)xq, y, (float*)ws, (int)m, (int)n, S, (int)mt, (int)nt,
+                       p.sb_per, tail_rb);
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess && p.parts > 1) e = launch_splitk_sum(y, (const float*)ws, m * n, p.parts - 1, stream);
+    if (e == hipSuccess && p.parts > 1) {
+        const int64_t r0 = (int64_t)tail_rb * BM;
+        e = launch_splitk_sum(y + r0, m, (const float*)ws, n, m - r0, p.parts - 1, stream);
+    }
     return e;
 }
 

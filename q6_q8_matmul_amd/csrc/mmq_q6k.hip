@@ -314,7 +314,7 @@ static hipError_t launch_mmq_q6k_any(const uint8_t* w, const uint16_t* wd, const
     else if (nt == 2) launch(mmq_q6k_kernel<2, SPLIT>);
     else launch(mmq_q6k_kernel<1, SPLIT>);
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess && p.parts > 1) e = launch_splitk_sum(y, part, m * n, p.parts - 1, stream);
+    if (e == hipSuccess && p.parts > 1) e = launch_splitk_sum(y, m, part, n, m, p.parts - 1, stream);
     return e;
 }
 

@@ -494,17 +494,19 @@ def test_mmq_q6k_ksplit(kq, m, n, k):
 
 
 # Q4_K: the prefill down projection (304 tiles of 192 x 128, 1.2 rounds of
-# one workgroup per CU: five K ranges), QKV (384 tiles: two), and small
-# products split up to eight ways, one of them on the clamped tile form.
+# one workgroup per CU: the 48 tiles past the first round in five K ranges),
+# QKV (384 tiles: the last 128 in two), gate-sized grids whose last round is
+# split, and small products split up to eight ways, one of them on the
+# clamped tile form.
 KSPLIT4 = [(3584, 2048, 18944), (4608, 2048, 3584), (400, 300, 4096), (129, 70, 1024),
-           (1000, 1000, 2560)]
+           (1000, 1000, 2560), (7168, 2048, 1024)]
 
 
 @pytest.mark.parametrize("m,n,k", KSPLIT4, ids=[f"m{c[0]}-n{c[1]}-k{c[2]}" for c in KSPLIT4])
 def test_mmq_q4k_ksplit(kq, m, n, k):
     say(f"mmq q4k K split m={m} n={n} k={k}")
     nb = kq.kq_mmq_q4k_workspace_bytes(m, n, k)
-    assert nb > 0 and nb % (m * n * 4) == 0 and nb // (m * n * 4) <= 7
+    assert nb > 0 and nb % (n * 4) == 0 and nb <= 7 * m * n * 4   # ranges of the split rows
     w, x, _ = random_case(m * 5 + n + k, "q4k", m, k, n)
     xq = oracle.quantize_q8_1(x)
     wd, xd = dev(w), dev(xq)
@@ -530,10 +532,14 @@ def test_mmq_q4k_ksplit(kq, m, n, k):
     assert torch.equal(none, kq.mmq_q4k(wd, xd, m, n, k))
 
 
-def test_mmq_q4k_ksplit_not_taken_for_gate(kq):
-    """Gate 18944 x 3584 at 2048 tokens (1584 tiles, 6.2 rounds) is not split."""
-    assert kq.kq_mmq_q4k_workspace_bytes(18944, 2048, 3584) == 0
-    assert kq.kq_mmq_q4k_workspace_bytes(7168, 2048, 256) == 0   # one superblock
+def test_mmq_q4k_ksplit_sizes(kq):
+    """The split covers only the row blocks past the whole rounds of one
+    workgroup per CU: gate 18944 x 3584 at 2048 tokens (1584 tiles: 6 rounds
+    and 48 tiles) splits its last 512 rows into five ranges.  A single
+    superblock and a grid of exactly one round are not split."""
+    assert kq.kq_mmq_q4k_workspace_bytes(18944, 2048, 3584) == 4 * 2048 * 512 * 4
+    assert kq.kq_mmq_q4k_workspace_bytes(7168, 2048, 256) == 0
+    assert kq.kq_mmq_q4k_workspace_bytes(6144, 1024, 4096) == 0   # 32 x 8 = 256 tiles: one round
 
 
 def test_mmq_q6k_ksplit_not_taken_when_tiles_fill(kq):
