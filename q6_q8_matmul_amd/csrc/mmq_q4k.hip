@@ -39,8 +39,13 @@
 //     -1.5*2^23*D per sub-block, m as bf16, -dmin) and each token block's
 //     d8 (rewritten in place as f32) and z parts;
 //   * the compute phase reads everything from LDS.
-// Outputs beyond m or n are computed from clamped (valid) rows/tokens and not
-// stored.  No atomics; results are bitwise reproducible.
+// The last tile of m or n is shifted inward to lie inside the tensor (its
+// first rows or tokens repeat the previous tile's and are not stored); a
+// problem smaller than one tile clamps its rows and tokens instead.  With a
+// workspace, the tiles of the grid's last, partly filled round can run as
+// several workgroups over K ranges (a K split), whose partial sums a second
+// launch adds in a fixed order.  No atomics; results are bitwise
+// reproducible.
 #include "kq_device.h"
 
 #include <algorithm>
@@ -394,9 +399,10 @@ void mmq_q4k_kernel(const uint8_t* __restrict__ w, const uint8_t* __restrict__ x
 // Only the row blocks that make up the last, partly filled round are split
 // (the whole grid when it is less than one round), into P = 2..8 ranges of
 // ceil(S/P) superblocks; the least estimated time wins, P = 1 (no split)
-// included.  Measured with the split of the whole grid: down 3584 x 18944
-// (304 tiles, 1.2 rounds) 690 -> 525 us with 5 ranges, QKV 4608 x 3584 (384
-// tiles) 149 -> 143 us with 2.
+// included.  Measured in one run: down 3584 x 18944 (304 tiles, 1.2 rounds)
+// 708 -> 482 us with 5 ranges over its last 512 rows, QKV 4608 x 3584 (384
+// tiles) 155 -> 136 us with 2 over its last 1536, gate 18944 x 3584 541 ->
+// 524 us.
 MmqPlan plan_mmq_q4k(int64_t m, int64_t n, int64_t k, int cus, int64_t max_ws) {
     const int S = (int)(k / kQK);
     const int64_t mt = (m + BM - 1) / BM, nt = (n + BN - 1) / BN, tiles = mt * nt;
