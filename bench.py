@@ -23,12 +23,21 @@ at decode and prefill sizes next to a standalone quantisation, separately
 stored q, k, v projections as three launches against one segmented launch,
 and the Q6_K launches on the raw layout against the split layout.
 
+The steps are launched as HIP graph replays, each graph holding at least
+16 consecutive steps (the weight copies in turn); a replay of a graph costs a
+fixed ~6.5 us on the device before its first kernel (measured with the
+decode step: 38.8 us per step with one graph per step, 32.3 us with eight
+steps per graph, 31.3 us from stream launches in C++), which a graph of one
+step would add to every step.  Steps left over from a whole graph run as
+one-step graphs.
+
 ``roofline`` describes the dominant kernel of the step, kq_gemv_q4k: its
 algorithmic bytes per launch (weights + q8_1 activation + f32 output) over
 its average launch duration.  Each launch of the step is timed on its own
-right after the timed steps: a HIP graph runs it back to back once per weight
-copy, and HIP events recorded on that stream around repeated replays give the
-average duration per launch.
+right after the timed steps: a HIP graph runs it back to back at least 16
+times (the weight copies in turn), and HIP events recorded on that stream
+around repeated replays, each after an untimed warm-up of the same length,
+give the average duration per launch.
 
 ``cpu_baseline`` times the CPU oracle on the host cores on the same step and
 also reports how far the GPU step outputs are from it.
@@ -50,6 +59,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA (5.0 POPS)
 MALL_BYTES = 256 * 2 ** 20      # Infinity Cache
+GRAPH_MIN = 16                  # steps (or launches) per HIP graph, at least
 METRIC = "Q4_K×q8_1 GEMV weight GB/s (% HBM peak); prefill MMQ int8 TOPS (% peak)"
 
 
@@ -169,18 +179,47 @@ class Workload:
         return 2.0 * op["m"] * rows * op["k"]
 
 
+def cycle_len(ncopies: int) -> int:
+    """Steps (or launches) per graph: whole rounds of the weight copies, at
+    least GRAPH_MIN."""
+    return ncopies * math.ceil(GRAPH_MIN / ncopies)
+
+
 def build_graphs(wl: Workload):
+    """A graph of cycle_len(ncopies) consecutive steps (copy i % ncopies for
+    step i) and one graph per copy of a single step, for a remainder."""
     import torch
 
-    graphs = []
     side = torch.cuda.Stream()
+    spg = cycle_len(wl.ncopies)
+    many = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(many, stream=side):
+        for i in range(spg):
+            wl.step(i % wl.ncopies)
+    single = []
     for c in range(wl.ncopies):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
             wl.step(c)
-        graphs.append(g)
+        single.append(g)
     torch.cuda.synchronize()
-    return graphs
+    return {"steps_per_graph": spg, "many": many, "single": single}
+
+
+def run_steps(wl: Workload, n: int, graphs=None):
+    """Steps 0..n-1 (copy i % ncopies for step i): whole multi-step graphs,
+    then one-step graphs for the rest; without graphs, eager launches."""
+    i = 0
+    while i < n:
+        if graphs is None:
+            wl.step(i % wl.ncopies)
+            i += 1
+        elif n - i >= graphs["steps_per_graph"]:
+            graphs["many"].replay()
+            i += graphs["steps_per_graph"]
+        else:
+            graphs["single"][i % wl.ncopies].replay()
+            i += 1
 
 
 def timed_steps(wl: Workload, steps: int, warmup: int, graphs=None):
@@ -188,15 +227,12 @@ def timed_steps(wl: Workload, steps: int, warmup: int, graphs=None):
     synchronisation; weights rotate over the copies."""
     import torch
 
-    run = (lambda c: graphs[c].replay()) if graphs else wl.step
-    for i in range(warmup):
-        run(i % wl.ncopies)
+    run_steps(wl, warmup, graphs)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
-    for i in range(steps):
-        run(i % wl.ncopies)
+    run_steps(wl, steps, graphs)
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
@@ -204,21 +240,28 @@ def timed_steps(wl: Workload, steps: int, warmup: int, graphs=None):
 
 def kernel_durations(wl: Workload, target_ms: float = 10.0, rounds: int = 5):
     """Duration (ms) of every launch of the step.  For each launch a HIP graph
-    holds it once per weight copy, back to back on one stream.  In each of
+    holds it cycle_len(ncopies) times (the weight copies in turn), back to
+    back on one stream.  In each of
     `rounds` interleaved rounds every launch's graph is replayed between two
     HIP events recorded on the stream the kernels run on, and the elapsed
-    time is divided by the launch count.  Returns (label, kind, mean, median,
-    min) over the rounds."""
+    time is divided by the launch count; in the same round the same launches
+    are also issued straight to that stream, back to back between two events
+    (a graph's kernel nodes start a few microseconds apart, which a long
+    kernel's per-launch figure otherwise carries; short kernels are limited
+    by the host's launch rate there instead).  Returns (label, kind, mean,
+    median, min) of the graph figures and the median of the stream figures
+    over the rounds."""
     import torch
 
     side = torch.cuda.Stream()
     launches = wl.launches(0)
+    nper = cycle_len(wl.ncopies)                  # launches per graph
     graphs = []
     for j in range(len(launches)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
-            for c in range(wl.ncopies):
-                wl.launches(c)[j][2]()
+            for i in range(nper):
+                wl.launches(i % wl.ncopies)[j][2]()
         graphs.append(g)
     stream = torch.cuda.current_stream()
     reps = []
@@ -232,9 +275,17 @@ def kernel_durations(wl: Workload, target_ms: float = 10.0, rounds: int = 5):
         b.record(stream)
         torch.cuda.synchronize()
         reps.append(max(3, min(200, int(target_ms / max(a.elapsed_time(b), 1e-3)))))
+    fns = [[wl.launches(c)[j][2] for c in range(wl.ncopies)] for j in range(len(launches))]
     per = [[] for _ in graphs]
+    per_s = [[] for _ in graphs]
     for _ in range(rounds):
         for j, g in enumerate(graphs):
+            # untimed warm-up of the same length: the measured launch of a
+            # round follows other (often light) launches, and the first few
+            # milliseconds of a heavy kernel after them run slower (the head
+            # 128256x4096: 84-87 against 79.5 us, converging after ~0.1 s)
+            for _ in range(reps[j]):
+                g.replay()
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
@@ -242,16 +293,24 @@ def kernel_durations(wl: Workload, target_ms: float = 10.0, rounds: int = 5):
                 g.replay()
             b.record(stream)
             torch.cuda.synchronize()
-            per[j].append(a.elapsed_time(b) / (reps[j] * wl.ncopies))
+            per[j].append(a.elapsed_time(b) / (reps[j] * nper))
+            a.record(stream)
+            for _ in range(reps[j]):
+                for i in range(nper):
+                    fns[j][i % wl.ncopies]()
+            b.record(stream)
+            torch.cuda.synchronize()
+            per_s[j].append(a.elapsed_time(b) / (reps[j] * nper))
     out = []
     for j, (label, kind, _) in enumerate(launches):
         v = sorted(per[j])
-        out.append((label, kind, sum(v) / len(v), v[len(v) // 2], v[0]))
+        vs = sorted(per_s[j])
+        out.append((label, kind, sum(v) / len(v), v[len(v) // 2], v[0], vs[len(vs) // 2]))
     del graphs
     return out
 
 
-def _graph_time_ms(fn, target_ms: float = 20.0, per_graph: int = 8):
+def _graph_time_ms(fn, target_ms: float = 20.0, per_graph: int = GRAPH_MIN):
     """Average duration (ms) of fn(): a HIP graph holds per_graph launches back
     to back; it is replayed between two events on the launching stream."""
     import torch
@@ -271,12 +330,41 @@ def _graph_time_ms(fn, target_ms: float = 20.0, per_graph: int = 8):
     b.record(stream)
     torch.cuda.synchronize()
     reps = max(3, min(500, int(target_ms / max(a.elapsed_time(b), 1e-3))))
+    for _ in range(reps):           # untimed warm-up of the same length
+        g.replay()
     a.record(stream)
     for _ in range(reps):
         g.replay()
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) / (reps * per_graph)
+
+
+def _stream_time_ms(fn, target_ms: float = 20.0, per_round: int = GRAPH_MIN):
+    """Average duration (ms) of fn() issued straight to the current stream,
+    per_round calls back to back per repetition, between two events."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for _ in range(per_round):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(per_round):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    reps = max(3, min(500, int(target_ms / max(a.elapsed_time(b), 1e-3))))
+    for _ in range(reps * per_round):   # untimed warm-up of the same length
+        fn()
+    a.record(stream)
+    for _ in range(reps * per_round):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (reps * per_round)
 
 
 def measure_producers(cfg: int):
@@ -407,12 +495,16 @@ def measure_split(cfg: int):
                 fn = kq.kq_mmq_q6k if name == "raw" else kq.kq_mmq_q6k_split
                 launch = lambda w, fn=fn: fn(w, xq, y, m, rows, k)
             it = iter(range(1 << 30))
-            us = _graph_time_ms(lambda: launch(ws[next(it) % ncopy]), per_graph=ncopy) * 1e3
+            us = _graph_time_ms(lambda: launch(ws[next(it) % ncopy]), per_graph=cycle_len(ncopy)) * 1e3
+            us_s = _stream_time_ms(lambda: launch(ws[next(it) % ncopy]), per_round=cycle_len(ncopy)) * 1e3
             e[f"{name}_us"] = round(us, 2)
+            e[f"{name}_stream_us"] = round(us_s, 2)
             if op["op"] == "gemv_q6k":
                 e[f"{name}_weight_GBps"] = round(h.nbytes / (us * 1e-6) / 1e9, 1)
+                e[f"{name}_stream_weight_GBps"] = round(h.nbytes / (us_s * 1e-6) / 1e9, 1)
             else:
                 e[f"{name}_tops"] = round(2.0 * m * rows * k / (us * 1e-6) / 1e12, 1)
+                e[f"{name}_stream_tops"] = round(2.0 * m * rows * k / (us_s * 1e-6) / 1e12, 1)
         out.append(e)
         del raw, split
         torch.cuda.empty_cache()
@@ -522,7 +614,7 @@ def measure_ksplit(cfg: int):
         for name, launch in (("no_workspace", lambda w: plain(w, xq, y, m, n, k)),
                              ("k_split", lambda w: split(w, xq, y, m, n, k, ws, nb))):
             it = iter(range(1 << 30))
-            us = _graph_time_ms(lambda: launch(ws_[next(it) % ncopy]), per_graph=ncopy) * 1e3
+            us = _graph_time_ms(lambda: launch(ws_[next(it) % ncopy]), per_graph=cycle_len(ncopy)) * 1e3
             e[f"{name}_us"] = round(us, 2)
             e[f"{name}_tops"] = round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)
         out.append(e)
@@ -622,7 +714,8 @@ def read_floors_us(wl: Workload):
             grid = form[0] * cus
             res = torch.empty(kq.kq_read_probe_words(nbytes, grid, form[1]), dtype=torch.int32, device="cuda")
             launches = [lambda b=b: kq.kq_read_probe(b, nbytes, res, grid, form[1]) for b in bufs]
-            ms = _graph_time_ms(lambda: [f() for f in launches], target_ms=5.0, per_graph=1) / len(launches)
+            ms = _graph_time_ms(lambda: [f() for f in launches], target_ms=5.0,
+                                per_graph=cycle_len(len(launches)) // len(launches)) / len(launches)
             if best is None or ms < best[0]:
                 best = (ms, form)
             del res
@@ -932,8 +1025,9 @@ MMQ_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_AC
 
 def summarize_counters(cfg: int, counters_csv: str):
     """Per launch of workload cfg, the median of each counter over the
-    run's steps, and for the MMQ launches the matrix-core and VALU busy
-    fractions and the int8 MFMA work the counters saw against 2*M*N*K."""
+    run's steps, and for the MMQ launches the matrix-core busy fraction, the
+    VALU instruction count charged at 4 cycles each (VALU x4) and the int8
+    MFMA work the counters saw against 2*M*N*K."""
     import csv
     from kq_inputs import WORKLOADS
 
@@ -944,7 +1038,10 @@ def summarize_counters(cfg: int, counters_csv: str):
     out = [f"counters: {len(steps)} steps matched in {counters_csv}",
            f"normalisation: kernel cycles = GRBM_GUI_ACTIVE / {MI355X_XCDS} XCDs; "
            f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / ({SIMDS_PER_CU} SIMDs x {MI355X_CUS} CUs x kernel cycles); "
-           f"VALU busy = SQ_ACTIVE_INST_VALU (4-cycle issue slots) x 4 / the same"]
+           f"VALU x4 = 4 x SQ_ACTIVE_INST_VALU / the same, i.e. every VALU instruction charged "
+           f"4 cycles; a plain v_fmac_f32 stream at 2-8 wavefronts per SIMD issues one "
+           f"instruction per ~2.2-2.8 cycles and reads 1.44-1.78 on this measure, so a "
+           f"saturated VALU reads about 1.6, not 1.0"]
     for t, lab in enumerate(labels):
         if kinds[t] == "quantize":
             continue
@@ -972,9 +1069,9 @@ def summarize_counters(cfg: int, counters_csv: str):
                 lrec["mfma_busy"] = round(busy, 4)
                 out.append(f"  MFMA busy {100 * busy:6.1f} %")
             if "SQ_ACTIVE_INST_VALU" in med:
-                vbusy = 4 * med['SQ_ACTIVE_INST_VALU'] / simd_cycles
-                lrec["valu_busy"] = round(vbusy, 4)
-                out.append(f"  VALU busy {100 * vbusy:6.1f} %")
+                vx4 = 4 * med['SQ_ACTIVE_INST_VALU'] / simd_cycles
+                lrec["valu_x4"] = round(vx4, 4)
+                out.append(f"  VALU x4   {100 * vx4:6.1f} %")
         if kinds[t].startswith("gemv") and med.get("SQ_INSTS_VALU"):
             # one Q4_K wavefront pass covers 16 superblock-rows, a Q6_K one 16
             sbrows = op["m"] * (op["k"] // 256)
@@ -1034,7 +1131,7 @@ def mmq_roofline(entry):
     """Roofline object of the prefill half of the metric: the Q4_K MMQ
     launches of the prefill workload, 2*M*N*K int8 ops per launch over the
     launch's mean duration, against the dense int8 MFMA peak; matrix-core
-    and VALU busy fractions from the committed counter summary when it was
+    busy fraction and VALU x4 figure from the committed counter summary when it was
     taken on the current source."""
     if not entry:
         return None
@@ -1054,13 +1151,13 @@ def mmq_roofline(entry):
     if rec:
         for lab, v in rec["launches"].items():
             if lab in out["per_launch"]:
-                out["per_launch"][lab].update({k: v[k] for k in ("mfma_busy", "valu_busy", "clock_GHz") if k in v})
+                out["per_launch"][lab].update({k: v[k] for k in ("mfma_busy", "valu_x4", "clock_GHz") if k in v})
         out["counters"] = f"profiles/mmq_q4k_{entry['workload']}_counters.txt"
     return out
 
 
 def read_counters(kernel: str, workload: str):
-    """MFMA/VALU busy fractions per launch of `kernel` from the committed
+    """Matrix-core busy and VALU x4 figures per launch of `kernel` from the committed
     counter summary, if the kernel source is unchanged since."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.txt")
     if not os.path.exists(path):
@@ -1091,7 +1188,7 @@ def main(argv=None):
     ap.add_argument("--fetch-csv", default=None)
     ap.add_argument("--write-csv", default=None)
     ap.add_argument("--counters-csv", default=None,
-                    help="one --pmc pass with the MMQ counters (matrix-core and VALU busy)")
+                    help="one --pmc pass with the MMQ counters (matrix-core busy, VALU instructions)")
     args = ap.parse_args(argv)
 
     if args.summarize:
@@ -1147,18 +1244,20 @@ def main(argv=None):
         wl, ms, durs, clocks = measure(cfg, steps, warm, use_graph)
         per_op = []
         for i, op in enumerate(wl.ops):
-            label, kind, avg_ms, med_ms, min_ms = [d for d in durs if d[0] == op["label"]][0]
+            label, kind, avg_ms, med_ms, min_ms, str_ms = [d for d in durs if d[0] == op["label"]][0]
             e = {"op": op["label"], "kernel": "kq_" + op["op"], "shape": [op["m"], op["k"], op.get("batch", op.get("n"))],
                  "avg_us": round(avg_ms * 1e3, 2), "median_us": round(med_ms * 1e3, 2),
-                 "min_us": round(min_ms * 1e3, 2)}
+                 "min_us": round(min_ms * 1e3, 2), "stream_median_us": round(str_ms * 1e3, 2)}
             if op["op"].startswith("mmq"):
                 tops = wl.op_ops(i) / (avg_ms * 1e-3) / 1e12
                 e["tops"] = round(tops, 2)
                 e["frac_int8_peak"] = round(tops / INT8_PEAK_TOPS, 4)
+                e["frac_int8_peak_stream"] = round(wl.op_ops(i) / (str_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
             else:
                 gbps = wl.host[op["w"]].nbytes / (avg_ms * 1e-3) / 1e9
                 e["weight_GBps"] = round(gbps, 1)
                 e["frac_hbm"] = round(gbps / HBM_PEAK_GBPS, 4)
+                e["frac_hbm_stream"] = round(wl.host[op["w"]].nbytes / (str_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
             per_op.append(e)
         if any(op["op"].startswith("gemv") for op in wl.ops):
             floors = read_floors_us(wl)
@@ -1171,8 +1270,11 @@ def main(argv=None):
         step_rate = wl.weight_bytes_step / (ms * 1e-3) / 1e9
         entry = {"workload": wl.wl["name"], "ms_per_step": round(ms, 5),
                  "weight_bytes_per_step": wl.weight_bytes_step, "weight_copies": wl.ncopies,
+                 "steps_per_graph": cycle_len(wl.ncopies) if use_graph else None,
                  "step_weight_GBps": round(step_rate, 1), "kernels": per_op, "quantize": quant,
-                 "timing": "kernel figures: mean, median and min over 5 interleaved rounds of graph replays",
+                 "timing": "kernel figures: mean, median and min over 5 interleaved rounds of graph "
+                           "replays (frac_* from the mean); stream_median_us / *_stream: the same launches "
+                           "issued straight to the stream in the same rounds (median)",
                  "clock_power": clocks}
         if prefill:
             tot_ops = sum(wl.op_ops(i) for i in range(len(wl.ops)))
@@ -1207,7 +1309,8 @@ def main(argv=None):
                            "shapes": "attn_out 4096x4096; gate and up 14336x4096 each, one launch over "
                                      "their contiguous 28672 rows; down 4096x14336",
                            "batch": 1, "weight_format": "Q4_K", "activation_format": "q8_1",
-                           "hip_graphs": use_graph},
+                           "hip_graphs": use_graph,
+                           "steps_per_graph": cycle_len(wl.ncopies) if use_graph else None},
                 "roofline": roofline,
             }
             if ceiling:

@@ -38,7 +38,7 @@ def test_source_hash_ignores_comments_not_code(tmp_path, monkeypatch):
     assert bench.source_hash("a") != ha
 
 
-def _collection(path, steps, ghz, mfma_busy, valu_busy, mops_factor):
+def _collection(path, steps, ghz, mfma_busy, valu_x4, mops_factor):
     """Counter rows for `steps` steps of workload 9 (quantise, v, quantise,
     down): each MMQ dispatch lasts 100 us at `ghz` on every XCD."""
     dur_ns = 100_000
@@ -60,7 +60,7 @@ def _collection(path, steps, ghz, mfma_busy, valu_busy, mops_factor):
                 m, n, k = shapes[label]
                 vals = {"SQ_INSTS_VALU_MFMA_MOPS_I8": mops_factor * 2 * m * n * k / 512,
                         "SQ_VALU_MFMA_BUSY_CYCLES": mfma_busy * simd_cycles,
-                        "SQ_ACTIVE_INST_VALU": valu_busy * simd_cycles / 4,
+                        "SQ_ACTIVE_INST_VALU": valu_x4 * simd_cycles / 4,
                         "SQ_INSTS_MFMA": 1.0, "SQ_INSTS_VALU": 1.0,
                         "GRBM_GUI_ACTIVE": 8 * cyc}
                 dur = dur_ns
@@ -77,7 +77,7 @@ def _collection(path, steps, ghz, mfma_busy, valu_busy, mops_factor):
 
 def test_counter_summary_fractions_work_and_clock(tmp_path):
     path = tmp_path / "run_counter_collection.csv"
-    _collection(path, steps=3, ghz=2.0, mfma_busy=0.25, valu_busy=0.5, mops_factor=2)
+    _collection(path, steps=3, ghz=2.0, mfma_busy=0.25, valu_x4=0.5, mops_factor=2)
     out = bench.summarize_counters(9, str(path))
     assert "3 steps matched" in out
     lines = out.split("\n")
@@ -90,13 +90,13 @@ def test_counter_summary_fractions_work_and_clock(tmp_path):
             block.append(l)
         block = "\n".join(block)
         assert "MFMA busy   25.0 %" in block, block
-        assert "VALU busy   50.0 %" in block, block
+        assert "VALU x4     50.0 %" in block, block
         assert "= 2.000 x 2MNK" in block, block
         assert "clock     2.000 GHz" in block, block
         assert "dispatch time 100.0 us" in block, block
     rec = [json.loads(l.split(": ", 1)[1]) for l in lines if l.startswith("counters_json: ")]
     assert len(rec) == 1 and rec[0]["kernel"] == "kq_mmq_q6k"
-    assert rec[0]["launches"]["down"] == {"mfma_busy": 0.25, "valu_busy": 0.5, "clock_GHz": 2.0}
+    assert rec[0]["launches"]["down"] == {"mfma_busy": 0.25, "valu_x4": 0.5, "clock_GHz": 2.0}
 
 
 def _decode_run(path, counter, steps, per_label, copy_factor):
