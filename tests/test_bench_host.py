@@ -185,3 +185,39 @@ def test_mmq_roofline_sums_ops_over_time():
     # 2 launches of 2*1000*2000*500 = 2e9 ops in 4 us: 1000 TOPS
     assert r["achieved"] == 1000.0 and r["frac"] == 0.2 and r["bound"] == "mfma"
     assert set(r["per_launch"]) == {"gate", "down"} and "counters" not in r
+
+
+def test_run_steps_whole_graphs_then_singles():
+    """run_steps covers steps 0..n-1 exactly once, copy i % ncopies for step
+    i: whole multi-step graphs first, one-step graphs for the remainder."""
+    import bench
+
+    class WL:
+        ncopies = 3
+
+        def __init__(self):
+            self.eager = []
+
+        def step(self, c):
+            self.eager.append(c)
+
+    log = []
+
+    class G:
+        def __init__(self, steps):
+            self.steps = steps
+
+        def replay(self):
+            log.extend(self.steps)
+
+    wl = WL()
+    spg = bench.cycle_len(wl.ncopies)
+    assert spg % wl.ncopies == 0 and spg >= bench.GRAPH_MIN
+    graphs = {"steps_per_graph": spg, "many": G([i % 3 for i in range(spg)]),
+              "single": [G([c]) for c in range(3)]}
+    for n in (0, 1, spg - 1, spg, 2 * spg + 5, 200):
+        log.clear()
+        bench.run_steps(wl, n, graphs)
+        assert log == [i % 3 for i in range(n)], n
+    bench.run_steps(wl, 7, None)
+    assert wl.eager == [i % 3 for i in range(7)]
