@@ -238,13 +238,15 @@ def timed_steps(wl: Workload, steps: int, warmup: int, graphs=None):
     return start.elapsed_time(end) / steps
 
 
-def kernel_durations(wl: Workload, target_ms: float = 10.0, rounds: int = 5):
+def kernel_durations(wl: Workload, target_ms: float = 10.0, rounds: int = 5,
+                     warm_ms: float = 50.0):
     """Duration (ms) of every launch of the step.  For each launch a HIP graph
     holds it cycle_len(ncopies) times (the weight copies in turn), back to
     back on one stream.  In each of
     `rounds` interleaved rounds every launch's graph is replayed between two
     HIP events recorded on the stream the kernels run on, and the elapsed
-    time is divided by the launch count; in the same round the same launches
+    time is divided by the launch count (after an untimed warm-up of at least
+    warm_ms of the same graph); in the same round the same launches
     are also issued straight to that stream, back to back between two events
     (a graph's kernel nodes start a few microseconds apart, which a long
     kernel's per-launch figure otherwise carries; short kernels are limited
@@ -264,7 +266,7 @@ def kernel_durations(wl: Workload, target_ms: float = 10.0, rounds: int = 5):
                 wl.launches(i % wl.ncopies)[j][2]()
         graphs.append(g)
     stream = torch.cuda.current_stream()
-    reps = []
+    reps, warm = [], []
     for g in graphs:
         g.replay()
         torch.cuda.synchronize()
@@ -274,17 +276,19 @@ def kernel_durations(wl: Workload, target_ms: float = 10.0, rounds: int = 5):
         g.replay()
         b.record(stream)
         torch.cuda.synchronize()
-        reps.append(max(3, min(200, int(target_ms / max(a.elapsed_time(b), 1e-3)))))
+        t_graph = max(a.elapsed_time(b), 1e-3)
+        reps.append(max(3, min(200, int(target_ms / t_graph))))
+        warm.append(max(reps[-1], math.ceil(warm_ms / t_graph)))
     fns = [[wl.launches(c)[j][2] for c in range(wl.ncopies)] for j in range(len(launches))]
     per = [[] for _ in graphs]
     per_s = [[] for _ in graphs]
     for _ in range(rounds):
         for j, g in enumerate(graphs):
-            # untimed warm-up of the same length: the measured launch of a
-            # round follows other (often light) launches, and the first few
-            # milliseconds of a heavy kernel after them run slower (the head
-            # 128256x4096: 84-87 against 79.5 us, converging after ~0.1 s)
-            for _ in range(reps[j]):
+            # untimed warm-up of at least warm_ms: the measured launch of a
+            # round follows other (often light) launches, and a heavy kernel
+            # right after them ran slower for a while (the head 128256x4096:
+            # 84-87 against 79.5 us, converging after ~0.1 s of it)
+            for _ in range(warm[j]):
                 g.replay()
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
