@@ -700,8 +700,8 @@ def stream_read_ceiling(nbytes: int = 2 << 30, reps: int = 10):
 def read_floors_us(wl: Workload):
     """Per GEMV launch of the step, the least time any kq_read_probe form of
     PROBE_FORMS takes to read the same weight tensor, rotated over the same
-    copies and timed the same way as the launch itself (graph replay of one
-    launch per copy).  Returns {label: (us, form)}."""
+    copies and timed the same way as the launch itself (graph replays of
+    whole rounds of the copies).  Returns {label: (us, form)}."""
     import torch
 
     import q6_q8_matmul_amd as kq
