@@ -51,3 +51,64 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for a, b in zip(ref, (xq, y4, y6, ym)):
             assert torch.equal(a, b)
+
+
+def test_multi_step_graph_over_copies_matches_eager():
+    """What bench.py replays: one graph holding several steps that rotate over
+    weight copies, here with the segmented GEMV and the K-split MMQ (whose
+    fixed-order sum is a second launch inside the graph).  Every replay, with
+    eager work in between, must give each copy's eager outputs bit for bit."""
+    import q6_q8_matmul_amd as kq
+    from kq_inputs import random_case
+
+    print("\n[case] multi-step graph: seg GEMV + K-split MMQ over 2 weight copies", flush=True)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    m_q, m_k, k, batch = 512, 256, 2048, 2
+    mm, nn, kk = 384, 256, 2048
+    nb = kq.kq_mmq_q4k_workspace_bytes(mm, nn, kk)
+    assert nb > 0, "the MMQ shape must take the K split"
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    copies = []
+    for c in range(2):
+        wq, x, _ = random_case(10 + c, "q4k", m_q, k, batch)
+        wk, _, _ = random_case(20 + c, "q4k", m_k, k, batch)
+        wm, xm, _ = random_case(30 + c, "q4k", mm, kk, nn)
+        copies.append({"wq": d(wq), "wk": d(wk), "wm": d(wm), "x": d(x), "xm": d(xm),
+                       "xq": torch.empty((batch, k // 32 * 36), dtype=torch.uint8, device="cuda"),
+                       "xqm": torch.empty((nn, kk // 32 * 36), dtype=torch.uint8, device="cuda"),
+                       "yq": torch.empty((batch, m_q), device="cuda"),
+                       "yk": torch.empty((batch, m_k), device="cuda"),
+                       "ym": torch.empty((nn, mm), device="cuda")})
+
+    def step(c):
+        t = copies[c]
+        kq.kq_quantize_q8_1(t["x"], t["xq"], batch, k)
+        kq.kq_gemv_q4k_seg([t["wq"], t["wk"]], [m_q, m_k], [t["yq"], t["yk"]], None, t["xq"], k, batch)
+        kq.kq_quantize_q8_1(t["xm"], t["xqm"], nn, kk)
+        kq.kq_mmq_q4k_ws(t["wm"], t["xqm"], t["ym"], mm, nn, kk, ws, nb)
+
+    outs = ("xq", "yq", "yk", "xqm", "ym")
+    ref = []
+    for c in range(2):
+        step(c)
+        torch.cuda.synchronize()
+        ref.append({n: copies[c][n].clone() for n in outs})
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(6):
+            step(i % 2)
+    for rep in range(3):
+        for c in range(2):
+            for n in outs:
+                copies[c][n].zero_()        # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for c in range(2):
+            for n in outs:
+                assert torch.equal(ref[c][n], copies[c][n]), f"replay {rep}, copy {c}: {n} differs"
+        step(rep % 2)                       # eager again, still identical
+        torch.cuda.synchronize()
+        for n in outs:
+            assert torch.equal(ref[rep % 2][n], copies[rep % 2][n])
