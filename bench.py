@@ -1025,13 +1025,15 @@ def summarize(cfg: int, trace_csv=None, fetch_csv=None, write_csv=None):
 MI355X_CUS, MI355X_XCDS, SIMDS_PER_CU = 256, 8, 4
 MMQ_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
                 "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE")
+LDS_COUNTERS = ("SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS")
 
 
 def summarize_counters(cfg: int, counters_csv: str):
     """Per launch of workload cfg, the median of each counter over the
     run's steps, and for the MMQ launches the matrix-core busy fraction, the
     VALU instruction count charged at 4 cycles each (VALU x4) and the int8
-    MFMA work the counters saw against 2*M*N*K."""
+    MFMA work the counters saw against 2*M*N*K; with the LDS counters, the
+    fraction of CU-cycles the LDS is busy and stalled on bank conflicts."""
     import csv
     from kq_inputs import WORKLOADS
 
@@ -1046,11 +1048,16 @@ def summarize_counters(cfg: int, counters_csv: str):
            f"4 cycles; a plain v_fmac_f32 stream at 2-8 wavefronts per SIMD issues one "
            f"instruction per ~2.2-2.8 cycles and reads 1.44-1.78 on this measure, so a "
            f"saturated VALU reads about 1.6, not 1.0"]
+    present = {r["Counter_Name"] for r in rows}
+    names = [n for n in MMQ_COUNTERS + LDS_COUNTERS if n in present]
+    if present & set(LDS_COUNTERS):
+        out.append(f"LDS busy = SQ_LDS_IDX_ACTIVE / ({MI355X_CUS} CUs x kernel cycles); LDS bank-conflict "
+                   f"= SQ_LDS_BANK_CONFLICT / the same")
     for t, lab in enumerate(labels):
         if kinds[t] == "quantize":
             continue
         med = {}
-        for name in MMQ_COUNTERS:
+        for name in names:
             v = sorted(sum(float(r["Counter_Value"]) for r in s[t] if r["Counter_Name"] == name)
                        for s in steps)
             if v:
@@ -1059,7 +1066,7 @@ def summarize_counters(cfg: int, counters_csv: str):
         rows = op.get("n", op.get("batch"))
         work = 2.0 * op["m"] * rows * op["k"]
         out.append(f"{lab} ({kinds[t]}, {op['m']}x{op['k']} x {rows} columns, 2MNK = {work:.4e}):")
-        for name in MMQ_COUNTERS:
+        for name in names:
             if name in med:
                 out.append(f"  {name:28s} median {med[name]:16,.0f}")
         cyc = med.get("GRBM_GUI_ACTIVE", 0) / MI355X_XCDS
@@ -1076,6 +1083,11 @@ def summarize_counters(cfg: int, counters_csv: str):
                 vx4 = 4 * med['SQ_ACTIVE_INST_VALU'] / simd_cycles
                 lrec["valu_x4"] = round(vx4, 4)
                 out.append(f"  VALU x4   {100 * vx4:6.1f} %")
+            if "SQ_LDS_IDX_ACTIVE" in med:
+                lds = med["SQ_LDS_IDX_ACTIVE"] / (MI355X_CUS * cyc)
+                conf = med.get("SQ_LDS_BANK_CONFLICT", 0.0) / (MI355X_CUS * cyc)
+                lrec["lds_busy"], lrec["lds_bank_conflict"] = round(lds, 4), round(conf, 4)
+                out.append(f"  LDS busy  {100 * lds:6.1f} %   bank-conflict {100 * conf:5.1f} %")
         if kinds[t].startswith("gemv") and med.get("SQ_INSTS_VALU"):
             # one Q4_K wavefront pass covers 16 superblock-rows, a Q6_K one 16
             sbrows = op["m"] * (op["k"] // 256)

@@ -38,7 +38,7 @@ def test_source_hash_ignores_comments_not_code(tmp_path, monkeypatch):
     assert bench.source_hash("a") != ha
 
 
-def _collection(path, steps, ghz, mfma_busy, valu_x4, mops_factor):
+def _collection(path, steps, ghz, mfma_busy, valu_x4, mops_factor, lds=None):
     """Counter rows for `steps` steps of workload 9 (quantise, v, quantise,
     down): each MMQ dispatch lasts 100 us at `ghz` on every XCD."""
     dur_ns = 100_000
@@ -63,6 +63,9 @@ def _collection(path, steps, ghz, mfma_busy, valu_x4, mops_factor):
                         "SQ_ACTIVE_INST_VALU": valu_x4 * simd_cycles / 4,
                         "SQ_INSTS_MFMA": 1.0, "SQ_INSTS_VALU": 1.0,
                         "GRBM_GUI_ACTIVE": 8 * cyc}
+                if lds is not None:           # (busy, bank-conflict) fractions of CU-cycles
+                    vals["SQ_LDS_IDX_ACTIVE"] = lds[0] * 256 * cyc
+                    vals["SQ_LDS_BANK_CONFLICT"] = lds[1] * 256 * cyc
                 dur = dur_ns
             for cname, v in vals.items():
                 rows.append({"Correlation_Id": disp, "Dispatch_Id": disp, "Kernel_Name": name,
@@ -221,3 +224,16 @@ def test_run_steps_whole_graphs_then_singles():
         assert log == [i % 3 for i in range(n)], n
     bench.run_steps(wl, 7, None)
     assert wl.eager == [i % 3 for i in range(7)]
+
+
+def test_summarize_lds_counters(tmp_path):
+    """With the LDS counters in the collection, the summary reports the LDS
+    busy and bank-conflict fractions of CU-cycles and records them."""
+    path = tmp_path / "c.csv"
+    _collection(path, steps=3, ghz=2.0, mfma_busy=0.25, valu_x4=0.5, mops_factor=2, lds=(0.3, 0.02))
+    text = bench.summarize_counters(9, str(path))
+    assert "LDS busy = SQ_LDS_IDX_ACTIVE" in text
+    assert text.count("LDS busy    30.0 %   bank-conflict   2.0 %") == 2, text
+    rec = [json.loads(l[len("counters_json: "):]) for l in text.splitlines() if l.startswith("counters_json: ")]
+    assert rec[0]["launches"]["down"]["lds_busy"] == 0.3
+    assert rec[0]["launches"]["down"]["lds_bank_conflict"] == 0.02
