@@ -125,6 +125,22 @@ class Workload:
                 self.res[op["residual"]] = torch.from_numpy(host[op["residual"]]).cuda()
         torch.cuda.synchronize()
 
+    def launch_fn(self, i: int, w):
+        """The launch of op i on weight tensor w."""
+        kq = self.kq
+        op = self.ops[i]
+        xq = self.xq[op["x"]]
+        y = self.y[i]
+        if op["op"] == "gemv_q4k" or op["op"] == "gemv_q6k":
+            res = self.res.get(op.get("residual"))
+            fn = kq.kq_gemv_q4k if op["op"] == "gemv_q4k" else kq.kq_gemv_q6k
+            return lambda: fn(w, xq, y, res, op["m"], op["k"], op["batch"])
+        ws = self.ws[i]
+        if op["op"] == "mmq_q6k":          # the K split when the product is small
+            return lambda: kq.kq_mmq_q6k_ws(w, xq, y, op["m"], op["n"], op["k"], ws, ws.numel())
+        # Q4_K: the K split where tiles leave CUs idle
+        return lambda: kq.kq_mmq_q4k_ws(w, xq, y, op["m"], op["n"], op["k"], ws, ws.numel())
+
     def launches(self, c: int):
         """(label, kind, callable) for every launch of one step on copy c."""
         kq = self.kq
@@ -138,26 +154,22 @@ class Workload:
                 out.append((f"quantize {xn}", "quantize",
                             lambda x=x, xq=xq, rows=rows, k=k: kq.kq_quantize_q8_1(x, xq, rows, k)))
                 done.add(xn)
-            w = self.w[c][op["w"]]
-            xq = self.xq[xn]
-            y = self.y[i]
-            if op["op"] == "gemv_q4k" or op["op"] == "gemv_q6k":
-                res = self.res.get(op.get("residual"))
-                fn = kq.kq_gemv_q4k if op["op"] == "gemv_q4k" else kq.kq_gemv_q6k
-                out.append((op["label"], op["op"],
-                            lambda fn=fn, w=w, xq=xq, y=y, res=res, op=op:
-                            fn(w, xq, y, res, op["m"], op["k"], op["batch"])))
-            elif op["op"] == "mmq_q6k":          # the K split when the product is small
-                ws = self.ws[i]
-                out.append((op["label"], op["op"],
-                            lambda w=w, xq=xq, y=y, op=op, ws=ws:
-                            kq.kq_mmq_q6k_ws(w, xq, y, op["m"], op["n"], op["k"], ws, ws.numel())))
-            else:                                 # Q4_K: the K split where tiles leave CUs idle
-                ws = self.ws[i]
-                out.append((op["label"], op["op"],
-                            lambda w=w, xq=xq, y=y, op=op, ws=ws:
-                            kq.kq_mmq_q4k_ws(w, xq, y, op["m"], op["n"], op["k"], ws, ws.numel())))
+            out.append((op["label"], op["op"], self.launch_fn(i, self.w[c][op["w"]])))
         return out
+
+    def launch_rotation(self, label: str):
+        """The callables that time launch `label` on its own: one per copy
+        of its weight tensor, enough copies that their footprint exceeds
+        twice the Infinity Cache (the step's copies, plus clones), so every
+        launch streams its weights from HBM; a quantisation has one."""
+        for i, op in enumerate(self.ops):
+            if op["label"] == label:
+                name = op["w"]
+                n = max(self.ncopies, copies_for(self.host[name].nbytes))
+                ws = [self.w[c][name] for c in range(self.ncopies)]
+                ws += [ws[0].clone() for _ in range(n - len(ws))]
+                return [self.launch_fn(i, w) for w in ws]
+        return [fn for lab, _, fn in self.launches(0) if lab == label]
 
     def step(self, c: int):
         for _, _, fn in self.launches(c):
@@ -241,8 +253,9 @@ def timed_steps(wl: Workload, steps: int, warmup: int, graphs=None):
 def kernel_durations(wl: Workload, target_ms: float = 10.0, rounds: int = 5,
                      warm_ms: float = 50.0):
     """Duration (ms) of every launch of the step.  For each launch a HIP graph
-    holds it cycle_len(ncopies) times (the weight copies in turn), back to
-    back on one stream.  In each of
+    holds it cycle_len(n) times over n copies of its own weight tensor
+    (Workload.launch_rotation: enough copies that every launch streams from
+    HBM), back to back on one stream.  In each of
     `rounds` interleaved rounds every launch's graph is replayed between two
     HIP events recorded on the stream the kernels run on, and the elapsed
     time is divided by the launch count (after an untimed warm-up of at least
@@ -257,13 +270,14 @@ def kernel_durations(wl: Workload, target_ms: float = 10.0, rounds: int = 5,
 
     side = torch.cuda.Stream()
     launches = wl.launches(0)
-    nper = cycle_len(wl.ncopies)                  # launches per graph
+    fns = [wl.launch_rotation(label) for label, _, _ in launches]
+    nper = [cycle_len(len(f)) for f in fns]       # launches per graph
     graphs = []
     for j in range(len(launches)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
-            for i in range(nper):
-                wl.launches(i % wl.ncopies)[j][2]()
+            for i in range(nper[j]):
+                fns[j][i % len(fns[j])]()
         graphs.append(g)
     stream = torch.cuda.current_stream()
     reps, warm = [], []
@@ -279,7 +293,6 @@ def kernel_durations(wl: Workload, target_ms: float = 10.0, rounds: int = 5,
         t_graph = max(a.elapsed_time(b), 1e-3)
         reps.append(max(3, min(200, int(target_ms / t_graph))))
         warm.append(max(reps[-1], math.ceil(warm_ms / t_graph)))
-    fns = [[wl.launches(c)[j][2] for c in range(wl.ncopies)] for j in range(len(launches))]
     per = [[] for _ in graphs]
     per_s = [[] for _ in graphs]
     for _ in range(rounds):
@@ -297,20 +310,21 @@ def kernel_durations(wl: Workload, target_ms: float = 10.0, rounds: int = 5,
                 g.replay()
             b.record(stream)
             torch.cuda.synchronize()
-            per[j].append(a.elapsed_time(b) / (reps[j] * nper))
+            per[j].append(a.elapsed_time(b) / (reps[j] * nper[j]))
             a.record(stream)
             for _ in range(reps[j]):
-                for i in range(nper):
-                    fns[j][i % wl.ncopies]()
+                for i in range(nper[j]):
+                    fns[j][i % len(fns[j])]()
             b.record(stream)
             torch.cuda.synchronize()
-            per_s[j].append(a.elapsed_time(b) / (reps[j] * nper))
+            per_s[j].append(a.elapsed_time(b) / (reps[j] * nper[j]))
     out = []
     for j, (label, kind, _) in enumerate(launches):
         v = sorted(per[j])
         vs = sorted(per_s[j])
         out.append((label, kind, sum(v) / len(v), v[len(v) // 2], v[0], vs[len(vs) // 2]))
-    del graphs
+    del graphs, fns
+    torch.cuda.empty_cache()
     return out
 
 
@@ -700,8 +714,8 @@ def stream_read_ceiling(nbytes: int = 2 << 30, reps: int = 10):
 def read_floors_us(wl: Workload):
     """Per GEMV launch of the step, the least time any kq_read_probe form of
     PROBE_FORMS takes to read the same weight tensor, rotated over the same
-    copies and timed the same way as the launch itself (graph replays of
-    whole rounds of the copies).  Returns {label: (us, form)}."""
+    number of copies as the launch's own timing and timed the same way
+    (graph replays of whole rounds of the copies).  Returns {label: (us, form)}."""
     import torch
 
     import q6_q8_matmul_amd as kq
@@ -711,7 +725,9 @@ def read_floors_us(wl: Workload):
     for op in wl.ops:
         if not op["op"].startswith("gemv"):
             continue
+        n = max(wl.ncopies, copies_for(wl.host[op["w"]].nbytes))
         bufs = [wl.w[c][op["w"]] for c in range(wl.ncopies)]
+        bufs += [bufs[0].clone() for _ in range(n - len(bufs))]
         nbytes = bufs[0].numel() // 16 * 16
         best = None
         for form in PROBE_FORMS:
@@ -724,6 +740,8 @@ def read_floors_us(wl: Workload):
                 best = (ms, form)
             del res
         out[op["label"]] = (round(best[0] * 1e3, 2), _probe_label(best[1]))
+        del bufs
+        torch.cuda.empty_cache()
     return out
 
 
@@ -930,6 +948,30 @@ def _op_bytes(cfg: int):
     return out, sorted(weights)
 
 
+def _copy_scale(readings, sizes, tol: float = 0.05):
+    """Bytes per counter unit from the plain copy kernels of a run: each copy
+    moves one weight tensor, of one of the known `sizes`, but how often each
+    tensor is copied varies.  The scale is the one under which the most
+    readings land within `tol` (relative) of some size -- at least 90 % of
+    them, else None -- refined over those matches."""
+    if not readings or not sizes:
+        return None
+    best = []
+    for r in readings:
+        for size in sizes:
+            s = size / r
+            matched = []
+            for r2 in readings:
+                near = min(sizes, key=lambda z: abs(math.log(z / (r2 * s))))
+                if abs(math.log(near / (r2 * s))) < tol:
+                    matched.append((near, r2))
+            if len(matched) > len(best):
+                best = matched
+    if len(best) < 0.9 * len(readings):
+        return None
+    return sum(z for z, _ in best) / sum(r for _, r in best)
+
+
 def summarize(cfg: int, trace_csv=None, fetch_csv=None, write_csv=None):
     """Text summary of rocprofv3 CSV output of this script for workload cfg.
     Counter readings are scaled by (bytes / reading) of the plain copy
@@ -983,11 +1025,9 @@ def summarize(cfg: int, trace_csv=None, fetch_csv=None, write_csv=None):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == name]
         copies = [float(r["Counter_Value"]) * 1024 for r in rows
                   if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) * 1024 >= min(weight_sizes) / 4]
-        # each copy moves one weight tensor: match readings to sizes by rank
-        copies.sort()
-        sizes = sorted(weight_sizes * (len(copies) // max(len(weight_sizes), 1)))
-        if len(sizes) == len(copies) and copies:
-            scale[name] = sum(sizes) / sum(copies)
+        sc = _copy_scale(copies, weight_sizes)
+        if sc is not None:
+            scale[name] = sc
         _, _, steps = _steps_in(rows, cfg)
         out.append(f"{name}: {len(steps)} steps matched in {path}; copy-kernel scale "
                    f"{scale.get(name, float('nan')):.4f} from {len(copies)} weight copies")

@@ -646,11 +646,17 @@ hipError_t launch_persistent(const Tab& tab, const void* xq, int64_t k, int schu
 
 // K-split launch (the whole activation in one piece of at most lds_limit).
 template <int BATCH, int RPW, int WH>
+size_t ksplit_lds(int64_t k) {
+    const int S = (int)(k / kQK);
+    return (size_t)((S + 7) & ~7) * lds_per_sb(BATCH) + (size_t)WH * RPW * 2 * BATCH * 4;
+}
+
+template <int BATCH, int RPW, int WH>
 hipError_t launch_ksplit(const void* w, const void* xq, float* y, const float* residual,
                          int64_t m, int64_t k, int lds_limit, hipStream_t stream) {
     const int S = (int)(k / kQK);
     const int schunk = (S + 7) & ~7;
-    const size_t lds = (size_t)schunk * lds_per_sb(BATCH) + (size_t)WH * RPW * 2 * BATCH * 4;
+    const size_t lds = ksplit_lds<BATCH, RPW, WH>(k);
     if (lds > (size_t)lds_limit) return hipErrorInvalidConfiguration;
     const int64_t ngroups = (m + WH * RPW * 2 - 1) / (WH * RPW * 2);
     hipLaunchKernelGGL((gemv_q4k_ksplit<BATCH, RPW, WH>), dim3((unsigned)ngroups), dim3(128 * WH),
@@ -716,11 +722,15 @@ hipError_t launch_gemv_q4k(const void* w, const void* xq, float* y, const float*
                            hipStream_t stream) {
     using namespace gemv4;
     // Launch shapes chosen by measurement on MI355X (back-to-back launches
-    // over rotating weight copies, Llama-3-8B decode shapes).  Batch 1: one
-    // row pair per wavefront, one pass ahead, persistent grid -- eight
-    // wavefronts and three workgroups per CU for tall or long rows (gate|up
-    // 28672x4096, down 4096x14336), else four wavefronts and four workgroups
-    // (4096x4096); two or three passes ahead were slower on all three.
+    // over enough rotating weight copies that every launch streams from HBM,
+    // Llama-3-8B decode shapes).  Batch 1: one row pair per wavefront, one
+    // pass ahead, persistent grid -- eight wavefronts and three workgroups
+    // per CU for tall or long rows (gate|up 28672x4096), else four
+    // wavefronts and four workgroups (4096x4096); two or three passes ahead
+    // were slower on all three.  Long rows with too few row pairs to occupy
+    // that grid (down 4096x14336: 2048 pairs of 7 passes for 6144
+    // wavefronts) take the K split instead, two wavefronts per row pair
+    // (8.5 against 9.0 us; three or four per pair: 8.6-10.3 us).
     // Batches 2-4 use the four-wavefront persistent form (QKV 6144x4096 at
     // batch 4) unless the activation needs more than 64 KB of LDS: at batch 4
     // the K split when the whole activation still fits one workgroup's LDS
@@ -731,8 +741,10 @@ hipError_t launch_gemv_q4k(const void* w, const void* xq, float* y, const float*
     const int64_t whole = (int64_t)lds_per_sb(batch) * s_round;
     const int one_piece = whole <= lds_limit ? lds_limit : 65536;
     const bool big = m >= 16384 || S > 16;
+    const bool split1 = S >= 32 && m < 48LL * cus && ksplit_lds<1, 1, 4>(k) <= (size_t)lds_limit;
     switch (batch) {
-        case 1: return big ? launch_variant<1, 1, 1, 8>(w, xq, y, residual, m, k, 65536, cus, 3, stream)
+        case 1: if (split1) return launch_ksplit<1, 1, 4>(w, xq, y, residual, m, k, lds_limit, stream);
+                return big ? launch_variant<1, 1, 1, 8>(w, xq, y, residual, m, k, 65536, cus, 3, stream)
                            : launch_variant<1, 1, 1, 4>(w, xq, y, residual, m, k, 65536, cus, 4, stream);
         case 2: return launch_variant<2, 1, 1, 4>(w, xq, y, residual, m, k, one_piece, cus, 6, stream);
         case 3: return launch_variant<3, 1, 1, 4>(w, xq, y, residual, m, k, one_piece, cus, 6, stream);

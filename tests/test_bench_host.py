@@ -237,3 +237,19 @@ def test_summarize_lds_counters(tmp_path):
     rec = [json.loads(l[len("counters_json: "):]) for l in text.splitlines() if l.startswith("counters_json: ")]
     assert rec[0]["launches"]["down"]["lds_busy"] == 0.3
     assert rec[0]["launches"]["down"]["lds_bank_conflict"] == 0.02
+
+
+def test_copy_scale_unequal_copy_counts():
+    """The counter scale comes from plain copies of the weight tensors; each
+    tensor may be copied a different number of times (per-launch rotations
+    clone the small ones more), so readings are matched by size, not rank."""
+    import random
+
+    sizes = [9_437_184, 66_060_288, 33_030_144]
+    rng = random.Random(5)
+    readings = [z * 0.5 * rng.uniform(0.996, 1.004)
+                for z, n in ((9_437_184, 62), (66_060_288, 8), (33_030_144, 17)) for _ in range(n)]
+    sc = bench._copy_scale(readings, sizes)
+    assert sc is not None and abs(sc - 2.0) < 0.01
+    # readings that match no size consistently give no scale
+    assert bench._copy_scale([1.0, 3.3, 7.7, 12.1], sizes) is None
